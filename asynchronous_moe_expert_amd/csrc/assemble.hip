@@ -1,0 +1,174 @@
+// moe_assemble: expert-grouped batch assembly from a scattered token pool.
+//
+// [SEP] (marsggbo, "SOSP'26 | StreamEP", section 3): tokens wait in a GPU pool, the expert
+// micro-queue lists them with their metadata, and the executor turns the queue's scattered
+// inputs into one contiguous batch.  Here the batch is grouped by local expert so that the
+// grouped FFN sees one contiguous row range per expert.
+//
+// Two kernels:
+//   1. index kernel (one 1024-thread workgroup): per-expert histogram in LDS, a wave scan
+//      for the exclusive offsets, then a stable scatter of queue indices.  Stability
+//      inside each 1024-pair chunk comes from a 9-bit wave "match" (ballot per key bit)
+//      giving each pair its rank among equal keys of lower lanes, plus per-wave counts
+//      scanned across the 16 waves.  Integer-only, so the result is deterministic.
+//   2. row gather: one 16-byte vector per thread, flattened over rows x 16-byte chunks so
+//      that consecutive lanes copy consecutive bytes of a row (fully coalesced reads of each
+//      pool row and writes of each batch row).
+#include "common.hpp"
+
+namespace moe {
+
+constexpr int kAsmThreads = 1024;
+constexpr int kAsmWaves = kAsmThreads / kWave;
+constexpr int kMaxElocAsm = 256;
+
+__global__ __launch_bounds__(kAsmThreads) void assemble_index_kernel(
+    int n, const int32_t* __restrict__ slot, const int32_t* __restrict__ expert, int base, int E_loc, int64_t P,
+    int32_t* __restrict__ perm, int32_t* __restrict__ pos, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, uint32_t* __restrict__ err) {
+  __shared__ int s_run[kMaxElocAsm];
+  __shared__ int s_wcnt[kAsmWaves][kMaxElocAsm + 1];
+  __shared__ int s_total;
+  __shared__ unsigned s_err;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+
+  for (int e = tid; e < E_loc; e += kAsmThreads) s_run[e] = 0;
+  if (tid == 0) s_err = 0u;
+  __syncthreads();
+
+  // pass 1: validate and count
+  unsigned myerr = 0u;
+  for (int i = tid; i < n; i += kAsmThreads) {
+    const int64_t s = slot[i];
+    const int e = expert[i] - base;
+    bool ok = true;
+    if (s < 0 || s >= P) { myerr |= MOE_ERR_SLOT_RANGE; ok = false; }
+    if (e < 0 || e >= E_loc) { myerr |= MOE_ERR_EXPERT_NONLOCAL; ok = false; }
+    if (ok) atomicAdd(&s_run[e], 1);
+  }
+  if (myerr) atomicOr(&s_err, myerr);
+  __syncthreads();
+
+  // exclusive scan of the counts (wave 0; 4 experts per lane covers E_loc <= 256)
+  if (wv == 0) {
+    int v[4], sum = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = lane * 4 + k;
+      v[k] = e < E_loc ? s_run[e] : 0;
+      sum += v[k];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int t = __shfl_up(incl, d);
+      if (lane >= d) incl += t;
+    }
+    int run = incl - sum;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = lane * 4 + k;
+      if (e < E_loc) {
+        counts[e] = v[k];
+        offsets[e] = run;
+        s_run[e] = run;  // running output row of expert e
+      }
+      run += v[k];
+    }
+    if (lane == 63) {
+      offsets[E_loc] = incl;
+      s_total = incl;
+    }
+  }
+  __syncthreads();
+
+  // pass 2: stable scatter, one chunk of 1024 queue entries at a time
+  for (int c0 = 0; c0 < n; c0 += kAsmThreads) {
+    const int i = c0 + tid;
+    int key = kMaxElocAsm;  // "rejected / past the end" key
+    if (i < n) {
+      const int64_t s = slot[i];
+      const int e = expert[i] - base;
+      if (s >= 0 && s < P && e >= 0 && e < E_loc) key = e;
+    }
+    for (int x = tid; x < kAsmWaves * E_loc; x += kAsmThreads) s_wcnt[x / E_loc][x % E_loc] = 0;
+    __syncthreads();
+    uint64_t peers = ~0ull;
+#pragma unroll
+    for (int b = 0; b < 9; ++b) {
+      const bool bit = (key >> b) & 1;
+      const uint64_t bal = __ballot(bit);
+      peers &= bit ? bal : ~bal;
+    }
+    const int rank = __popcll(peers & ((1ull << lane) - 1ull));
+    if (key < kMaxElocAsm && rank == 0) s_wcnt[wv][key] = __popcll(peers);
+    __syncthreads();
+    if (tid < E_loc) {
+      int run = s_run[tid];
+#pragma unroll
+      for (int w = 0; w < kAsmWaves; ++w) {
+        const int cnt = s_wcnt[w][tid];
+        s_wcnt[w][tid] = run;
+        run += cnt;
+      }
+      s_run[tid] = run;
+    }
+    __syncthreads();
+    if (key < kMaxElocAsm) {
+      const int r = s_wcnt[wv][key] + rank;
+      perm[r] = i;
+      if (pos) pos[i] = r;
+    } else if (i < n && pos) {
+      pos[i] = -1;
+    }
+    __syncthreads();
+  }
+  for (int r = s_total + tid; r < n; r += kAsmThreads) perm[r] = -1;
+  if (tid == 0 && s_err) atomicOr(err, s_err);
+}
+
+__global__ __launch_bounds__(256) void gather_rows_kernel(const int32_t* __restrict__ perm,
+                                                           const int32_t* __restrict__ slot,
+                                                           const int32_t* __restrict__ n_valid_ptr,
+                                                           const char* __restrict__ pool, int64_t pitch_bytes,
+                                                           char* __restrict__ xb, int row_bytes, int cpr) {
+  const int64_t lim = (int64_t)(*n_valid_ptr) * cpr;
+  for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < lim; g += (int64_t)gridDim.x * 256) {
+    const int r = (int)(g / cpr);
+    const int c = (int)(g - (int64_t)r * cpr);
+    const int64_t s = slot[perm[r]];
+    const uint4 v = *reinterpret_cast<const uint4*>(pool + s * pitch_bytes + (int64_t)c * 16);
+    *reinterpret_cast<uint4*>(xb + (int64_t)r * row_bytes + (int64_t)c * 16) = v;
+  }
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" int moe_assemble(const moe_assemble_args* a, hipStream_t stream) {
+  if (!a) return MOE_EINVAL_NULL;
+  if (a->n < 0 || a->n > (1 << 24) || a->E_loc < 1 || a->E_loc > kMaxElocAsm || a->H < 1 || a->P < 0 ||
+      a->pool_pitch < a->H)
+    return MOE_EINVAL_SIZE;
+  if (a->act_dtype != MOE_F32 && a->act_dtype != MOE_BF16) return MOE_EINVAL_DTYPE;
+  if (!a->counts || !a->offsets || !a->err) return MOE_EINVAL_NULL;
+  const int esz = dtype_size(a->act_dtype);
+  const int row_bytes = a->H * esz;
+  const int64_t pitch_bytes = a->pool_pitch * esz;
+  if (row_bytes % 16 || pitch_bytes % 16) return MOE_EINVAL_ALIGN;
+  if (a->n > 0) {
+    if (!a->slot || !a->expert || !a->perm || !a->pool || !a->xb) return MOE_EINVAL_NULL;
+    if (!aligned16(a->pool) || !aligned16(a->xb)) return MOE_EINVAL_ALIGN;
+  }
+  hipLaunchKernelGGL(assemble_index_kernel, dim3(1), dim3(kAsmThreads), 0, stream, a->n, a->slot, a->expert,
+                     a->expert_base, a->E_loc, a->P, a->perm, a->pos, a->counts, a->offsets, a->err);
+  if (a->n == 0) return launch_status();
+  const int cpr = row_bytes / 16;
+  const int64_t work = (int64_t)a->n * cpr;
+  int64_t blocks = (work + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a->perm, a->slot,
+                     a->offsets + a->E_loc, (const char*)a->pool, pitch_bytes, (char*)a->xb, row_bytes, cpr);
+  return launch_status();
+}

@@ -1,0 +1,70 @@
+"""One rank's expert step as three C-ABI calls on one stream, with the buffers they need.
+
+torch only allocates device memory here; every stage runs in libmoestep's kernels:
+  moe_assemble -> moe_expert_ffn_grouped -> moe_combine_release
+The local results are combined straight from the FFN output: arrival i of the combine is
+queue entry i, whose result row is pos[i] (the batch row moe_assemble gave it).
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _native as N
+
+_TORCH = {N.MOE_F32: torch.float32, N.MOE_BF16: torch.bfloat16, N.MOE_FP8_E4M3: torch.uint8}
+
+
+class ExpertStep:
+    def __init__(self, E_loc: int, H: int, I: int, K: int, act_dtype: int, w_dtype: int, n_max: int, T_cap: int,
+                 device="cuda"):
+        self.E_loc, self.H, self.I, self.K = E_loc, H, I, K
+        self.act_dtype, self.w_dtype, self.n_max, self.T_cap = act_dtype, w_dtype, n_max, T_cap
+        dev = torch.device(device)
+        adt = _TORCH[act_dtype]
+        nm = max(n_max, 1)
+        self.perm = torch.empty(nm, dtype=torch.int32, device=dev)
+        self.pos = torch.empty(nm, dtype=torch.int32, device=dev)
+        self.counts = torch.empty(E_loc, dtype=torch.int32, device=dev)
+        self.offsets = torch.empty(E_loc + 1, dtype=torch.int32, device=dev)
+        self.xb = torch.empty((nm, H), dtype=adt, device=dev)
+        self.y = torch.empty((nm, H), dtype=adt, device=dev)
+        ws = N.moe_ffn_workspace_size(nm, E_loc, H, I, act_dtype)
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
+        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.rel_list = torch.empty(max(T_cap, 1), dtype=torch.int32, device=dev)
+        self.rel_count = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.state = N.CombineState(T_cap, H, device=dev)
+        self.out = torch.empty((T_cap, H), dtype=adt, device=dev)
+        self.w_gu = self.w_d = None
+        self.s_gate = self.s_up = self.s_down = None
+        N.moe_state_reset(self.state, 0)
+
+    def load_weights(self, wg, wu, wd, s_gate=None, s_up=None, s_down=None, stream=None) -> None:
+        """wg, wu: [E][I][H], wd: [E][H][I] device tensors in the weight dtype (row-major);
+        fp8 weights come as uint8 codes with fp32 row scales."""
+        self.w_gu = torch.empty(self.E_loc * 2 * self.I * self.H, dtype=wg.dtype, device=wg.device)
+        self.w_d = torch.empty(self.E_loc * self.H * self.I, dtype=wg.dtype, device=wg.device)
+        N.moe_pack_ffn_weights(wg, wu, wd, self.w_gu, self.w_d, self.w_dtype, stream=stream)
+        self.s_gate, self.s_up, self.s_down = s_gate, s_up, s_down
+
+    def assemble(self, slot, expert, expert_base: int, pool, n: int | None = None, stream=None) -> None:
+        N.moe_assemble(slot, expert, expert_base, self.E_loc, pool, self.perm, self.pos, self.counts, self.offsets,
+                       self.xb, self.err, n=n, stream=stream)
+
+    def ffn(self, n: int, ev_mid: int | None = None, stream=None) -> None:
+        N.moe_expert_ffn_grouped(n, self.E_loc, self.H, self.I, self.act_dtype, self.w_dtype, self.xb, self.offsets,
+                                 self.w_gu, self.w_d, self.y, self.workspace, self.s_gate, self.s_up, self.s_down,
+                                 ev_mid=ev_mid, stream=stream)
+
+    def combine(self, rows, row_idx, tok, kslot, w, gen, m: int | None = None, n_rows: int | None = None,
+                stream=None) -> None:
+        N.moe_combine_release(rows, row_idx, tok, kslot, w, gen, self.K, self.state, self.out, self.rel_list,
+                              self.rel_count, self.err, m=m, n_rows=n_rows, stream=stream)
+
+    def run(self, slot, expert, expert_base: int, pool, tok, kslot, w, gen, n: int | None = None,
+            ev_mid: int | None = None, stream=None) -> None:
+        """The whole step on one batch: assemble, FFN, combine of the local results."""
+        n = int(slot.numel() if n is None else n)
+        self.assemble(slot, expert, expert_base, pool, n=n, stream=stream)
+        self.ffn(n, ev_mid=ev_mid, stream=stream)
+        self.combine(self.y, self.pos, tok, kslot, w, gen, m=n, n_rows=n, stream=stream)

@@ -1,0 +1,42 @@
+"""Shared helpers for the GPU parity tests (run the HIP path, compare with the oracle)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle as O
+from workloads.device import tensor, to_numpy_bits
+
+TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2}
+
+
+def row_rel_err(gpu: np.ndarray, ref: np.ndarray) -> float:
+    """max over rows of ||gpu_r - ref_r||_inf / ||ref_r||_inf (rows with a zero reference
+    must match to 1e-30 absolute)."""
+    gpu = np.asarray(gpu, np.float64).reshape(len(ref), -1)
+    ref = np.asarray(ref, np.float64).reshape(len(ref), -1)
+    worst = 0.0
+    for g, r in zip(gpu, ref):
+        den = np.abs(r).max()
+        num = np.abs(g - r).max()
+        if den == 0:
+            assert num <= 1e-30, "nonzero output where the reference row is zero"
+            continue
+        worst = max(worst, num / den)
+    return worst
+
+
+def decode_tensor(t: torch.Tensor) -> np.ndarray:
+    a = to_numpy_bits(t)
+    if a.dtype == np.uint16:
+        return O.decode_bf16(a)
+    return a.astype(np.float64)
+
+
+def dev(a, dtype=None):
+    return tensor(a, dtype, "cuda")
+
+
+def sync_err(t: torch.Tensor) -> int:
+    torch.cuda.synchronize()
+    return int(t.item()) & 0xFFFFFFFF

@@ -1,0 +1,360 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle, element by element
+on the same seeded inputs.  Integer outputs bit-exact; rows within the per-dtype tolerance
+(max over rows of ||gpu - ref||_inf / ||ref||_inf: 1e-5 fp32, 2e-2 bf16, 6e-2 fp8)."""
+import numpy as np
+import pytest
+import torch
+
+import asynchronous_moe_expert_amd as M
+import oracle as O
+import workloads as W
+from gpu_helpers import TOL, decode_tensor, dev, row_rel_err, sync_err
+from workloads.device import batch_tensors, to_numpy_bits, weight_tensors
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    M.load()
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+# --------------------------------------------------------------------------- assemble
+ASM_CASES = [
+    # (n, E_loc, base, P, H, act, pitch_extra, bad_frac)
+    (0, 4, 0, 16, 64, "bf16", 0, 0.0),
+    (1, 1, 3, 8, 64, "f32", 0, 0.0),
+    (7, 5, 10, 40, 8, "f32", 4, 0.3),
+    (1023, 8, 0, 2048, 192, "bf16", 8, 0.0),
+    (1024, 8, 16, 1024, 64, "bf16", 0, 0.05),
+    (1025, 3, 0, 300, 64, "bf16", 0, 0.1),
+    (3000, 256, 0, 5000, 64, "bf16", 0, 0.02),
+    (5000, 32, 64, 9000, 2880, "bf16", 0, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", ASM_CASES, ids=[f"n{c[0]}_E{c[1]}_H{c[4]}" for c in ASM_CASES])
+def test_assemble_matches_oracle(case):
+    n, E, base, P, H, act, extra, bad = case
+    _say("assemble case", case)
+    rng = np.random.default_rng(n * 7 + E)
+    slot = rng.integers(0, P, size=n).astype(np.int32)
+    expert = (base + rng.integers(0, E, size=n)).astype(np.int32)
+    nb = int(bad * n)
+    if nb:
+        idx = rng.choice(n, size=nb, replace=False)
+        slot[idx[: nb // 2]] = rng.choice([-1, P, P + 5], size=nb // 2)
+        expert[idx[nb // 2:]] = rng.choice([base - 1, base + E, -7], size=nb - nb // 2)
+    raw = rng.standard_normal((P, H + extra)).astype(np.float32)
+    pool_np = W.to_bf16_bits(raw) if act == "bf16" else raw
+    pool_full = dev(pool_np, act)
+    pool = pool_full[:, :H]
+    st_xb = torch.empty((max(n, 1), H), dtype=pool.dtype, device="cuda")
+    perm = torch.full((max(n, 1),), -9, dtype=torch.int32, device="cuda")
+    pos = torch.full((max(n, 1),), -9, dtype=torch.int32, device="cuda")
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    M.moe_assemble(dev(slot), dev(expert), base, E, pool, perm, pos, counts, offsets, st_xb, err, n=n)
+    e = sync_err(err)
+    a = O.assemble(slot, expert, base, E, P)
+    assert e == a["err"]
+    assert np.array_equal(counts.cpu().numpy(), a["counts"])
+    assert np.array_equal(offsets.cpu().numpy(), a["offsets"])
+    if n:
+        assert np.array_equal(perm.cpu().numpy()[:n], a["perm"])
+        assert np.array_equal(pos.cpu().numpy()[:n], a["pos"])
+        nv = int(a["offsets"][-1])
+        ref = O.gather_rows(pool_np[:, :H], slot, a["perm"], nv)
+        got = to_numpy_bits(st_xb[:nv])
+        assert np.array_equal(got.view(np.uint8), np.ascontiguousarray(ref).view(np.uint8))
+
+
+# ------------------------------------------------------------------------------- FFN
+FFN_CASES = [
+    # (act/weight dtype, E, H, I, counts)
+    ("f32", 3, 64, 128, [5, 0, 17]),
+    ("bf16", 4, 128, 192, [1, 64, 0, 130]),
+    ("bf16", 2, 2880, 2880, [37, 70]),
+    ("bf16", 5, 256, 128, [0, 0, 200, 1, 16]),
+    ("fp8", 3, 256, 128, [65, 3, 0]),
+    ("fp8", 2, 4096, 2048, [129, 40]),
+]
+
+
+@pytest.mark.parametrize("case", FFN_CASES, ids=[f"{c[0]}_E{c[1]}_H{c[2]}_I{c[3]}" for c in FFN_CASES])
+def test_ffn_matches_oracle(case):
+    wdt, E, H, I, counts = case
+    _say("ffn case", case)
+    rng = np.random.default_rng(E * 1000 + H + I)
+    act = "f32" if wdt == "f32" else "bf16"
+    wts = W.make_layer_weights(rng, E, H, I, 0.05, wdt)
+    n = int(sum(counts))
+    x_raw = rng.standard_normal((n, H)).astype(np.float32)
+    x_np = x_raw if act == "f32" else W.to_bf16_bits(x_raw)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    codes = {"f32": M.MOE_F32, "bf16": M.MOE_BF16, "fp8": M.MOE_FP8_E4M3}
+    st = M.ExpertStep(E, H, I, 2, codes[act], codes[wdt], n, 4)
+    wt = weight_tensors(wts)
+    st.load_weights(wt["wg"], wt["wu"], wt["wd"], wt.get("s_gate"), wt.get("s_up"), wt.get("s_down"))
+    st.xb[:n].copy_(dev(x_np, act))
+    st.offsets.copy_(dev(offsets))
+    st.ffn(n)
+    torch.cuda.synchronize()
+    y_ref = O.expert_ffn(O.decode(x_np, act), offsets, wts)
+    err = row_rel_err(decode_tensor(st.y[:n]), y_ref)
+    _say(f"  row rel err {err:.3e}")
+    assert err <= TOL[wdt]
+
+
+def test_ffn_empty_batch_is_a_no_op():
+    st = M.ExpertStep(2, 64, 64, 2, M.MOE_BF16, M.MOE_BF16, 4, 4)
+    z = torch.zeros((2, 64, 64), dtype=torch.bfloat16, device="cuda")
+    st.load_weights(z, z, z)
+    st.y.fill_(3.0)
+    st.offsets.zero_()
+    st.ffn(0)
+    torch.cuda.synchronize()
+    assert torch.all(st.y == 3.0)
+
+
+# --------------------------------------------------------------------------- combine
+def _combine_call(st, rows_t, rows64, arr, ocs, K):
+    """Run one combine call on GPU and oracle; compare err, rel list and state."""
+    row_idx, tok, ks, w, gen = (np.array(c) for c in zip(*arr)) if arr else [np.zeros(0, np.int32)] * 5
+    m = len(arr)
+    st.err.zero_()
+    d = [dev(np.asarray(v, dt)) for v, dt in ((row_idx, np.int32), (tok, np.int32), (ks, np.int32),
+                                               (w, np.float32), (gen, np.uint32))]
+    st.combine(rows_t, *d, m=m, n_rows=rows_t.shape[0])
+    e = sync_err(st.err)
+    out, rel, oerr = O.combine_release(ocs, rows64, row_idx, tok, ks, np.asarray(w, np.float32), gen)
+    n_rel = int(st.rel_count.item())
+    assert e == oerr, (e, oerr)
+    assert np.array_equal(st.rel_list[:n_rel].cpu().numpy(), rel)
+    assert np.array_equal(st.state.mask.cpu().numpy().view(np.uint32), ocs.mask)
+    assert np.array_equal(st.state.tgen.cpu().numpy().view(np.uint32), ocs.tgen)
+    assert np.all(st.state.done.cpu().numpy() == 0)
+    return out, rel
+
+
+@pytest.mark.parametrize("rdt", ["f32", "bf16"])
+def test_combine_integer_toy_is_bit_exact_over_split_calls(rdt):
+    _say("combine integer toy", rdt)
+    rng = np.random.default_rng(11)
+    T, K, H = 200, 4, 64
+    # small integers and power-of-two weights: every partial sum is exact in fp32 and bf16
+    rows_np = rng.integers(-8, 8, size=(T * K + 10, H)).astype(np.float32)
+    rows64 = rows_np.astype(np.float64)
+    rows_t = dev(W.to_bf16_bits(rows_np), "bf16") if rdt == "bf16" else dev(rows_np)
+    arrivals = [(t * K + j, t, j, 2.0 ** -int(rng.integers(0, 3)), 0) for t in range(T) for j in range(K)]
+    order = rng.permutation(len(arrivals))
+    arrivals = [arrivals[i] for i in order]
+    st = M.ExpertStep(1, H, 64, K, M.MOE_BF16 if rdt == "bf16" else M.MOE_F32, M.MOE_BF16, 1, T)
+    ocs = O.CombineState(T, K)
+    cuts = [0, 250, 251, 520, len(arrivals)]
+    released = []
+    for c in range(4):
+        chunk = arrivals[cuts[c]:cuts[c + 1]]
+        if c == 1:  # a retry of an earlier result and a stale result ride along
+            chunk = chunk + [arrivals[3], (T * K + 1, arrivals[5][1], arrivals[5][2], 1.0, 7)]
+        out, rel = _combine_call(st, rows_t, rows64, chunk, ocs, K)
+        g = st.out.cpu()
+        g = O.decode_bf16(to_numpy_bits(g)) if rdt == "bf16" else g.numpy().astype(np.float64)
+        for t in rel:
+            assert np.array_equal(g[t], out[t])  # exact
+        released += list(rel)
+    assert sorted(released) == list(range(T))
+
+
+def test_combine_errors_duplicates_and_generations():
+    _say("combine errors")
+    K, T, H = 2, 6, 64
+    rows_np = np.arange(10 * H, dtype=np.float32).reshape(10, H) / 64
+    rows_t, rows64 = dev(rows_np), rows_np.astype(np.float64)
+    st = M.ExpertStep(1, H, 64, K, M.MOE_F32, M.MOE_F32, 1, T)
+    ocs = O.CombineState(T, K)
+    # in-call duplicate with different rows: exactly one is accepted (which one is left open,
+    # so only flags, release lists and state are compared for it)
+    _combine_call(st, rows_t, rows64, [(0, 0, 0, 1.0, 0), (1, 0, 0, 1.0, 0)], ocs, K)
+    _combine_call(st, rows_t, rows64, [(2, 0, 1, 1.0, 0)], ocs, K)  # releases token 0
+    _combine_call(st, rows_t, rows64, [(3, 0, 0, 1.0, 0)], ocs, K)  # stale generation
+    _combine_call(st, rows_t, rows64, [(3, 9, 0, 1.0, 0), (3, 1, 5, 1.0, 0), (99, 1, 0, 1.0, 0), (-1, 2, 1, 1, 0)],
+                  ocs, K)
+    _combine_call(st, rows_t, rows64, [], ocs, K)  # empty call
+    out, rel = _combine_call(st, rows_t, rows64, [(4, 5, 0, 0.5, 0), (4, 5, 0, 0.5, 0), (5, 5, 1, 0.25, 0)], ocs, K)
+    assert list(rel) == [5]
+    g = st.out.cpu().numpy().astype(np.float64)
+    assert np.array_equal(g[5], out[5])  # identical duplicate rows: result independent of the winner
+
+
+@pytest.mark.parametrize("K", [1, 3, 32])
+def test_combine_k_extremes(K):
+    _say("combine K", K)
+    rng = np.random.default_rng(K)
+    T, H = 40, 128
+    rows_np = rng.standard_normal((T * K, H)).astype(np.float32)
+    rows_t, rows64 = dev(rows_np), rows_np.astype(np.float64)
+    st = M.ExpertStep(1, H, 64, K, M.MOE_F32, M.MOE_F32, 1, T)
+    ocs = O.CombineState(T, K)
+    arr = [(t * K + j, t, j, float(rng.random()), 0) for t in range(T) for j in range(K)]
+    arr = [arr[i] for i in rng.permutation(len(arr))]
+    h = len(arr) // 2
+    _combine_call(st, rows_t, rows64, arr[:h], ocs, K)
+    out, rel = _combine_call(st, rows_t, rows64, arr[h:], ocs, K)
+    g = st.out.cpu().numpy().astype(np.float64)
+    all_out = {**out}
+    assert row_rel_err(g[list(all_out)], np.array([all_out[t] for t in all_out])) <= 1e-6
+
+
+# --------------------------------------------------------------------- whole configs
+def _run_config_step(b, wts, act_code, w_code, check_rows=True, sample_rows=None, T_cap=None):
+    """Deliver the remote results (one call), then run the step on the local pairs.
+    Returns the GPU step and the oracle pieces for comparison."""
+    d = batch_tensors(b)
+    wt = weight_tensors(wts)
+    st = M.ExpertStep(b.E_loc, b.H, wts.I, b.K, act_code, w_code, b.n, T_cap or b.T)
+    st.load_weights(wt["wg"], wt["wu"], wt["wd"], wt.get("s_gate"), wt.get("s_up"), wt.get("s_down"))
+    if "r_rows" in d:
+        st.combine(d["r_rows"], d["r_idx"], d["r_tok"], d["r_kslot"], d["r_w"], d["r_gen"])
+        torch.cuda.synchronize()
+        assert int(st.rel_count.item()) == 0
+    st.run(d["slot"], d["expert"], b.expert_base, d["pool"], d["tok"], d["kslot"], d["w"], d["gen"])
+    e = sync_err(st.err)
+    return st, e
+
+
+def test_c0_tiny_full_step():
+    b, wts = W.c0_tiny()
+    _say("C0 tiny fp32 step")
+    st, e = _run_config_step(b, wts, M.MOE_F32, M.MOE_F32)
+    a = O.assemble(b.slot, b.expert, b.expert_base, b.E_loc, b.P)
+    assert e == 0 == a["err"]
+    assert np.array_equal(st.perm.cpu().numpy(), a["perm"])
+    y = O.expert_ffn(O.decode(O.gather_rows(b.pool, b.slot, a["perm"], b.n), "f32"), a["offsets"], wts)
+    assert row_rel_err(st.y.cpu().numpy(), y) <= TOL["f32"]
+    ocs = O.CombineState(b.T, b.K)
+    out, rel, oerr = O.combine_release(ocs, y, a["pos"], b.tok, b.kslot, b.w, b.gen)
+    n_rel = int(st.rel_count.item())
+    assert np.array_equal(st.rel_list[:n_rel].cpu().numpy(), rel) and n_rel == b.T == 32
+    g = st.out.cpu().numpy()
+    assert row_rel_err(g[rel], np.array([out[t] for t in rel])) <= TOL["f32"]
+
+
+def _oracle_step(b, wts, y_rows=None):
+    a = O.assemble(b.slot, b.expert, b.expert_base, b.E_loc, b.P)
+    xb = O.decode(O.gather_rows(b.pool, b.slot, a["perm"], b.n), b.act)
+    y = O.expert_ffn(xb, a["offsets"], wts) if y_rows is None else y_rows
+    return a, y
+
+
+def _check_step(st, e, b, wts, a, y, tol):
+    assert e == a["err"] == 0
+    assert np.array_equal(st.perm.cpu().numpy()[: b.n], a["perm"])
+    assert np.array_equal(st.pos.cpu().numpy()[: b.n], a["pos"])
+    assert np.array_equal(st.offsets.cpu().numpy(), a["offsets"])
+    assert np.array_equal(st.counts.cpu().numpy(), a["counts"])
+    ey = row_rel_err(decode_tensor(st.y[: b.n]), y)
+    ocs = O.CombineState(b.T, b.K)
+    r = b.remote
+    O.combine_release(ocs, O.decode(r.rows, r.dtype), r.row_idx, r.tok, r.kslot, r.w, r.gen)
+    out, rel, oerr = O.combine_release(ocs, y, a["pos"], b.tok, b.kslot, b.w, b.gen)
+    n_rel = int(st.rel_count.item())
+    assert oerr == 0 and np.array_equal(st.rel_list[:n_rel].cpu().numpy(), rel) and n_rel == b.T
+    g = decode_tensor(st.out[torch.as_tensor(rel, device="cuda").long()])
+    eo = row_rel_err(g, np.array([out[t] for t in rel]))
+    _say(f"  Y row err {ey:.3e}, combined row err {eo:.3e}, released {n_rel}")
+    assert ey <= tol and eo <= tol
+
+
+def test_c1_decode_full_step():
+    _say("C1 decode bf16 step")
+    b, wts = W.c1_decode()
+    st, e = _run_config_step(b, wts, M.MOE_BF16, M.MOE_BF16)
+    a, y = _oracle_step(b, wts)
+    _check_step(st, e, b, wts, a, y, TOL["bf16"])
+
+
+def test_c1_decode_other_rank():
+    _say("C1 decode bf16 step, rank 5")
+    b, wts = W.c1_decode(rank=5)
+    st, e = _run_config_step(b, wts, M.MOE_BF16, M.MOE_BF16)
+    a, y = _oracle_step(b, wts)
+    _check_step(st, e, b, wts, a, y, TOL["bf16"])
+
+
+def test_c2_skewed_batches():
+    """All 200 batches: integer parts bit-exact; rows checked on every 20th batch and on
+    the smallest and largest batch."""
+    _say("C2 skewed ragged, 200 batches")
+    wts = W.c2_weights()
+    pool = W.c2_pool()
+    wt = weight_tensors(wts)
+    st = M.ExpertStep(8, 2880, 2880, 4, M.MOE_BF16, M.MOE_BF16, 512, 512)
+    st.load_weights(wt["wg"], wt["wu"], wt["wd"])
+    pool_t = dev(pool, "bf16")
+    batches = [W.c2_skewed_batch(i, pool) for i in range(200)]
+    ns = [bb.n for bb in batches]
+    float_check = set(range(0, 200, 20)) | {int(np.argmin(ns)), int(np.argmax(ns))}
+    for i, b in enumerate(batches):
+        d = batch_tensors(b)
+        d["pool"] = pool_t
+        M.moe_state_reset(st.state, 0)
+        st.err.zero_()
+        st.combine(d["r_rows"], d["r_idx"], d["r_tok"], d["r_kslot"], d["r_w"], d["r_gen"])
+        st.run(d["slot"], d["expert"], 0, d["pool"], d["tok"], d["kslot"], d["w"], d["gen"])
+        e = sync_err(st.err)
+        a = O.assemble(b.slot, b.expert, 0, 8, b.P)
+        assert e == 0
+        assert np.array_equal(st.perm.cpu().numpy()[: b.n], a["perm"]), i
+        assert np.array_equal(st.offsets.cpu().numpy(), a["offsets"]), i
+        n_rel = int(st.rel_count.item())
+        assert np.array_equal(st.rel_list[:n_rel].cpu().numpy(), np.arange(b.n)), i
+        if i in float_check:
+            _say(f" batch {i} n={b.n}")
+            a, y = _oracle_step(b, wts)
+            _check_step(st, e, b, wts, a, y, TOL["bf16"])
+
+
+def test_c4_prefill_wave0_sampled():
+    """Full-size prefill wave (6554 pairs, 32 experts, fp8 weights): integer parts
+    bit-exact; FFN and combined rows on a seeded sample of 96 rows / tokens."""
+    _say("C4 prefill fp8 wave 0")
+    s = W.c4_prefill_setup()
+    b = W.c4_wave(s, 0)
+    st, e = _run_config_step(b, s.weights, M.MOE_BF16, M.MOE_FP8_E4M3, T_cap=b.T)
+    a = O.assemble(b.slot, b.expert, 0, b.E_loc, b.P)
+    assert e == 0 == a["err"]
+    assert np.array_equal(st.perm.cpu().numpy()[: b.n], a["perm"])
+    assert np.array_equal(st.offsets.cpu().numpy(), a["offsets"])
+    n_rel = int(st.rel_count.item())
+    assert np.array_equal(st.rel_list[:n_rel].cpu().numpy(), np.sort(b.tok))
+    rng = np.random.default_rng(99)
+    # sample rows across experts: the hot expert, cold experts, chunk boundaries
+    rows = np.unique(np.concatenate([rng.choice(b.n, 80, replace=False), a["offsets"][:-1][a["counts"] > 0][:8],
+                                     (a["offsets"][1:][a["counts"] > 0] - 1)[:8]]))
+    x = O.decode(b.pool[b.slot[a["perm"][rows]]], "bf16")
+    le = np.searchsorted(a["offsets"], rows, side="right") - 1
+    y_ref = O.ffn_rows(x, le, s.weights)
+    ey = row_rel_err(decode_tensor(st.y[torch.as_tensor(rows, device="cuda").long()]), y_ref)
+    # combined rows of the sampled tokens: remote parts + the local result
+    r = b.remote
+    r_of = {}
+    for k in range(r.m):
+        r_of.setdefault(int(r.tok[k]), []).append(k)
+    toks = b.tok[a["perm"][rows]]
+    refs = []
+    for qi, t in enumerate(toks):
+        parts = {int(r.kslot[k]): (r.w[k], O.decode_bf16(r.rows[r.row_idx[k]])) for k in r_of[int(t)]}
+        p = a["perm"][rows[qi]]
+        parts[int(b.kslot[p])] = (b.w[p], y_ref[qi])
+        refs.append(O.combine_token([parts[j] for j in range(b.K)]))
+    eo = row_rel_err(decode_tensor(st.out[torch.as_tensor(toks, device="cuda").long()]), np.array(refs))
+    _say(f"  sampled Y row err {ey:.3e}, combined row err {eo:.3e}")
+    assert ey <= TOL["fp8"] and eo <= TOL["fp8"]
