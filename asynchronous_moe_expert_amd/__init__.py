@@ -21,6 +21,7 @@ from ._native import (  # noqa: F401
     load,
     moe_assemble,
     moe_combine_release,
+    moe_combine_workspace_size,
     moe_expert_ffn_grouped,
     moe_ffn_workspace_size,
     moe_pack_ffn_weights,

@@ -44,19 +44,20 @@ class FfnArgs(C.Structure):
 
 
 class StateC(C.Structure):
-    _fields_ = [("acc", _p), ("mask", _p), ("done", _p), ("tgen", _p), ("span", _p), ("T_cap", _i32), ("H", _i32)]
+    _fields_ = [("acc", _p), ("mask", _p), ("head", _p), ("tgen", _p), ("rflag", _p), ("T_cap", _i32), ("H", _i32)]
 
 
 class CombineArgs(C.Structure):
     _fields_ = [("m", _i32), ("K", _i32), ("rows", _p), ("row_dtype", _i32), ("row_pitch", _i64),
                 ("n_rows", _i64), ("row_idx", _p), ("tok", _p), ("kslot", _p), ("w", _p), ("gen", _p),
                 ("state", StateC), ("out", _p), ("out_dtype", _i32), ("out_pitch", _i64), ("rel_list", _p),
-                ("rel_count", _p), ("err", _p)]
+                ("rel_count", _p), ("err", _p), ("workspace", _p), ("workspace_bytes", C.c_size_t)]
 
 
 _STRUCTS = [AssembleArgs, PackArgs, FfnArgs, StateC, CombineArgs]
 EXPORTS = ["moe_assemble", "moe_pack_ffn_weights", "moe_ffn_workspace_size", "moe_expert_ffn_grouped",
-           "moe_state_reset", "moe_combine_release", "moe_strerror", "moe_version", "moe_struct_size"]
+           "moe_state_reset", "moe_combine_release", "moe_combine_workspace_size", "moe_strerror", "moe_version",
+           "moe_struct_size"]
 
 
 class MoeError(RuntimeError):
@@ -87,6 +88,8 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     lib.moe_strerror.restype = C.c_char_p
     lib.moe_ffn_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32]
     lib.moe_ffn_workspace_size.restype = C.c_size_t
+    lib.moe_combine_workspace_size.argtypes = [_i32]
+    lib.moe_combine_workspace_size.restype = C.c_size_t
     lib.moe_struct_size.argtypes = [C.c_int]
     lib.moe_struct_size.restype = C.c_size_t
     for k, s in enumerate(_STRUCTS):
@@ -169,12 +172,12 @@ class CombineState:
         self.T_cap, self.H = T_cap, H
         self.acc = torch.empty((T_cap, H), dtype=torch.float32, device=device)
         self.mask = torch.empty(T_cap, dtype=torch.int32, device=device)
-        self.done = torch.empty(T_cap, dtype=torch.int32, device=device)
+        self.head = torch.empty(T_cap, dtype=torch.int32, device=device)
         self.tgen = torch.empty(T_cap, dtype=torch.int32, device=device)
-        self.span = torch.empty(2, dtype=torch.int32, device=device)
+        self.rflag = torch.empty((T_cap + 15) // 16 * 16, dtype=torch.uint8, device=device)
 
     def c(self) -> StateC:
-        return StateC(_ptr(self.acc), _ptr(self.mask), _ptr(self.done), _ptr(self.tgen), _ptr(self.span),
+        return StateC(_ptr(self.acc), _ptr(self.mask), _ptr(self.head), _ptr(self.tgen), _ptr(self.rflag),
                       self.T_cap, self.H)
 
 
@@ -183,11 +186,15 @@ def moe_state_reset(state: CombineState, gen0: int = 0, stream=None) -> None:
     _check(load().moe_state_reset(C.byref(s), gen0, _stream(stream)), "moe_state_reset")
 
 
+def moe_combine_workspace_size(m_max: int) -> int:
+    return load().moe_combine_workspace_size(m_max)
+
+
 def moe_combine_release(rows, row_idx, tok, kslot, w, gen, K: int, state: CombineState, out, rel_list, rel_count,
-                        err, m: int | None = None, n_rows: int | None = None, stream=None) -> None:
+                        err, workspace, m: int | None = None, n_rows: int | None = None, stream=None) -> None:
     """rows: [n_rows][pitch] f32/bf16 result rows; out: [T_cap][pitch] f32/bf16."""
     a = CombineArgs(int(tok.numel() if m is None else m), K, _ptr(rows), dtype_code(rows), rows.stride(0),
                     rows.shape[0] if n_rows is None else n_rows, _ptr(row_idx), _ptr(tok), _ptr(kslot), _ptr(w),
                     _ptr(gen), state.c(), _ptr(out), dtype_code(out), out.stride(0), _ptr(rel_list),
-                    _ptr(rel_count), _ptr(err))
+                    _ptr(rel_count), _ptr(err), _ptr(workspace), workspace.numel() * workspace.element_size())
     _check(load().moe_combine_release(C.byref(a), _stream(stream)), "moe_combine_release")

@@ -8,25 +8,22 @@
 // with its weight, tagged with a reuse generation; no result may be dropped.  [CEP]
 // (CascadeEP abstract / readiness tracking): state is reset only after release.
 //
-// Two kernels:
-//   1. arrive: one wave per arrival.  Lane 0 validates the indices and the generation and
-//      claims bit j of mask[t] with an atomic OR (a second claim of the same bit, in this
-//      call or an earlier one, is a duplicate).  The row is gathered with 16-byte loads,
-//      scaled by w and
-//        - if this arrival completes the token and every other accepted result has
-//          finished accumulating (done[t] == K-1), written straight out:
-//          out[t] = RNE(acc[t] + w * row), acc[t] = 0  (the common decode case: one
-//          atomic-free pass over the row);
-//        - otherwise added to acc[t] with fp32 atomics; after a release fence the wave
-//          bumps done[t], and the wave that brings done[t] to K finalises the token.
-//   2. release: one workgroup scans the token range touched by the call (tracked in
-//      span[]) in ascending order, compacts the tokens whose mask is full into rel_list
-//      (deterministic order), clears their mask and advances their generation.
+// Three kernels per call; none needs another workgroup's float results within a launch,
+// so there are no device-scope fences (on this GPU a fence writes back and invalidates the
+// XCD's whole L2) and no float atomics:
+//   1. link: one thread per arrival.  Index/generation checks, then a lock-free push onto
+//      the token's arrival list (head[t], next[i]).
+//   2. merge: one workgroup per arrival; the workgroup holding the list head owns the token
+//      for the call.  It sorts the token's arrivals by index, accepts top-k positions in
+//      that order (a position already held is a duplicate), and computes
+//      acc + sum w_a * row_a in fp32 in the same order (bit-reproducible).  If the token is
+//      complete it writes out[t] = RNE(sum), clears mask[t], advances tgen[t] and sets its
+//      release flag; otherwise it stores the partial sum back into acc[t].
+//   3. release: one workgroup compacts the release flags into rel_list in ascending token
+//      order (16 flags per thread per pass) and clears them.
 #include "common.hpp"
 
 namespace moe {
-
-constexpr int kCmbWavesPerBlock = 4;
 
 template <typename T>
 struct RowIO;
@@ -66,15 +63,20 @@ struct RowIO<uint16_t> {
   }
 };
 
-template <typename TR, typename TO>
-__global__ __launch_bounds__(256) void combine_arrive_kernel(
-    int m, int K, int H, const TR* __restrict__ rows, int64_t row_pitch, int64_t n_rows,
-    const int32_t* __restrict__ row_idx, const int32_t* __restrict__ tok, const int32_t* __restrict__ kslot,
-    const float* __restrict__ wgt, const uint32_t* __restrict__ gen, float* __restrict__ acc,
-    uint32_t* __restrict__ mask, uint32_t* __restrict__ done, const uint32_t* __restrict__ tgen,
-    int32_t* __restrict__ span, int T_cap, TO* __restrict__ out, int64_t out_pitch, uint32_t* __restrict__ err) {
-  const int lane = threadIdx.x & 63;
-  const int i = blockIdx.x * kCmbWavesPerBlock + (threadIdx.x >> 6);
+constexpr int kCmbThreads = 256;
+constexpr int kMaxChain = 64;  // arrivals of one token handled per pass of the merge
+
+// Kernel 1: one thread per arrival.  Range and generation checks, then a push onto the
+// token's arrival list (head[t] = newest arrival, next[i] = the one pushed before it).
+__global__ __launch_bounds__(256) void combine_link_kernel(int m, int K, int64_t n_rows,
+                                                           const int32_t* __restrict__ row_idx,
+                                                           const int32_t* __restrict__ tok,
+                                                           const int32_t* __restrict__ kslot,
+                                                           const uint32_t* __restrict__ gen,
+                                                           const uint32_t* __restrict__ tgen, int T_cap,
+                                                           int32_t* __restrict__ head, int32_t* __restrict__ next,
+                                                           uint32_t* __restrict__ err) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= m) return;
   const int t = tok[i], j = kslot[i];
   const int64_t r = row_idx[i];
@@ -83,90 +85,163 @@ __global__ __launch_bounds__(256) void combine_arrive_kernel(
   if (j < 0 || j >= K) flag |= MOE_ERR_KSLOT_RANGE;
   if (r < 0 || r >= n_rows) flag |= MOE_ERR_ROW_RANGE;
   if (!flag && gen[i] != tgen[t]) flag |= MOE_ERR_STALE_GEN;
-  int path = 0;  // 1: accumulate with atomics, 2: direct finalise
-  if (!flag) {
-    const uint32_t bit = 1u << j;
-    uint32_t old = 0u;
-    uint32_t d = 0u;
-    if (lane == 0) {
-      old = atomicOr(&mask[t], bit);
-      if (!(old & bit) && __popc(old | bit) == K) d = __hip_atomic_load(&done[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    old = __shfl(old, 0);
-    d = __shfl(d, 0);
-    if (old & bit) {
-      flag |= MOE_ERR_DUPLICATE;
-    } else {
-      path = (__popc(old | bit) == K && d == (uint32_t)(K - 1)) ? 2 : 1;
-      if (lane == 0) {
-        atomicMin(&span[0], t);
-        atomicMax(&span[1], t);
-      }
-    }
-  }
   if (flag) {
-    if (lane == 0) atomicOr(err, flag);
+    atomicOr(err, flag);
+    next[i] = -2;  // not linked
     return;
   }
-  const float w = wgt[i];
-  const TR* src = rows + r * row_pitch;
+  next[i] = atomicExch(&head[t], i);
+}
+
+// Kernel 2: one workgroup per arrival; the workgroup whose arrival heads its token's list
+// owns the token for this call (exactly one per touched token), all others exit.  The
+// owner sorts the token's arrivals by index, accepts top-k positions in that order (a
+// repeat of a held position is a duplicate), and sums acc + w_a * row_a in the same
+// order in fp32, so results do not depend on scheduling.  acc[t] is only read while the
+// token holds earlier results (mask != 0): a fresh token starts from zero.
+template <typename TR, typename TO>
+__global__ __launch_bounds__(kCmbThreads) void combine_merge_kernel(
+    int K, int H, const TR* __restrict__ rows, int64_t row_pitch, const int32_t* __restrict__ row_idx,
+    const int32_t* __restrict__ tok, const int32_t* __restrict__ kslot, const float* __restrict__ wgt,
+    float* __restrict__ acc, uint32_t* __restrict__ mask, uint32_t* __restrict__ tgen,
+    uint8_t* __restrict__ rflag, int32_t* __restrict__ head, const int32_t* __restrict__ next,
+    TO* __restrict__ out, int64_t out_pitch, uint32_t* __restrict__ err) {
+  __shared__ int s_list[kMaxChain];
+  __shared__ int s_buf[kMaxChain];
+  __shared__ int s_n, s_more, s_first;
+  __shared__ uint32_t s_mask0, s_mask1;
+  const int tid = threadIdx.x;
+  const int i = blockIdx.x;
+  if (next[i] == -2) return;  // rejected by the range/generation checks
+  const int t = tok[i];
+  if (head[t] != i) return;   // another arrival owns this token
+  const uint32_t full = K >= 32 ? 0xffffffffu : ((1u << K) - 1u);
   float* a = acc + (int64_t)t * H;
   TO* o = out + (int64_t)t * out_pitch;
   const int nv = H >> 3;
-  if (path == 2) {
-    __threadfence();  // acquire: the other K-1 results are complete in acc[t]
-    for (int v = lane; v < nv; v += 64) {
-      float x[8], s[8];
-      RowIO<TR>::load8(src + v * 8, x);
-      RowIO<float>::load8(a + v * 8, s);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) s[k] = fmaf(w, x[k], s[k]);
-      RowIO<TO>::store8(o + v * 8, s);
-      const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      RowIO<float>::store8(a + v * 8, z);
+  const int cursor = i;  // list head
+  int lo = -1;      // arrivals with index <= lo are already merged
+  bool have = false;  // acc values of this call live in `a` (not yet in registers)
+  if (tid == 0) s_mask0 = mask[t];
+  __syncthreads();
+  uint32_t m_now = s_mask0;
+  bool started = m_now != 0u;  // acc[t] holds earlier results
+  while (true) {
+    // collect the next batch of up to kMaxChain arrivals with the smallest indices > lo
+    if (tid == 0) {
+      int n = 0, more = 0, c = cursor;
+      // the list is in push order; walk all of it, keep the kMaxChain smallest above lo
+      int* buf = s_buf;
+      while (c >= 0) {
+        if (c > lo) {
+          if (n < kMaxChain) {
+            buf[n++] = c;
+          } else {
+            int mx = 0;
+            for (int q = 1; q < n; ++q) mx = buf[q] > buf[mx] ? q : mx;
+            if (c < buf[mx]) buf[mx] = c;
+            more = 1;
+          }
+        }
+        c = next[c];
+      }
+      for (int q = 1; q < n; ++q) {  // insertion sort, ascending arrival index
+        const int v = buf[q];
+        int p = q - 1;
+        while (p >= 0 && buf[p] > v) {
+          buf[p + 1] = buf[p];
+          --p;
+        }
+        buf[p + 1] = v;
+      }
+      // accept in index order; duplicates of held positions are rejected
+      uint32_t mk = m_now;
+      unsigned flag = 0u;
+      int na = 0;
+      for (int q = 0; q < n; ++q) {
+        const uint32_t bit = 1u << kslot[buf[q]];
+        if (mk & bit) {
+          flag |= MOE_ERR_DUPLICATE;
+        } else {
+          mk |= bit;
+          s_list[na++] = buf[q];
+        }
+      }
+      if (flag) atomicOr(err, flag);
+      s_n = na;
+      s_more = more;
+      s_first = n ? buf[n - 1] : lo;
+      s_mask1 = mk;
     }
-    if (lane == 0) __hip_atomic_store(&done[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return;
-  }
-  for (int v = lane; v < nv; v += 64) {
-    float x[8];
-    RowIO<TR>::load8(src + v * 8, x);
+    __syncthreads();
+    const int na = s_n;
+    const bool more = s_more;
+    const uint32_t m_new = s_mask1;
+    const bool complete = !more && m_new == full;
+    for (int v = tid; v < nv; v += kCmbThreads) {
+      float sum[8];
+      if (started || have) {
+        RowIO<float>::load8(a + v * 8, sum);
+      } else {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) unsafeAtomicAdd(a + v * 8 + k, w * x[k]);
+        for (int k = 0; k < 8; ++k) sum[k] = 0.f;
+      }
+      for (int q = 0; q < na; ++q) {
+        const int arr = s_list[q];
+        const float w = wgt[arr];
+        float x[8];
+        RowIO<TR>::load8(rows + (int64_t)row_idx[arr] * row_pitch + v * 8, x);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sum[k] = fmaf(w, x[k], sum[k]);
+      }
+      if (complete) RowIO<TO>::store8(o + v * 8, sum);
+      else RowIO<float>::store8(a + v * 8, sum);
+    }
+    have = have || na > 0;
+    m_now = m_new;
+    lo = s_first;
+    __syncthreads();
+    if (!more) break;
   }
-  __threadfence();  // release: this result's additions are visible before done[t] moves
-  uint32_t prev = 0u;
-  if (lane == 0) prev = atomicAdd(&done[t], 1u);
-  prev = __shfl(prev, 0);
-  if (prev != (uint32_t)(K - 1)) return;
-  __threadfence();  // acquire: all K results are in acc[t]
-  for (int v = lane; v < nv; v += 64) {
-    float s[8];
-    RowIO<float>::load8(a + v * 8, s);
-    RowIO<TO>::store8(o + v * 8, s);
-    const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    RowIO<float>::store8(a + v * 8, z);
+  if (tid == 0) {
+    head[t] = -1;
+    if (m_now == full) {
+      mask[t] = 0u;
+      tgen[t] = tgen[t] + 1u;
+      rflag[t] = 1;
+    } else {
+      mask[t] = m_now;
+    }
   }
-  if (lane == 0) __hip_atomic_store(&done[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 constexpr int kRelThreads = 1024;
 
-__global__ __launch_bounds__(kRelThreads) void combine_release_kernel(int K, uint32_t* __restrict__ mask,
-                                                                      uint32_t* __restrict__ tgen,
-                                                                      int32_t* __restrict__ span,
+// Kernel 3: ascending compaction of the tokens whose release flag is set: 16 flags per
+// thread per pass (one 16-byte load), a workgroup-wide exclusive scan of the per-thread
+// counts, then each thread writes its tokens in order and clears their flags.
+__global__ __launch_bounds__(kRelThreads) void combine_release_kernel(int T_cap, uint8_t* __restrict__ rflag,
                                                                       int32_t* __restrict__ rel_list,
                                                                       int32_t* __restrict__ rel_count) {
   __shared__ int s_wtot[kRelThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int lo = span[0], hi = span[1];
-  const uint32_t full = K >= 32 ? 0xffffffffu : ((1u << K) - 1u);
+  const int nvec = (T_cap + 15) >> 4;
   int base = 0;
-  for (int t0 = lo; t0 <= hi; t0 += kRelThreads) {  // empty when nothing was accepted
-    const int t = t0 + tid;
-    const bool rel = t <= hi && mask[t] == full;
-    const uint64_t bal = __ballot(rel);
-    if (lane == 0) s_wtot[wv] = __popcll(bal);
+  for (int v0 = 0; v0 < nvec; v0 += kRelThreads) {
+    const int v = v0 + tid;
+    uint4 f = make_uint4(0u, 0u, 0u, 0u);
+    if (v < nvec) f = reinterpret_cast<const uint4*>(rflag)[v];
+    const uint32_t fw[4] = {f.x, f.y, f.z, f.w};
+    int cnt = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) cnt += __popc(fw[k] & 0x01010101u);
+    int incl = cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int x = __shfl_up(incl, d);
+      if (lane >= d) incl += x;
+    }
+    if (lane == 63) s_wtot[wv] = incl;
     __syncthreads();
     int before = 0, total = 0;
 #pragma unroll
@@ -175,58 +250,61 @@ __global__ __launch_bounds__(kRelThreads) void combine_release_kernel(int K, uin
       before += w < wv ? c : 0;
       total += c;
     }
-    if (rel) {
-      rel_list[base + before + __popcll(bal & ((1ull << lane) - 1ull))] = t;
-      mask[t] = 0u;
-      tgen[t] = tgen[t] + 1u;
+    if (cnt) {
+      int o = base + before + incl - cnt;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        if ((fw[k >> 2] >> (8 * (k & 3))) & 1u) {
+          const int t = v * 16 + k;
+          rel_list[o++] = t;
+        }
+      }
+      reinterpret_cast<uint4*>(rflag)[v] = make_uint4(0u, 0u, 0u, 0u);
     }
     base += total;
     __syncthreads();
   }
-  if (tid == 0) {
-    *rel_count = base;
-    span[0] = 0x7fffffff;
-    span[1] = -1;
-  }
+  if (tid == 0) *rel_count = base;
 }
 
 __global__ __launch_bounds__(256) void state_reset_kernel(float* __restrict__ acc, int64_t n_acc,
-                                                          uint32_t* __restrict__ mask, uint32_t* __restrict__ done,
-                                                          uint32_t* __restrict__ tgen, int32_t* __restrict__ span,
+                                                          uint32_t* __restrict__ mask, int32_t* __restrict__ head,
+                                                          uint32_t* __restrict__ tgen, uint8_t* __restrict__ rflag,
                                                           int T_cap, uint32_t gen0) {
   const int64_t stride = (int64_t)gridDim.x * 256;
   for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < n_acc; x += stride) acc[x] = 0.f;
   for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < T_cap; x += stride) {
     mask[x] = 0u;
-    done[x] = 0u;
+    head[x] = -1;
     tgen[x] = gen0;
   }
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    span[0] = 0x7fffffff;
-    span[1] = -1;
-  }
+  const int64_t nf = ((int64_t)T_cap + 15) / 16 * 16;
+  for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < nf; x += stride) rflag[x] = 0;
 }
 
 template <typename TR, typename TO>
-static void launch_arrive(const moe_combine_args* a, hipStream_t stream) {
+static void launch_merge(const moe_combine_args* a, hipStream_t stream) {
   const moe_combine_state& s = a->state;
-  const unsigned blocks = (unsigned)((a->m + kCmbWavesPerBlock - 1) / kCmbWavesPerBlock);
-  hipLaunchKernelGGL((combine_arrive_kernel<TR, TO>), dim3(blocks), dim3(64 * kCmbWavesPerBlock), 0, stream, a->m,
-                     a->K, s.H, (const TR*)a->rows, a->row_pitch, a->n_rows, a->row_idx, a->tok, a->kslot, a->w,
-                     a->gen, s.acc, s.mask, s.done, s.tgen, s.span, s.T_cap, (TO*)a->out, a->out_pitch, a->err);
+  hipLaunchKernelGGL((combine_merge_kernel<TR, TO>), dim3((unsigned)a->m), dim3(kCmbThreads), 0, stream, a->K, s.H,
+                     (const TR*)a->rows, a->row_pitch, a->row_idx, a->tok, a->kslot, a->w, s.acc, s.mask, s.tgen,
+                     s.rflag, s.head, (const int32_t*)a->workspace, (TO*)a->out, a->out_pitch, a->err);
 }
 
 static int check_state(const moe_combine_state* s) {
   if (s->T_cap < 1 || s->T_cap > (1 << 30) || s->H < 8) return MOE_EINVAL_SIZE;
   if (s->H % 8) return MOE_EINVAL_SHAPE;
-  if (!s->acc || !s->mask || !s->done || !s->tgen || !s->span) return MOE_EINVAL_NULL;
-  if (!aligned16(s->acc)) return MOE_EINVAL_ALIGN;
+  if (!s->acc || !s->mask || !s->head || !s->tgen || !s->rflag) return MOE_EINVAL_NULL;
+  if (!aligned16(s->acc) || !aligned16(s->rflag)) return MOE_EINVAL_ALIGN;
   return MOE_OK;
 }
 
 }  // namespace moe
 
 using namespace moe;
+
+extern "C" size_t moe_combine_workspace_size(int32_t m_max) {
+  return m_max <= 0 ? 16 : ((size_t)m_max * 4 + 15) / 16 * 16;
+}
 
 extern "C" int moe_state_reset(const moe_combine_state* st, uint32_t gen0, hipStream_t stream) {
   if (!st) return MOE_EINVAL_NULL;
@@ -236,7 +314,7 @@ extern "C" int moe_state_reset(const moe_combine_state* st, uint32_t gen0, hipSt
   int64_t blocks = (n_acc + 255) / 256;
   if (blocks > 16384) blocks = 16384;
   hipLaunchKernelGGL(state_reset_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, st->acc, n_acc, st->mask,
-                     st->done, st->tgen, st->span, st->T_cap, gen0);
+                     st->head, st->tgen, st->rflag, st->T_cap, gen0);
   return launch_status();
 }
 
@@ -256,13 +334,18 @@ extern "C" int moe_combine_release(const moe_combine_args* a, hipStream_t stream
     if ((a->row_pitch * rs) % 16 || (a->out_pitch * os) % 16 || !aligned16(a->out) ||
         (a->rows && !aligned16(a->rows)))
       return MOE_EINVAL_ALIGN;
+    if (!a->workspace || a->workspace_bytes < moe_combine_workspace_size(a->m)) return MOE_EWORKSPACE;
     const bool rb = a->row_dtype == MOE_BF16, ob = a->out_dtype == MOE_BF16;
-    if (rb && ob) launch_arrive<uint16_t, uint16_t>(a, stream);
-    else if (rb) launch_arrive<uint16_t, float>(a, stream);
-    else if (ob) launch_arrive<float, uint16_t>(a, stream);
-    else launch_arrive<float, float>(a, stream);
+    const moe_combine_state& s = a->state;
+    hipLaunchKernelGGL(combine_link_kernel, dim3((unsigned)((a->m + 255) / 256)), dim3(256), 0, stream, a->m, a->K,
+                       a->n_rows, a->row_idx, a->tok, a->kslot, a->gen, s.tgen, s.T_cap, s.head,
+                       (int32_t*)a->workspace, a->err);
+    if (rb && ob) launch_merge<uint16_t, uint16_t>(a, stream);
+    else if (rb) launch_merge<uint16_t, float>(a, stream);
+    else if (ob) launch_merge<float, uint16_t>(a, stream);
+    else launch_merge<float, float>(a, stream);
   }
-  hipLaunchKernelGGL(combine_release_kernel, dim3(1), dim3(kRelThreads), 0, stream, a->K, a->state.mask,
-                     a->state.tgen, a->state.span, a->rel_list, a->rel_count);
+  hipLaunchKernelGGL(combine_release_kernel, dim3(1), dim3(kRelThreads), 0, stream, a->state.T_cap, a->state.rflag,
+                     a->rel_list, a->rel_count);
   return launch_status();
 }

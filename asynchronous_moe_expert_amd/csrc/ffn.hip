@@ -27,10 +27,12 @@
 
 namespace moe {
 
-constexpr int kBM = 64;        // rows per work unit
-constexpr int kBN = 64;        // packed output columns per work unit
 constexpr int kBK = 64;        // contraction per k-step
 constexpr int kFfnWaves = 4;
+#ifndef MOE_FFN_STAGES
+#define MOE_FFN_STAGES 2
+#endif
+constexpr int kStages = MOE_FFN_STAGES;  // register-ring depth of the weight/activation stream
 
 // ------------------------------------------------------------------------- packing
 template <typename T>
@@ -94,10 +96,6 @@ __global__ __launch_bounds__(256) void down_f32_kernel(const float* __restrict__
 }
 
 // -------------------------------------------------------------- bf16 / fp8 MFMA path
-struct BFrag {
-  bf16x8 v[2];
-};
-
 // Widen 8 e4m3 codes (two dwords) to 8 bf16 values (exact).
 __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
   const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
@@ -115,18 +113,17 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
   return r;
 }
 
-template <int WDT>
-struct WTile;  // registers holding one k-step of the 4 weight strips
+template <int WDT, int NS>
+struct WTile;  // one k-step of NS weight strips, as loaded (16 bytes per lane per run)
 
-template <>
-struct WTile<MOE_BF16> {
-  uint4 raw[4][2];
-  __device__ __forceinline__ void load(const char* __restrict__ strip0, int64_t strip_stride, int lane) {
+template <int NS>
+struct WTile<MOE_BF16, NS> {
+  uint4 raw[NS][2];
+  __device__ __forceinline__ void load(const char* __restrict__ p, int64_t strip_stride) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const char* p = strip0 + s * strip_stride + lane * 16;
-      raw[s][0] = *reinterpret_cast<const uint4*>(p);
-      raw[s][1] = *reinterpret_cast<const uint4*>(p + 1024);
+    for (int s = 0; s < NS; ++s) {
+      raw[s][0] = *reinterpret_cast<const uint4*>(p + s * strip_stride);
+      raw[s][1] = *reinterpret_cast<const uint4*>(p + s * strip_stride + 1024);
     }
   }
   __device__ __forceinline__ bf16x8 frag(int s, int h) const {
@@ -136,30 +133,50 @@ struct WTile<MOE_BF16> {
   }
 };
 
-template <>
-struct WTile<MOE_FP8_E4M3> {
-  uint4 raw[4];
-  __device__ __forceinline__ void load(const char* __restrict__ strip0, int64_t strip_stride, int lane) {
+template <int NS>
+struct WTile<MOE_FP8_E4M3, NS> {
+  uint4 raw[NS];
+  __device__ __forceinline__ void load(const char* __restrict__ p, int64_t strip_stride) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) raw[s] = *reinterpret_cast<const uint4*>(strip0 + s * strip_stride + lane * 16);
+    for (int s = 0; s < NS; ++s) raw[s] = *reinterpret_cast<const uint4*>(p + s * strip_stride);
   }
   __device__ __forceinline__ bf16x8 frag(int s, int h) const {
     return h == 0 ? e4m3x8_to_bf16(raw[s].x, raw[s].y) : e4m3x8_to_bf16(raw[s].z, raw[s].w);
   }
 };
 
+template <int MT>
 struct ATile {
-  uint4 raw[4][2];
+  uint4 raw[MT][2];
+  __device__ __forceinline__ void load(const uint16_t* const* arow, int k0) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const uint4* p = reinterpret_cast<const uint4*>(arow[mt] + k0);
+      raw[mt][0] = p[0];
+      raw[mt][1] = p[1];
+    }
+  }
 };
 
 // MODE 0: gate/up GEMM + SwiGLU epilogue -> h [n][I];  MODE 1: down GEMM -> y [n][H].
-template <int MODE, int WDT>
-__global__ __launch_bounds__(256) void ffn_mfma_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets,
+// A work unit is MT*16 rows of one expert x NS*16 packed output columns.
+template <int MODE, int WDT, int NS, int MT>
+#ifndef MOE_FFN_WPE
+#define MOE_FFN_WPE 0  // > 0: ask the compiler for this many waves per SIMD
+#endif
+#if MOE_FFN_WPE > 0
+#define MOE_FFN_OCC __attribute__((amdgpu_waves_per_eu(MOE_FFN_WPE, MOE_FFN_WPE)))
+#else
+#define MOE_FFN_OCC
+#endif
+__global__ __launch_bounds__(256) MOE_FFN_OCC void ffn_mfma_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets,
                                                        int E_loc, const char* __restrict__ W,
                                                        const float* __restrict__ s0, const float* __restrict__ s1,
                                                        uint16_t* __restrict__ out, int Kd, int Nw, int out_ld,
                                                        int n_blocks_N, int chunks_max, int n_rows) {
-  __shared__ f32x4 red[kFfnWaves - 1][4][4][64];
+  constexpr int BM = MT * 16;
+  static_assert(MODE == 1 || NS % 2 == 0, "gate/up tiles pair gate and up strips");
+  __shared__ f32x4 red[kFfnWaves - 1][MT][NS][64];
   constexpr int esz = WDT == MOE_FP8_E4M3 ? 1 : 2;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
 
@@ -175,127 +192,125 @@ __global__ __launch_bounds__(256) void ffn_mfma_kernel(const uint16_t* __restric
   for (e = 0; e < E_loc; ++e) {
     // clamp to [0, n_rows] so that inconsistent offsets can never address past the batch
     const int a0 = min(max(offsets[e], 0), n_rows), a1 = min(max(offsets[e + 1], a0), n_rows);
-    const int nc = (a1 - a0 + kBM - 1) / kBM;
+    const int nc = (a1 - a0 + BM - 1) / BM;
     if (c < nc) {
-      m0 = a0 + c * kBM;
-      mend = min(a1, m0 + kBM);
+      m0 = a0 + c * BM;
+      mend = min(a1, m0 + BM);
       found = true;
       break;
     }
     c -= nc;
   }
   if (!found) return;
-  const int mt_active = (mend - m0 + 15) >> 4;
   const int KS = Kd / kBK;
 
-  // weight tile: strips 4nb..4nb+3 of expert e; block (strip, ks) at (strip*KS + ks) KiB-blocks
+  // weight strips NS*nb .. NS*nb+NS-1 of expert e; block (strip, ks) at (strip*KS + ks) blocks
   const int64_t blk_bytes = 1024 * esz;
-  const char* wexp = W + (int64_t)e * Nw * Kd * esz;
   const int64_t strip_stride = (int64_t)KS * blk_bytes;
-  const char* wstrip0 = wexp + (int64_t)(nb * 4) * strip_stride;
+  const char* wlane = W + (int64_t)e * Nw * Kd * esz + (int64_t)(nb * NS) * strip_stride + lane * 16;
 
-  // activation rows: lane -> row m0 + 16mt + lane%16 (clamped into the chunk), 32 bytes at
+  // activation rows: lane -> row m0 + 16mt + lane%16 (clamped into the chunk; rows past the
+  // chunk are computed on a copy of its last row and never stored), 32 bytes at
   // k = 64ks + 16*(lane/16)
-  const uint16_t* arow[4];
+  const uint16_t* arow[MT];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int mt = 0; mt < MT; ++mt) {
     int r = m0 + mt * 16 + (lane & 15);
     r = r < mend ? r : mend - 1;
     arow[mt] = A + (int64_t)r * Kd + (lane >> 4) * 16;
   }
 
-  f32x4 acc[4][4];
+  f32x4 acc[MT][NS];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NS; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  WTile<WDT> wc, wn;
-  ATile ac, an;
-  auto load_a = [&](ATile& t, int ks) {
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      if (mt < mt_active) {
-        const uint4* p = reinterpret_cast<const uint4*>(arow[mt] + ks * kBK);
-        t.raw[mt][0] = p[0];
-        t.raw[mt][1] = p[1];
-      }
-    }
-  };
-  auto compute = [&](const WTile<WDT>& wt, const ATile& at) {
+  auto compute = [&](const WTile<WDT, NS>& wt, const ATile<MT>& at) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      bf16x8 bf[4];
+      bf16x8 bf[NS];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) bf[s] = wt.frag(s, h);
+      for (int s = 0; s < NS; ++s) bf[s] = wt.frag(s, h);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        if (mt < mt_active) {
-          bf16x8 af;
-          __builtin_memcpy(&af, &at.raw[mt][h], 16);
+      for (int mt = 0; mt < MT; ++mt) {
+        bf16x8 af;
+        __builtin_memcpy(&af, &at.raw[mt][h], 16);
 #pragma unroll
-          for (int s = 0; s < 4; ++s) acc[mt][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[s], acc[mt][s], 0, 0, 0);
-        }
+        for (int s = 0; s < NS; ++s) acc[mt][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[s], acc[mt][s], 0, 0, 0);
       }
     }
   };
 
-  int ks = wv;
-  if (ks < KS) {
-    wc.load(wstrip0 + ks * blk_bytes, strip_stride, lane);
-    load_a(ac, ks);
-  }
-  for (; ks < KS; ks += kFfnWaves) {
-    const int kn = ks + kFfnWaves;
-    if (kn < KS) {
-      wn.load(wstrip0 + kn * blk_bytes, strip_stride, lane);
-      load_a(an, kn);
+  // this wave's k-steps are wv, wv+4, ...; a ring of kStages register sets keeps the loads
+  // of the next kStages-1 steps in flight while the current step feeds the MFMAs.  Loads
+  // past the end are clamped to the last step (valid memory, result unused), so no load is
+  // conditional; the scheduling barriers keep each prefetch batch ahead of the MFMAs.
+  const int nsteps = KS > wv ? (KS - wv + kFfnWaves - 1) / kFfnWaves : 0;
+  auto kstep = [&](int i) { return min(wv + kFfnWaves * i, KS - 1); };
+  if (nsteps > 0) {
+    WTile<WDT, NS> wr[kStages];
+    ATile<MT> ar[kStages];
+#pragma unroll
+    for (int u = 0; u < kStages - 1; ++u) {
+      wr[u].load(wlane + kstep(u) * blk_bytes, strip_stride);
+      ar[u].load(arow, kstep(u) * kBK);
     }
-    compute(wc, ac);
-    wc = wn;
-    ac = an;
+    int it = 0;
+#pragma clang loop unroll(disable)
+    for (; it + kStages <= nsteps; it += kStages) {
+#pragma unroll
+      for (int u = 0; u < kStages; ++u) {
+        const int ld = (u + kStages - 1) % kStages;
+        wr[ld].load(wlane + kstep(it + u + kStages - 1) * blk_bytes, strip_stride);
+        ar[ld].load(arow, kstep(it + u + kStages - 1) * kBK);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(wr[u], ar[u]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    const int rest = nsteps - it;  // < kStages; those steps sit in ring slots 0..rest-1
+#pragma unroll
+    for (int u = 0; u < kStages - 1; ++u)
+      if (u < rest) compute(wr[u], ar[u]);
   }
 
   // split-k reduction: waves 1..3 park their partial tiles in LDS, wave 0 sums
   if (wv > 0) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-      if (mt < mt_active)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) red[wv - 1][mt][s][lane] = acc[mt][s];
+      for (int s = 0; s < NS; ++s) red[wv - 1][mt][s][lane] = acc[mt][s];
   }
   __syncthreads();
   if (wv != 0) return;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-    if (mt < mt_active)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
+    for (int s = 0; s < NS; ++s)
 #pragma unroll
-        for (int w = 0; w < kFfnWaves - 1; ++w) acc[mt][s] += red[w][mt][s][lane];
+      for (int w = 0; w < kFfnWaves - 1; ++w) acc[mt][s] += red[w][mt][s][lane];
 
   // epilogue; the accumulator of lane l holds column l%16 of a strip and rows 4(l/16)+q
   const int col16 = lane & 15, rq = (lane >> 4) * 4;
   if (MODE == 0) {
     const int I = out_ld;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int i = nb * 32 + p * 16 + col16;
+    for (int p = 0; p < NS / 2; ++p) {
+      const int i = (nb * (NS / 2) + p) * 16 + col16;
       float sg = 1.f, su = 1.f;
       if (WDT == MOE_FP8_E4M3) {
         sg = s0[(int64_t)e * I + i];
         su = s1[(int64_t)e * I + i];
       }
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        if (mt < mt_active) {
+      for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int row = m0 + mt * 16 + rq + q;
-            if (row < mend) {
-              const float g = acc[mt][2 * p][q] * sg, u = acc[mt][2 * p + 1][q] * su;
-              out[(int64_t)row * I + i] = f32_to_bf16(silu_mul(g, u));
-            }
+        for (int q = 0; q < 4; ++q) {
+          const int row = m0 + mt * 16 + rq + q;
+          if (row < mend) {
+            const float g = acc[mt][2 * p][q] * sg, u = acc[mt][2 * p + 1][q] * su;
+            out[(int64_t)row * I + i] = f32_to_bf16(silu_mul(g, u));
           }
         }
       }
@@ -303,32 +318,63 @@ __global__ __launch_bounds__(256) void ffn_mfma_kernel(const uint16_t* __restric
   } else {
     const int H = out_ld;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int col = nb * 64 + s * 16 + col16;
+    for (int s = 0; s < NS; ++s) {
+      const int col = (nb * NS + s) * 16 + col16;
       const float sc = WDT == MOE_FP8_E4M3 ? s0[(int64_t)e * H + col] : 1.f;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        if (mt < mt_active) {
+      for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int row = m0 + mt * 16 + rq + q;
-            if (row < mend) out[(int64_t)row * H + col] = f32_to_bf16(acc[mt][s][q] * sc);
-          }
+        for (int q = 0; q < 4; ++q) {
+          const int row = m0 + mt * 16 + rq + q;
+          if (row < mend) out[(int64_t)row * H + col] = f32_to_bf16(acc[mt][s][q] * sc);
         }
       }
     }
   }
 }
 
+template <int MODE, int WDT, int NS, int MT>
+static void launch_mfma_t(const void* A, const int32_t* offsets, int E_loc, const void* W, const float* s0,
+                          const float* s1, void* out, int Kd, int Nw, int out_ld, int n, hipStream_t stream) {
+  constexpr int BM = MT * 16;
+  const int n_blocks_N = Nw / (16 * NS);
+  const int chunks_max = (n + (BM - 1) * E_loc) / BM;
+  int64_t grid = (int64_t)chunks_max * n_blocks_N;
+  grid = (grid + 7) / 8 * 8;
+  hipLaunchKernelGGL((ffn_mfma_kernel<MODE, WDT, NS, MT>), dim3((unsigned)grid), dim3(256), 0, stream,
+                     (const uint16_t*)A, offsets, E_loc, (const char*)W, s0, s1, (uint16_t*)out, Kd, Nw, out_ld,
+                     n_blocks_N, chunks_max, n);
+}
+
+// Row-chunk height: tall enough that an average expert group fits one chunk with room for
+// the spread of a ragged batch (1.5x the mean group), so each weight tile is read once.
+#ifndef MOE_FFN_MT
+#define MOE_FFN_MT 0  // 0: choose from the batch shape
+#endif
+#ifndef MOE_FFN_NS_GU
+#define MOE_FFN_NS_GU 4
+#endif
+#ifndef MOE_FFN_NS_D
+#define MOE_FFN_NS_D 4
+#endif
+
+static int pick_mt(int n, int E_loc) {
+  if (MOE_FFN_MT > 0) return MOE_FFN_MT;
+  const int want = (3 * n + 2 * E_loc - 1) / (2 * E_loc);
+  const int mt = (want + 15) / 16;
+  return mt < 2 ? 2 : (mt > 3 ? 3 : mt);  // taller chunks measured slower at decode sizes
+}
+
 template <int MODE, int WDT>
 static void launch_mfma(const void* A, const int32_t* offsets, int E_loc, const void* W, const float* s0,
                         const float* s1, void* out, int Kd, int Nw, int out_ld, int n, hipStream_t stream) {
-  const int n_blocks_N = Nw / kBN;
-  const int chunks_max = (n + (kBM - 1) * E_loc) / kBM;
-  int64_t grid = (int64_t)chunks_max * n_blocks_N;
-  grid = (grid + 7) / 8 * 8;
-  hipLaunchKernelGGL((ffn_mfma_kernel<MODE, WDT>), dim3((unsigned)grid), dim3(256), 0, stream, (const uint16_t*)A,
-                     offsets, E_loc, (const char*)W, s0, s1, (uint16_t*)out, Kd, Nw, out_ld, n_blocks_N, chunks_max, n);
+  // gate/up: 4 strips (32 gate + 32 up columns) per workgroup; down: 4 strips
+  constexpr int NS = MODE == 0 ? MOE_FFN_NS_GU : MOE_FFN_NS_D;
+  switch (pick_mt(n, E_loc)) {
+    case 2: launch_mfma_t<MODE, WDT, NS, 2>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, stream); break;
+    case 3: launch_mfma_t<MODE, WDT, NS, 3>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, stream); break;
+    default: launch_mfma_t<MODE, WDT, NS, 4>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, stream); break;
+  }
 }
 
 }  // namespace moe

@@ -34,6 +34,8 @@ class ExpertStep:
         self.rel_list = torch.empty(max(T_cap, 1), dtype=torch.int32, device=dev)
         self.rel_count = torch.zeros(1, dtype=torch.int32, device=dev)
         self.state = N.CombineState(T_cap, H, device=dev)
+        self.cmb_ws_m = max(n_max, 1)
+        self.cmb_ws = torch.empty(N.moe_combine_workspace_size(self.cmb_ws_m), dtype=torch.uint8, device=dev)
         self.out = torch.empty((T_cap, H), dtype=adt, device=dev)
         self.w_gu = self.w_d = None
         self.s_gate = self.s_up = self.s_down = None
@@ -58,8 +60,14 @@ class ExpertStep:
 
     def combine(self, rows, row_idx, tok, kslot, w, gen, m: int | None = None, n_rows: int | None = None,
                 stream=None) -> None:
+        m = int(tok.numel() if m is None else m)
+        if m > self.cmb_ws_m:  # plumbing: grow the caller-owned scratch (outside any timed loop)
+            self.cmb_ws_m = m
+            self.cmb_ws = torch.empty(N.moe_combine_workspace_size(m), dtype=torch.uint8, device=self.cmb_ws.device)
+        if m > self.rel_list.numel():
+            self.rel_list = torch.empty(m, dtype=torch.int32, device=self.rel_list.device)
         N.moe_combine_release(rows, row_idx, tok, kslot, w, gen, self.K, self.state, self.out, self.rel_list,
-                              self.rel_count, self.err, m=m, n_rows=n_rows, stream=stream)
+                              self.rel_count, self.err, self.cmb_ws, m=m, n_rows=n_rows, stream=stream)
 
     def run(self, slot, expert, expert_base: int, pool, tok, kslot, w, gen, n: int | None = None,
             ev_mid: int | None = None, stream=None) -> None:

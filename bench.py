@@ -1,0 +1,231 @@
+"""Benchmark: one expert-parallel rank's expert step on one MI355X.
+
+Workload (decode-shaped rank share): 128 experts, top-4, 16 ranks -> 8 local experts,
+hidden 2880, SwiGLU intermediate 2880, bf16; 256 token-expert pairs gathered from random
+slots of a 4096-slot token pool, uniform routing, weights ~ N(0, 0.02).
+
+A step = moe_assemble + moe_expert_ffn_grouped + moe_combine_release on one batch, all
+inputs resident in HBM.  Each step combines its local results into tokens of its own
+(distinct state indices per step), whose results from the other 15 ranks were delivered
+before the timed region; every step therefore releases all of its tokens.
+
+Prints one JSON line with the step throughput (expert tokens/s), the roofline of the
+dominant kernel (the gate/up GEMM, timed with HIP events on the launch stream) and the
+CPU oracle timed on a bounded sample on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_ffn_gateup_decode.json")
+FFN_SRC = os.path.join(ROOT, "asynchronous_moe_expert_amd", "csrc", "ffn.hip")
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (the library records one between its two FFN kernels)."""
+
+    def __init__(self):
+        self.hip = C.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.hip.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [C.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [C.c_void_p]
+
+    def create(self) -> int:
+        e = C.c_void_p()
+        assert self.hip.hipEventCreate(C.byref(e)) == 0
+        return e.value
+
+    def record(self, ev: int, stream: int) -> None:
+        assert self.hip.hipEventRecord(C.c_void_p(ev), C.c_void_p(stream)) == 0
+
+    def ms(self, a: int, b: int) -> float:
+        self.hip.hipEventSynchronize(C.c_void_p(b))
+        out = C.c_float()
+        assert self.hip.hipEventElapsedTime(C.byref(out), C.c_void_p(a), C.c_void_p(b)) == 0
+        return float(out.value)
+
+
+def stored_traffic(per_launch_bytes: float):
+    """HBM traffic of the gate/up kernel from the committed rocprofv3 counter summary, if it
+    was taken on the kernel source as it is now (else null)."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        src = hashlib.sha256(open(FFN_SRC, "rb").read()).hexdigest()
+        if t.get("ffn_hip_sha256") != src:
+            return None
+        return float(t["fetch_bytes_per_launch"]) + float(t["write_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(b, wts, seconds: float) -> dict:
+    """The oracle (fp64 numpy) on the host: whole decode steps, repeated until `seconds`."""
+    import threadpoolctl
+
+    import oracle as O
+
+    info = threadpoolctl.threadpool_info()
+    cores = max([i.get("num_threads", 1) for i in info] or [1])
+    r = b.remote
+    rows_remote = O.decode(r.rows, r.dtype)
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        a = O.assemble(b.slot, b.expert, b.expert_base, b.E_loc, b.P)
+        xb = O.decode(O.gather_rows(b.pool, b.slot, a["perm"], b.n), b.act)
+        y = O.expert_ffn(xb, a["offsets"], wts)
+        cs = O.CombineState(b.T, b.K)
+        O.combine_release(cs, rows_remote, r.row_idx, r.tok, r.kslot, r.w, r.gen)
+        O.combine_release(cs, y, a["pos"], b.tok, b.kslot, b.w, b.gen)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": b.n * reps / el, "unit": "expert tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{reps} whole decode steps of {b.n} token-expert pairs (assemble, fp64 SwiGLU FFN over "
+                      f"8 experts, combine incl. the delivery of the remote results), {el:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle CPU-baseline budget (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs one expert-parallel rank's share on a single GPU; multi-GPU runs are not part "
+              "of this build (use --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import asynchronous_moe_expert_amd as M
+    import workloads as W
+    from workloads.device import batch_tensors, weight_tensors
+
+    M.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    b, wts = W.c1_decode()
+    K_steps, W_steps = args.steps, args.warmup
+    S = W_steps + 2 * K_steps  # warmup, the timed loop, then the loop timed per stage
+    d = batch_tensors(b)
+    wt = weight_tensors(wts)
+    st = M.ExpertStep(b.E_loc, b.H, wts.I, b.K, M.MOE_BF16, M.MOE_BF16, b.n, S * b.T)
+    st.load_weights(wt["wg"], wt["wu"], wt["wd"])
+    del wt
+    # per-step token indices (each step completes tokens of its own) and the remote
+    # results of every step's tokens, delivered before timing
+    tok_steps = [d["tok"] + s * b.T for s in range(S)]
+    r_tok = torch.cat([d["r_tok"] + s * b.T for s in range(S)])
+    rep = lambda x: torch.cat([x] * S)  # noqa: E731
+    st.combine(d["r_rows"], rep(d["r_idx"]), r_tok, rep(d["r_kslot"]), rep(d["r_w"]), rep(d["r_gen"]))
+    torch.cuda.synchronize()
+    assert int(st.rel_count.item()) == 0
+
+    ev = HipEvents()
+    stream = torch.cuda.current_stream().cuda_stream
+    e_asm = [ev.create() for _ in range(S)]
+    e_mid = [ev.create() for _ in range(S)]
+    e_ffn = [ev.create() for _ in range(S)]
+    e_end = [ev.create() for _ in range(S)]
+    e_start = ev.create()
+
+    def step(s: int) -> None:
+        st.run(d["slot"], d["expert"], b.expert_base, d["pool"], tok_steps[s], d["kslot"], d["w"], d["gen"], n=b.n)
+
+    def step_timed(s: int) -> None:
+        # the same three calls with HIP events between them on the launch stream
+        st.assemble(d["slot"], d["expert"], b.expert_base, d["pool"])
+        ev.record(e_asm[s], stream)
+        st.ffn(b.n, ev_mid=e_mid[s])
+        ev.record(e_ffn[s], stream)
+        st.combine(st.y, st.pos, tok_steps[s], d["kslot"], d["w"], d["gen"], m=b.n, n_rows=b.n)
+        ev.record(e_end[s], stream)
+
+    for s in range(W_steps):
+        step(s)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for s in range(W_steps, W_steps + K_steps):
+        step(s)
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    assert int(st.err.item()) == 0, "device error flags raised"
+    assert int(st.rel_count.item()) == b.T
+
+    timed = range(W_steps + K_steps, S)
+    ev.record(e_start, stream)
+    for s in timed:
+        step_timed(s)
+    torch.cuda.synchronize()
+    assert int(st.err.item()) == 0 and int(st.rel_count.item()) == b.T
+    prev = [e_start] + [e_end[s] for s in timed][:-1]
+    asm_ms = np.mean([ev.ms(p, e_asm[s]) for p, s in zip(prev, timed)])
+    gu_ms = np.mean([ev.ms(e_asm[s], e_mid[s]) for s in timed])
+    dn_ms = np.mean([ev.ms(e_mid[s], e_ffn[s]) for s in timed])
+    cb_ms = np.mean([ev.ms(e_ffn[s], e_end[s]) for s in timed])
+
+    counts = st.counts.cpu().numpy()
+    active = int((counts > 0).sum())
+    H, I, n = b.H, wts.I, b.n
+    gu_bytes = active * 2 * H * I * 2 + n * H * 2 + n * I * 2
+    gu_flops = 4.0 * n * H * I
+    achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
+    ms_step = total_ms / K_steps
+    value = n * K_steps / (total_ms * 1e-3)
+    out = {
+        "metric": "expert tokens/sec per GPU (assemble+FFN+combine)",
+        "value": round(value, 1),
+        "unit": "expert tokens/s",
+        "n_gpus": 1,
+        "steps": K_steps,
+        "warmup": W_steps,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; random-init expert weights)",
+        "config": {"workload": "decode-shaped EP rank share: 8 of 128 experts, top-4, hidden 2880, SwiGLU "
+                               "intermediate 2880, 256 token-expert pairs from a 4096-slot token pool",
+                   "E_loc": b.E_loc, "K": b.K, "H": H, "I": I, "pairs": n, "tokens": b.T, "pool_slots": b.P},
+        "roofline": {"bound": "hbm", "kernel": "ffn_mfma_kernel<gate/up, bf16>", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": stored_traffic(gu_bytes), "algorithmic_bytes": gu_bytes,
+                     "mfma_frac": round(gu_flops / (gu_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 5)},
+        "stages_us": {"assemble": round(asm_ms * 1e3, 2), "ffn_gate_up": round(gu_ms * 1e3, 2),
+                      "ffn_down": round(dn_ms * 1e3, 2), "combine": round(cb_ms * 1e3, 2),
+                      "note": "second K-step loop with HIP events between the calls (events add a "
+                              "few us of launch latency to each interval); value is from the loop without"},
+    }
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(b, wts, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

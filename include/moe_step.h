@@ -173,18 +173,20 @@ int moe_expert_ffn_grouped(const moe_ffn_args* args, hipStream_t stream);
 
 /* ------------------------------------------------------------- moe_combine_release --
  * Per-token combine state of the home rank (all device memory, caller-owned):
- *   acc[t][H]  fp32 running sum of accepted w_j * E_j(x); all zero while mask[t] == 0
+ *   acc[t][H]  fp32 running sum of the accepted w_j * E_j(x); meaningful only while
+ *              mask[t] != 0 (a token with no held result starts from zero)
  *   mask[t]    bit j set once the result for top-k position j was accepted
- *   done[t]    accepted results whose accumulation finished (internal; 0 between calls)
  *   tgen[t]    generation that the token's next results must carry
- *   span[2]    internal scratch, {INT32_MAX, -1} between calls
+ *   head[t]    internal (arrival list of the running call), -1 between calls
+ *   rflag[]    internal release flags, one byte per token, (T_cap + 15) / 16 * 16 bytes,
+ *              16-byte aligned, all zero between calls
  * moe_state_reset() puts every token in generation `gen0` with nothing accepted. */
 typedef struct moe_combine_state {
   float* acc;
   uint32_t* mask;
-  uint32_t* done;
+  int32_t* head;
   uint32_t* tgen;
-  int32_t* span;
+  uint8_t* rflag;
   int32_t T_cap;           /* tokens the state can hold */
   int32_t H;
 } moe_combine_state;
@@ -201,14 +203,17 @@ int moe_state_reset(const moe_combine_state* st, uint32_t gen0, hipStream_t stre
  * top-k position kslot[i] for token tok[i] in generation gen[i], with router weight w[i].
  * It is rejected (flag raised, no effect) if tok, kslot or row_idx is out of range, if
  * gen[i] != tgen[tok[i]], or if the token already holds position kslot[i] (from an earlier
- * call, or from another arrival of the same call: then exactly one of them is accepted).
+ * call, or from an arrival of the same call with a lower index: the lowest index wins).
  * After the call every token holding all K positions is released:
- *   out[t][:]   = round-to-nearest-even(acc_t) in out_dtype, acc_t = sum_j w_j row_j (fp32)
+ *   out[t][:]   = round-to-nearest-even(acc_t) in out_dtype, where acc_t is the fp32 sum
+ *                 of the held partial sum and this call's w_a * row_a in arrival-index order
+ *                 (the same inputs give the same bits)
  *   rel_list    = released tokens in ascending order, *rel_count of them (device int32)
- *   state       : mask[t] = 0, acc[t] = 0, tgen[t] += 1
+ *   state       : mask[t] = 0, tgen[t] += 1
  * Tokens still missing results keep their partial sums.
  * Limits: 1 <= K <= 32, 0 <= m <= 2^24, H % 8 == 0, rows/out dtypes F32 or BF16,
- * rel_list holds at least min(m, T_cap) entries. */
+ * rel_list holds at least min(m, T_cap) entries; the workspace (device memory, 16-byte
+ * aligned) holds moe_combine_workspace_size(m) bytes. */
 typedef struct moe_combine_args {
   int32_t m;               /* arrivals */
   int32_t K;               /* results per token (top-k) */
@@ -228,7 +233,11 @@ typedef struct moe_combine_args {
   int32_t* rel_list;       /* out */
   int32_t* rel_count;      /* out, device int32 */
   uint32_t* err;           /* device error word (OR-ed) */
+  void* workspace;         /* scratch for the call */
+  size_t workspace_bytes;
 } moe_combine_args;
+
+size_t moe_combine_workspace_size(int32_t m_max);
 
 int moe_combine_release(const moe_combine_args* args, hipStream_t stream);
 

@@ -140,7 +140,8 @@ def _combine_call(st, rows_t, rows64, arr, ocs, K):
     assert np.array_equal(st.rel_list[:n_rel].cpu().numpy(), rel)
     assert np.array_equal(st.state.mask.cpu().numpy().view(np.uint32), ocs.mask)
     assert np.array_equal(st.state.tgen.cpu().numpy().view(np.uint32), ocs.tgen)
-    assert np.all(st.state.done.cpu().numpy() == 0)
+    assert np.all(st.state.head.cpu().numpy() == -1)  # per-call lists are torn down
+    assert np.all(st.state.rflag.cpu().numpy() == 0)
     return out, rel
 
 
@@ -180,10 +181,11 @@ def test_combine_errors_duplicates_and_generations():
     rows_t, rows64 = dev(rows_np), rows_np.astype(np.float64)
     st = M.ExpertStep(1, H, 64, K, M.MOE_F32, M.MOE_F32, 1, T)
     ocs = O.CombineState(T, K)
-    # in-call duplicate with different rows: exactly one is accepted (which one is left open,
-    # so only flags, release lists and state are compared for it)
+    # in-call duplicate with different rows: the lower arrival index wins, as in the oracle
     _combine_call(st, rows_t, rows64, [(0, 0, 0, 1.0, 0), (1, 0, 0, 1.0, 0)], ocs, K)
-    _combine_call(st, rows_t, rows64, [(2, 0, 1, 1.0, 0)], ocs, K)  # releases token 0
+    out, rel = _combine_call(st, rows_t, rows64, [(2, 0, 1, 1.0, 0)], ocs, K)  # releases token 0
+    assert list(rel) == [0]
+    assert np.array_equal(st.out.cpu().numpy()[0].astype(np.float64), out[0])
     _combine_call(st, rows_t, rows64, [(3, 0, 0, 1.0, 0)], ocs, K)  # stale generation
     _combine_call(st, rows_t, rows64, [(3, 9, 0, 1.0, 0), (3, 1, 5, 1.0, 0), (99, 1, 0, 1.0, 0), (-1, 2, 1, 1, 0)],
                   ocs, K)
@@ -192,6 +194,25 @@ def test_combine_errors_duplicates_and_generations():
     assert list(rel) == [5]
     g = st.out.cpu().numpy().astype(np.float64)
     assert np.array_equal(g[5], out[5])  # identical duplicate rows: result independent of the winner
+
+
+def test_combine_long_chain_for_one_token():
+    """More arrivals for one token in one call than the merge takes per pass (64): retries
+    of position 0 interleaved with the other positions, the last position at the end."""
+    _say("combine long chain")
+    K, T, H = 4, 3, 64
+    rng = np.random.default_rng(5)
+    rows_np = rng.integers(-4, 4, size=(200, H)).astype(np.float32)
+    rows_t, rows64 = dev(rows_np), rows_np.astype(np.float64)
+    st = M.ExpertStep(1, H, 64, K, M.MOE_F32, M.MOE_F32, 1, T)
+    ocs = O.CombineState(T, K)
+    arr = [(q, 1, 0, 0.5, 0) for q in range(130)]                 # 130 claims of position 0
+    arr[40] = (40, 1, 1, 0.25, 0)
+    arr[100] = (100, 1, 2, 2.0, 0)
+    arr += [(150, 2, 0, 1.0, 0), (151, 1, 3, 1.0, 0)]             # token 2 stays partial
+    out, rel = _combine_call(st, rows_t, rows64, arr, ocs, K)
+    assert list(rel) == [1]
+    assert np.array_equal(st.out.cpu().numpy()[1].astype(np.float64), out[1])
 
 
 @pytest.mark.parametrize("K", [1, 3, 32])

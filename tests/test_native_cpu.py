@@ -32,7 +32,8 @@ def _declared():
 def test_header_declares_the_three_calls_and_helpers():
     d = _declared()
     for name in ["moe_assemble", "moe_expert_ffn_grouped", "moe_combine_release", "moe_state_reset",
-                 "moe_pack_ffn_weights", "moe_ffn_workspace_size", "moe_strerror", "moe_version", "moe_struct_size"]:
+                 "moe_pack_ffn_weights", "moe_ffn_workspace_size", "moe_combine_workspace_size", "moe_strerror",
+                 "moe_version", "moe_struct_size"]:
         assert name in d
     assert sorted(N.EXPORTS) == d
 
@@ -58,6 +59,7 @@ def test_workspace_size(lib):
     assert M.moe_ffn_workspace_size(64, 8, 64, 128, M.MOE_F32) == 64 * 128 * 4
     assert M.moe_ffn_workspace_size(3, 1, 64, 64, M.MOE_BF16) == 512  # rounded up to 256 B
     assert M.moe_ffn_workspace_size(1, 1, 64, 64, 7) == 0
+    assert M.moe_combine_workspace_size(256) == 1024 and M.moe_combine_workspace_size(3) == 16
 
 
 def test_host_validation_rejects_bad_arguments(lib):
@@ -85,16 +87,21 @@ def test_host_validation_rejects_bad_arguments(lib):
                   w_gu=16, w_d=16, y=16, workspace=16, workspace_bytes=8)
     assert lib.moe_expert_ffn_grouped(C.byref(f), null) == -6  # workspace too small
 
-    st = N.StateC(acc=16, mask=16, done=16, tgen=16, span=16, T_cap=8, H=64)
+    st = N.StateC(acc=16, mask=16, head=16, tgen=16, rflag=16, T_cap=8, H=64)
     c = N.CombineArgs(m=1, K=33, state=st)
     assert lib.moe_combine_release(C.byref(c), null) == -2  # K > 32
     c = N.CombineArgs(m=1, K=4, row_dtype=M.MOE_FP8_E4M3, state=st)
     assert lib.moe_combine_release(C.byref(c), null) == -3
-    st2 = N.StateC(acc=16, mask=16, done=16, tgen=16, span=16, T_cap=8, H=60)
+    st2 = N.StateC(acc=16, mask=16, head=16, tgen=16, rflag=16, T_cap=8, H=60)
     c = N.CombineArgs(m=1, K=4, state=st2)
     assert lib.moe_combine_release(C.byref(c), null) == -5  # H % 8
-    st3 = N.StateC(acc=0, mask=16, done=16, tgen=16, span=16, T_cap=8, H=64)
+    st3 = N.StateC(acc=0, mask=16, head=16, tgen=16, rflag=16, T_cap=8, H=64)
     assert lib.moe_state_reset(C.byref(st3), 0, null) == -1
+
+    c = N.CombineArgs(m=4, K=2, row_dtype=M.MOE_F32, row_pitch=64, n_rows=4, rows=16, row_idx=16, tok=16,
+                      kslot=16, w=16, gen=16, out=16, out_dtype=M.MOE_F32, out_pitch=64, rel_list=16, rel_count=16,
+                      err=16, state=st, workspace=16, workspace_bytes=8)
+    assert lib.moe_combine_release(C.byref(c), null) == -6  # workspace too small for 4 arrivals
 
     p = N.PackArgs(E_loc=2, H=64, I=96, w_dtype=M.MOE_BF16)
     assert lib.moe_pack_ffn_weights(C.byref(p), null) == -5
