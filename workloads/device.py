@@ -48,3 +48,15 @@ def weight_tensors(wts, device="cuda") -> dict:
         d.update(s_gate=tensor(wts.sg, device=device), s_up=tensor(wts.su, device=device),
                  s_down=tensor(wts.sd, device=device))
     return d
+
+
+def device_layer_weights(seed: int, layer: int, E: int, H: int, I: int, sigma: float, device="cuda") -> dict:
+    """One layer's bf16 expert weights drawn on the device with torch's seeded generator
+    (wg, wu: [E][I][H], wd: [E][H][I]); the same (seed, layer) gives the same tensors."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 1000 + int(layer))
+    out = {}
+    for name, shape in (("wg", (E, I, H)), ("wu", (E, I, H)), ("wd", (E, H, I))):
+        t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        out[name] = (t * sigma).to(torch.bfloat16)
+    return out
