@@ -6,29 +6,36 @@
 //
 // Design (gfx950):
 //   * Two launches: gate/up GEMM with the SwiGLU epilogue (writes h), then the down GEMM.
-//   * Work unit = (row chunk of <= 64 rows of one expert, 64 packed output columns).  The
-//     chunk list is derived on the device from `offsets`, so ragged and empty experts need
-//     no host round trip; the grid is sized for the worst case and surplus workgroups exit.
-//   * Each workgroup (4 waves) splits the contraction over its waves (k-steps w, w+4, ...),
-//     streams the 64-column weight tile exactly once from HBM straight into registers
-//     (packed layout: one contiguous 1 KiB run per wave load), and reduces the four partial
-//     tiles through LDS.  At decode sizes (tens of rows per expert) the step is bound by
-//     streaming the expert weights, so the design goal is all CUs reading disjoint weight
-//     bytes with deep load queues; MFMA v_mfma_f32_16x16x32_bf16 does the math.
-//   * The contraction order inside a 64-wide k-step is permuted (lane group g takes 16
-//     consecutive k, split over two MFMAs) so that an activation row is read as 32-byte
-//     runs; the packed weight layout applies the same permutation, so the sums are exact
-//     dot products over all k.
+//   * Work unit = (row chunk of <= 48 rows of one expert, 4 waves x NS weight strips of 16
+//     output columns).  The chunk list is derived on the device from `offsets`, so ragged
+//     and empty experts need no host round trip.  The grid is what the device holds at
+//     once (CUs x occupancy) and strides over the active units only: a decode batch's
+//     units all start in the first round and no workgroup slot is spent on an idle unit.
+//   * At decode sizes (tens of rows per expert) the step is bound by streaming the expert
+//     weights once from HBM.  Each wave owns its strips over the whole contraction and
+//     keeps R-1 k-steps of weight loads in flight in a register ring (packed layout: one
+//     contiguous 1 KiB run per wave load); there is no split-k reduction.  The activation
+//     k-tile is loaded once per workgroup, a quarter per wave issued together with the
+//     weights of the same k-step (loads retire in order, so a shallower activation ring
+//     would drain the weight ring), and shared through a double-buffered LDS tile whose
+//     layout is the MFMA operand order (conflict-free 16-byte reads).
+//   * MFMA v_mfma_f32_16x16x32_bf16 does the math.  The contraction order inside a 64-wide
+//     k-step is permuted (lane group g takes 16 consecutive k, split over two MFMAs); the
+//     packed weight layout and the activation tile apply the same permutation, so the
+//     sums are exact dot products over all k.
 //   * fp8 e4m3 weights are widened to bf16 in registers (exact: every e4m3 value is a
 //     bf16 value) and the per-row scale is applied to the fp32 result in the epilogue.
-//   * Workgroup ids are remapped so that each XCD gets a contiguous range of work units:
-//     chunks sharing a weight tile run on one XCD, back to back (L2 reuse for big experts).
+//   * Units are spread XCD-aware: each XCD gets an equal contiguous range of unit ids, so
+//     the chunks that share a weight tile run on one XCD's L2 (reuse for big experts).
+#include <algorithm>
+#include <type_traits>
+#include <utility>
+
 #include "common.hpp"
 
 namespace moe {
 
 constexpr int kBK = 64;        // contraction per k-step
-constexpr int kFfnWaves = 4;
 #ifndef MOE_FFN_STAGES
 #define MOE_FFN_STAGES 2
 #endif
@@ -145,205 +152,298 @@ struct WTile<MOE_FP8_E4M3, NS> {
   }
 };
 
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>), unrolled at compile time
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// This thread's share of one k-step activation tile (MT*16 rows x 64 k) staged through LDS.
+// Tile piece t (16 bytes) is the MFMA A-operand run of lane t%64 for row tile t/128 and
+// k-half (t/64)%2, so piece t sits at LDS byte 16t and a lane's operand read is one
+// conflict-free 16-byte access at 16*((2mt + h)*64 + lane).
 template <int MT>
-struct ATile {
-  uint4 raw[MT][2];
-  __device__ __forceinline__ void load(const uint16_t* const* arow, int k0) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const uint4* p = reinterpret_cast<const uint4*>(arow[mt] + k0);
-      raw[mt][0] = p[0];
-      raw[mt][1] = p[1];
-    }
+struct APart {
+  static constexpr int kPieces = MT * 128;
+  static constexpr int J = (kPieces + 255) / 256;
+  u32x4 raw[J];
+  __device__ __forceinline__ void load(const uint16_t* const* ap, int k0) {
+    static_for<J>([&](auto j) { raw[j()] = *reinterpret_cast<const u32x4*>(ap[j()] + k0); });
+  }
+  __device__ __forceinline__ void store(u32x4* lds, int tid) const {
+    static_for<J>([&](auto j) {
+      if (j() * 256 + tid < kPieces) lds[j() * 256 + tid] = raw[j()];
+    });
   }
 };
 
-// MODE 0: gate/up GEMM + SwiGLU epilogue -> h [n][I];  MODE 1: down GEMM -> y [n][H].
-// A work unit is MT*16 rows of one expert x NS*16 packed output columns.
-template <int MODE, int WDT, int NS, int MT>
-#ifndef MOE_FFN_WPE
-#define MOE_FFN_WPE 0  // > 0: ask the compiler for this many waves per SIMD
-#endif
-#if MOE_FFN_WPE > 0
-#define MOE_FFN_OCC __attribute__((amdgpu_waves_per_eu(MOE_FFN_WPE, MOE_FFN_WPE)))
-#else
-#define MOE_FFN_OCC
-#endif
-__global__ __launch_bounds__(256) MOE_FFN_OCC void ffn_mfma_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets,
-                                                       int E_loc, const char* __restrict__ W,
-                                                       const float* __restrict__ s0, const float* __restrict__ s1,
-                                                       uint16_t* __restrict__ out, int Kd, int Nw, int out_ld,
-                                                       int n_blocks_N, int chunks_max, int n_rows) {
-  constexpr int BM = MT * 16;
-  static_assert(MODE == 1 || NS % 2 == 0, "gate/up tiles pair gate and up strips");
-  __shared__ f32x4 red[kFfnWaves - 1][MT][NS][64];
-  constexpr int esz = WDT == MOE_FP8_E4M3 ? 1 : 2;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+// Active work units of a ragged batch, found on the device from `offsets` (no host round
+// trip).  A unit is (column block nb, row chunk c) where the chunks are the BM-row pieces of
+// the non-empty expert groups, numbered in expert order; units are ordered nb-major, so the
+// chunks that share a weight tile are neighbours.  Every wave of a workgroup builds the same
+// table: lane j covers experts j, j+64, j+128, j+192.
+struct ChunkTable {
+  int a0[4], a1[4], start[4], nc[4];
+  int total;  // number of row chunks (wave-uniform)
 
-  // XCD-aware remap: physical workgroup b runs on XCD b % 8; give each XCD a contiguous
-  // range of logical ids, ordered (column block, chunk) so chunks sharing weights are adjacent.
-  const int G = gridDim.x, b = blockIdx.x;
-  const int L = (b & 7) * (G >> 3) + (b >> 3);
-  const int nb = L / chunks_max;
-  int c = L - nb * chunks_max;
-  if (nb >= n_blocks_N) return;
-  int e = 0, m0 = 0, mend = 0;
-  bool found = false;
-  for (e = 0; e < E_loc; ++e) {
-    // clamp to [0, n_rows] so that inconsistent offsets can never address past the batch
-    const int a0 = min(max(offsets[e], 0), n_rows), a1 = min(max(offsets[e + 1], a0), n_rows);
-    const int nc = (a1 - a0 + BM - 1) / BM;
-    if (c < nc) {
-      m0 = a0 + c * BM;
-      mend = min(a1, m0 + BM);
-      found = true;
-      break;
-    }
-    c -= nc;
+  __device__ __forceinline__ void build(const int32_t* __restrict__ offsets, int E_loc, int n_rows, int BM, int lane) {
+    int base = 0;
+    static_for<4>([&](auto jc) {
+      constexpr int j = jc();
+      const int e = lane + 64 * j;
+      int lo = 0, hi = 0;
+      if (e < E_loc) {
+        // clamp to [0, n_rows] so that inconsistent offsets can never address past the batch
+        lo = min(max(offsets[e], 0), n_rows);
+        hi = min(max(offsets[e + 1], lo), n_rows);
+      }
+      a0[j] = lo;
+      a1[j] = hi;
+      nc[j] = (hi - lo + BM - 1) / BM;
+      int incl = nc[j];  // inclusive scan over the wave
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int v = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += v;
+      }
+      start[j] = base + incl - nc[j];
+      base += __shfl(incl, 63, 64);
+    });
+    total = __builtin_amdgcn_readfirstlane(base);
   }
-  if (!found) return;
-  const int KS = Kd / kBK;
 
-  // weight strips NS*nb .. NS*nb+NS-1 of expert e; block (strip, ks) at (strip*KS + ks) blocks
+  // expert, first row and end row of chunk c (0 <= c < total; e = -1 otherwise)
+  __device__ __forceinline__ void find(int c, int BM, int& e, int& m0, int& mend) const {
+    e = -1;
+    m0 = mend = 0;
+    static_for<4>([&](auto jc) {
+      constexpr int j = jc();
+      const uint64_t hit = __ballot(c >= start[j] && c < start[j] + nc[j]);
+      if (hit && e < 0) {
+        const int l = __builtin_ctzll(hit);
+        e = l + 64 * j;
+        m0 = __shfl(a0[j], l, 64) + (c - __shfl(start[j], l, 64)) * BM;
+        mend = min(__shfl(a1[j], l, 64), m0 + BM);
+      }
+    });
+  }
+};
+
+__device__ __forceinline__ void wg_barrier() {
+  // LDS writes of every wave are complete and visible; global loads stay in flight
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+constexpr int kFfnWaves = 4;
+
+// expert (or -1), column block and rows of unit u of the batch, when u < u_end
+__device__ __forceinline__ int next_unit(const int32_t* __restrict__ offsets, int E_loc, int n_rows, int BM, int lane,
+                                         int u, int u_end, int total, int& nb, int& m0, int& mend) {
+  int e = -1;
+  if (u < u_end) {
+    ChunkTable tab;
+    tab.build(offsets, E_loc, n_rows, BM, lane);
+    nb = u / total;
+    tab.find(u - nb * total, BM, e, m0, mend);
+  }
+  return e;
+}
+
+
+// MODE 0: gate/up GEMM + SwiGLU epilogue -> h [n][I];  MODE 1: down GEMM -> y [n][H].
+// A unit is MT*16 rows of one expert x 4*NS weight strips (16 output columns each).  Each
+// of the 4 waves owns NS strips over the whole contraction and streams them from HBM into a
+// ring of R register sets (R-1 k-steps in flight), so no split-k reduction is needed; the
+// activation k-tile is loaded once per workgroup (a quarter per wave, issued with the
+// weights of the same k-step) and shared through a double-buffered LDS tile.  The grid is
+// at most what the device holds at once and strides over the units, so every unit of a
+// decode-sized batch starts in the first round and no workgroup slot goes to an idle unit.
+template <int MODE, int WDT, int NS, int MT, int R>
+__global__ __launch_bounds__(256) void ffn_mfma_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets,
+                                                    int E_loc, const char* __restrict__ W,
+                                                    const float* __restrict__ s0, const float* __restrict__ s1,
+                                                    uint16_t* __restrict__ out, int Kd, int Nw, int out_ld,
+                                                    int n_blocks_N, int n_rows) {
+  constexpr int BM = MT * 16;
+  static_assert(MODE == 1 || NS % 2 == 0, "gate/up waves own (gate, up) strip pairs");
+  __shared__ u32x4 a_lds[2][APart<MT>::kPieces];
+  constexpr int esz = WDT == MOE_FP8_E4M3 ? 1 : 2;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int KS = Kd / kBK;
+  const int n_strips = Nw / 16;
   const int64_t blk_bytes = 1024 * esz;
   const int64_t strip_stride = (int64_t)KS * blk_bytes;
-  const char* wlane = W + (int64_t)e * Nw * Kd * esz + (int64_t)(nb * NS) * strip_stride + lane * 16;
 
-  // activation rows: lane -> row m0 + 16mt + lane%16 (clamped into the chunk; rows past the
-  // chunk are computed on a copy of its last row and never stored), 32 bytes at
-  // k = 64ks + 16*(lane/16)
-  const uint16_t* arow[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    int r = m0 + mt * 16 + (lane & 15);
-    r = r < mend ? r : mend - 1;
-    arow[mt] = A + (int64_t)r * Kd + (lane >> 4) * 16;
+  // XCD-aware order: physical workgroup b runs on XCD b % 8.  Each XCD gets an equal,
+  // contiguous range of unit ids (so the chunks that share a weight tile run on one XCD's
+  // L2), and its G/8 workgroups stride through that range.  The chunk table is built once
+  // for the first unit and again for each later one, so that it holds no registers across
+  // the contraction.
+  const int G = gridDim.x, b = blockIdx.x, xcd = b & 7;
+  int total, u, u_end, nb = 0, e = -1, m0 = 0, mend = 0;
+  {
+    ChunkTable tab;
+    tab.build(offsets, E_loc, n_rows, BM, lane);
+    total = tab.total;
+    const int U = total * n_blocks_N;
+    u = (int)((int64_t)U * xcd / 8) + (b >> 3);
+    u_end = (int)((int64_t)U * (xcd + 1) / 8);
+    if (u < u_end) {
+      nb = u / total;
+      tab.find(u - nb * total, BM, e, m0, mend);
+    }
   }
+  for (; u < u_end; u += G >> 3, e = next_unit(offsets, E_loc, n_rows, BM, lane, u, u_end, total, nb, m0, mend)) {
+    if (e < 0) break;  // not reachable: the table is the same on every build
+    const int strip0 = (nb * kFfnWaves + wv) * NS;  // this wave's first strip
+    const bool wact = strip0 < n_strips;            // (the last block may be partial)
+    const char* wlane = W + (int64_t)e * Nw * Kd * esz + (int64_t)(wact ? strip0 : 0) * strip_stride + lane * 16;
+    // activation pieces of this thread (rows past the chunk read a copy of its last row;
+    // their results are never stored)
+    const uint16_t* ap[APart<MT>::J];
+#pragma unroll
+    for (int j = 0; j < APart<MT>::J; ++j) {
+      const int t = min(j * 256 + tid, APart<MT>::kPieces - 1), l = t & 63;
+      int r = m0 + (t >> 7) * 16 + (l & 15);
+      r = r < mend ? r : mend - 1;
+      ap[j] = A + (int64_t)r * Kd + (l >> 4) * 16 + ((t >> 6) & 1) * 8;
+    }
 
-  f32x4 acc[MT][NS];
+    f32x4 acc[MT][NS];
 #pragma unroll
-  for (int i = 0; i < MT; ++i)
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int j = 0; j < NS; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < NS; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const WTile<WDT, NS>& wt, const ATile<MT>& at) {
+    auto compute = [&](const WTile<WDT, NS>& wt, const u32x4* tile) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      bf16x8 bf[NS];
+      for (int h = 0; h < 2; ++h) {
+        bf16x8 bf[NS];
 #pragma unroll
-      for (int s = 0; s < NS; ++s) bf[s] = wt.frag(s, h);
+        for (int s = 0; s < NS; ++s) bf[s] = wt.frag(s, h);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        bf16x8 af;
-        __builtin_memcpy(&af, &at.raw[mt][h], 16);
+        for (int mt = 0; mt < MT; ++mt) {
+          const u32x4 araw = tile[(mt * 2 + h) * 64 + lane];
+          bf16x8 af;
+          __builtin_memcpy(&af, &araw, 16);
 #pragma unroll
-        for (int s = 0; s < NS; ++s) acc[mt][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[s], acc[mt][s], 0, 0, 0);
+          for (int s = 0; s < NS; ++s)
+            acc[mt][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[s], acc[mt][s], 0, 0, 0);
+        }
       }
-    }
-  };
+    };
 
-  // this wave's k-steps are wv, wv+4, ...; a ring of kStages register sets keeps the loads
-  // of the next kStages-1 steps in flight while the current step feeds the MFMAs.  Loads
-  // past the end are clamped to the last step (valid memory, result unused), so no load is
-  // conditional; the scheduling barriers keep each prefetch batch ahead of the MFMAs.
-  const int nsteps = KS > wv ? (KS - wv + kFfnWaves - 1) / kFfnWaves : 0;
-  auto kstep = [&](int i) { return min(wv + kFfnWaves * i, KS - 1); };
-  if (nsteps > 0) {
-    WTile<WDT, NS> wr[kStages];
-    ATile<MT> ar[kStages];
-#pragma unroll
-    for (int u = 0; u < kStages - 1; ++u) {
-      wr[u].load(wlane + kstep(u) * blk_bytes, strip_stride);
-      ar[u].load(arow, kstep(u) * kBK);
-    }
+    // k-step i: issue the loads of step i+R-1 (clamped to the last step: valid memory,
+    // result unused), park this thread's activation piece of step i in LDS, barrier, MFMAs.
+    // Ring slots are compile-time indices so that every slot lives in registers.
+    WTile<WDT, NS> wr[R];
+    APart<MT> ar[R];
+    auto issue = [&](auto slot, int ks) {
+      ks = min(ks, KS - 1);
+      if (wact) wr[slot()].load(wlane + ks * blk_bytes, strip_stride);
+      ar[slot()].load(ap, ks * kBK);
+    };
+    auto step = [&](auto slot, int i) {
+      ar[slot()].store(a_lds[i & 1], tid);
+      wg_barrier();
+      if (wact) compute(wr[slot()], a_lds[i & 1]);
+    };
+    static_for<R - 1>([&](auto v) { issue(v, v()); });
     int it = 0;
 #pragma clang loop unroll(disable)
-    for (; it + kStages <= nsteps; it += kStages) {
-#pragma unroll
-      for (int u = 0; u < kStages; ++u) {
-        const int ld = (u + kStages - 1) % kStages;
-        wr[ld].load(wlane + kstep(it + u + kStages - 1) * blk_bytes, strip_stride);
-        ar[ld].load(arow, kstep(it + u + kStages - 1) * kBK);
+    for (; it + R <= KS; it += R) {
+      static_for<R>([&](auto v) {
+        issue(std::integral_constant<int, (v() + R - 1) % R>{}, it + v() + R - 1);
         __builtin_amdgcn_sched_barrier(0);
-        compute(wr[u], ar[u]);
+        step(v, it + v());
         __builtin_amdgcn_sched_barrier(0);
-      }
+      });
     }
-    const int rest = nsteps - it;  // < kStages; those steps sit in ring slots 0..rest-1
-#pragma unroll
-    for (int u = 0; u < kStages - 1; ++u)
-      if (u < rest) compute(wr[u], ar[u]);
-  }
+    // the remaining KS - it < R steps sit in slots 0, 1, ...
+    static_for<R - 1>([&](auto v) {
+      if (it + v() < KS) step(v, it + v());
+    });
+    wg_barrier();  // the next unit's first LDS writes wait for this unit's last reads
+    if (!wact) continue;
 
-  // split-k reduction: waves 1..3 park their partial tiles in LDS, wave 0 sums
-  if (wv > 0) {
+    // epilogue; the accumulator of lane l holds column l%16 of a strip and rows 4(l/16)+q
+    const int col16 = lane & 15, rq = (lane >> 4) * 4;
+    if (MODE == 0) {
+      const int I = out_ld;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+      for (int p = 0; p < NS / 2; ++p) {
+        const int i = (strip0 / 2 + p) * 16 + col16;
+        float sg = 1.f, su = 1.f;
+        if (WDT == MOE_FP8_E4M3) {
+          sg = s0[(int64_t)e * I + i];
+          su = s1[(int64_t)e * I + i];
+        }
 #pragma unroll
-      for (int s = 0; s < NS; ++s) red[wv - 1][mt][s][lane] = acc[mt][s];
-  }
-  __syncthreads();
-  if (wv != 0) return;
+        for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-      for (int w = 0; w < kFfnWaves - 1; ++w) acc[mt][s] += red[w][mt][s][lane];
-
-  // epilogue; the accumulator of lane l holds column l%16 of a strip and rows 4(l/16)+q
-  const int col16 = lane & 15, rq = (lane >> 4) * 4;
-  if (MODE == 0) {
-    const int I = out_ld;
-#pragma unroll
-    for (int p = 0; p < NS / 2; ++p) {
-      const int i = (nb * (NS / 2) + p) * 16 + col16;
-      float sg = 1.f, su = 1.f;
-      if (WDT == MOE_FP8_E4M3) {
-        sg = s0[(int64_t)e * I + i];
-        su = s1[(int64_t)e * I + i];
-      }
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int row = m0 + mt * 16 + rq + q;
-          if (row < mend) {
-            const float g = acc[mt][2 * p][q] * sg, u = acc[mt][2 * p + 1][q] * su;
-            out[(int64_t)row * I + i] = f32_to_bf16(silu_mul(g, u));
+          for (int q = 0; q < 4; ++q) {
+            const int row = m0 + mt * 16 + rq + q;
+            if (row < mend) {
+              const float g = acc[mt][2 * p][q] * sg, uu = acc[mt][2 * p + 1][q] * su;
+              out[(int64_t)row * I + i] = f32_to_bf16(silu_mul(g, uu));
+            }
           }
         }
       }
-    }
-  } else {
-    const int H = out_ld;
+    } else {
+      const int H = out_ld;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const int col = (nb * NS + s) * 16 + col16;
-      const float sc = WDT == MOE_FP8_E4M3 ? s0[(int64_t)e * H + col] : 1.f;
+      for (int s = 0; s < NS; ++s) {
+        const int col = (strip0 + s) * 16 + col16;
+        const float sc = WDT == MOE_FP8_E4M3 ? s0[(int64_t)e * H + col] : 1.f;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
+        for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int row = m0 + mt * 16 + rq + q;
-          if (row < mend) out[(int64_t)row * H + col] = f32_to_bf16(acc[mt][s][q] * sc);
+          for (int q = 0; q < 4; ++q) {
+            const int row = m0 + mt * 16 + rq + q;
+            if (row < mend) out[(int64_t)row * H + col] = f32_to_bf16(acc[mt][s][q] * sc);
+          }
         }
       }
     }
   }
 }
 
-template <int MODE, int WDT, int NS, int MT>
+// Workgroups of one kernel that the device holds at once (its CU count times the kernel's
+// occupancy), cached per device and kernel instance.
+template <typename K>
+static int resident_workgroups(K kernel, int threads) {
+  constexpr int kMaxDev = 64;
+  static int cache[kMaxDev];  // 0 = not yet known; racing writers store the same value
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) dev = -1;
+  if (dev >= 0 && cache[dev] > 0) return cache[dev];
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) != hipSuccess) cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) per_cu = 0;
+  const int r = cus > 0 && per_cu > 0 ? cus * per_cu : 1024;
+  if (dev >= 0) cache[dev] = r;
+  return r;
+}
+
+template <int MODE, int WDT, int NS, int MT, int R>
 static void launch_mfma_t(const void* A, const int32_t* offsets, int E_loc, const void* W, const float* s0,
                           const float* s1, void* out, int Kd, int Nw, int out_ld, int n, hipStream_t stream) {
   constexpr int BM = MT * 16;
-  const int n_blocks_N = Nw / (16 * NS);
-  const int chunks_max = (n + (BM - 1) * E_loc) / BM;
-  int64_t grid = (int64_t)chunks_max * n_blocks_N;
-  grid = (grid + 7) / 8 * 8;
-  hipLaunchKernelGGL((ffn_mfma_kernel<MODE, WDT, NS, MT>), dim3((unsigned)grid), dim3(256), 0, stream,
-                     (const uint16_t*)A, offsets, E_loc, (const char*)W, s0, s1, (uint16_t*)out, Kd, Nw, out_ld,
-                     n_blocks_N, chunks_max, n);
+  auto kernel = ffn_mfma_kernel<MODE, WDT, NS, MT, R>;
+  const int n_blocks_N = (Nw / 16 + kFfnWaves * NS - 1) / (kFfnWaves * NS);
+  const int64_t chunks_max = (n + (int64_t)(BM - 1) * E_loc) / BM;  // ragged worst case
+  int64_t grid = std::min<int64_t>(chunks_max * n_blocks_N, resident_workgroups(kernel, 256));
+  grid = (grid + 7) / 8 * 8;  // the XCD-aware order needs a multiple of 8
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), 0, stream, (const uint16_t*)A, offsets, E_loc,
+                     (const char*)W, s0, s1, (uint16_t*)out, Kd, Nw, out_ld, n_blocks_N, n);
 }
 
 // Row-chunk height: tall enough that an average expert group fits one chunk with room for
@@ -352,28 +452,33 @@ static void launch_mfma_t(const void* A, const int32_t* offsets, int E_loc, cons
 #define MOE_FFN_MT 0  // 0: choose from the batch shape
 #endif
 #ifndef MOE_FFN_NS_GU
-#define MOE_FFN_NS_GU 4
+#define MOE_FFN_NS_GU 2
 #endif
 #ifndef MOE_FFN_NS_D
-#define MOE_FFN_NS_D 4
+#define MOE_FFN_NS_D 2
+#endif
+#ifndef MOE_FFN_R_GU
+#define MOE_FFN_R_GU 3
+#endif
+#ifndef MOE_FFN_R_D
+#define MOE_FFN_R_D 4
 #endif
 
 static int pick_mt(int n, int E_loc) {
   if (MOE_FFN_MT > 0) return MOE_FFN_MT;
   const int want = (3 * n + 2 * E_loc - 1) / (2 * E_loc);
   const int mt = (want + 15) / 16;
-  return mt < 2 ? 2 : (mt > 3 ? 3 : mt);  // taller chunks measured slower at decode sizes
+  return mt < 2 ? 2 : (mt > 3 ? 3 : mt);
 }
 
 template <int MODE, int WDT>
 static void launch_mfma(const void* A, const int32_t* offsets, int E_loc, const void* W, const float* s0,
                         const float* s1, void* out, int Kd, int Nw, int out_ld, int n, hipStream_t stream) {
-  // gate/up: 4 strips (32 gate + 32 up columns) per workgroup; down: 4 strips
   constexpr int NS = MODE == 0 ? MOE_FFN_NS_GU : MOE_FFN_NS_D;
+  constexpr int R = MODE == 0 ? MOE_FFN_R_GU : MOE_FFN_R_D;
   switch (pick_mt(n, E_loc)) {
-    case 2: launch_mfma_t<MODE, WDT, NS, 2>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, stream); break;
-    case 3: launch_mfma_t<MODE, WDT, NS, 3>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, stream); break;
-    default: launch_mfma_t<MODE, WDT, NS, 4>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, stream); break;
+    case 2: launch_mfma_t<MODE, WDT, NS, 2, R>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, stream); break;
+    default: launch_mfma_t<MODE, WDT, NS, 3, R>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, stream); break;
   }
 }
 
