@@ -20,6 +20,7 @@ import ctypes as C
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -30,7 +31,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_ffn_gateup_decode.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn_gateup_decode_traffic.md")
+CALIB_BYTES = 256 << 20
 FFN_SRC = os.path.join(ROOT, "asynchronous_moe_expert_amd", "csrc", "ffn.hip")
 
 
@@ -60,17 +62,16 @@ class HipEvents:
         return float(out.value)
 
 
-def stored_traffic(per_launch_bytes: float):
-    """HBM traffic of the gate/up kernel from the committed rocprofv3 counter summary, if it
-    was taken on the kernel source as it is now (else null)."""
+def stored_traffic():
+    """HBM bytes per launch of the gate/up kernel from the committed rocprofv3 counter
+    summary, if its counters were taken on the kernel source as it is now (else None)."""
     try:
-        with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
+        text = open(TRAFFIC_FILE).read()
+        sha = re.search(r"ffn\.hip sha256: ([0-9a-f]{64})", text).group(1)
+        val = re.search(r"traffic bytes per launch: ([0-9]+)", text).group(1)
         src = hashlib.sha256(open(FFN_SRC, "rb").read()).hexdigest()
-        if t.get("ffn_hip_sha256") != src:
-            return None
-        return float(t["fetch_bytes_per_launch"]) + float(t["write_bytes_per_launch"])
-    except (OSError, KeyError, ValueError):
+        return float(val) if sha == src else None
+    except (OSError, AttributeError, ValueError):
         return None
 
 
@@ -108,6 +109,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle CPU-baseline budget (0 = skip)")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="copy 256 MiB device to device once before the warm-up (reference dispatch for "
+                         "rocprofv3 byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs one expert-parallel rank's share on a single GPU; multi-GPU runs are not part "
@@ -160,6 +164,13 @@ def main() -> int:
         st.combine(st.y, st.pos, tok_steps[s], d["kslot"], d["w"], d["gen"], m=b.n, n_rows=b.n)
         ev.record(e_end[s], stream)
 
+    if args.calibration_copy:
+        src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for s in range(W_steps):
         step(s)
     torch.cuda.synchronize()
@@ -212,7 +223,7 @@ def main() -> int:
                    "E_loc": b.E_loc, "K": b.K, "H": H, "I": I, "pairs": n, "tokens": b.T, "pool_slots": b.P},
         "roofline": {"bound": "hbm", "kernel": "ffn_mfma_kernel<gate/up, bf16>", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": stored_traffic(gu_bytes), "algorithmic_bytes": gu_bytes,
+                     "traffic": stored_traffic(), "algorithmic_bytes": gu_bytes,
                      "mfma_frac": round(gu_flops / (gu_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 5)},
         "stages_us": {"assemble": round(asm_ms * 1e3, 2), "ffn_gate_up": round(gu_ms * 1e3, 2),
                       "ffn_down": round(dn_ms * 1e3, 2), "combine": round(cb_ms * 1e3, 2),
