@@ -66,6 +66,10 @@ __device__ __forceinline__ int expert_of_row(const int32_t* __restrict__ offsets
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+// the same with a hardware reciprocal (about 1 ulp), for results rounded to bf16
+__device__ __forceinline__ float silu_mul_fast(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
 
 // ------------------------------------------------------------------------- fp32 path
 // Small-shape path (fp32 activations and weights): one thread per output element.
@@ -103,21 +107,15 @@ __global__ __launch_bounds__(256) void down_f32_kernel(const float* __restrict__
 }
 
 // -------------------------------------------------------------- bf16 / fp8 MFMA path
-// Widen 8 e4m3 codes (two dwords) to 8 bf16 values (exact).
+// Widen 8 e4m3 codes (two dwords) to 8 bf16 values (exact: every e4m3 value is a bf16
+// value); one v_cvt_scalef32_pk_bf16_fp8 per pair of codes, scale 1.
 __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
-  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
-  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
-  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
-  const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
-  uint32_t p[4];
-  // values are exact in bf16, so truncating the low half of the fp32 pattern is exact
-  p[0] = (__float_as_uint(a.x) >> 16) | (__float_as_uint(a.y) & 0xffff0000u);
-  p[1] = (__float_as_uint(b.x) >> 16) | (__float_as_uint(b.y) & 0xffff0000u);
-  p[2] = (__float_as_uint(c.x) >> 16) | (__float_as_uint(c.y) & 0xffff0000u);
-  p[3] = (__float_as_uint(d.x) >> 16) | (__float_as_uint(d.y) & 0xffff0000u);
-  bf16x8 r;
-  __builtin_memcpy(&r, p, 16);
-  return r;
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 template <int WDT, int NS>
@@ -242,15 +240,24 @@ __device__ __forceinline__ void wg_barrier() {
 
 constexpr int kFfnWaves = 4;
 
-// expert (or -1), column block and rows of unit u of the batch, when u < u_end
+// expert (or -1), column block and rows of unit u of the batch, when u < u_end.  Units are
+// numbered column-block-major (u = nb * total + chunk) or, with n_blocks > 0, chunk-major
+// (u = chunk * n_blocks + nb).
 __device__ __forceinline__ int next_unit(const int32_t* __restrict__ offsets, int E_loc, int n_rows, int BM, int lane,
-                                         int u, int u_end, int total, int& nb, int& m0, int& mend) {
+                                         int u, int u_end, int total, int& nb, int& m0, int& mend, int n_blocks = 0) {
   int e = -1;
   if (u < u_end) {
     ChunkTable tab;
     tab.build(offsets, E_loc, n_rows, BM, lane);
-    nb = u / total;
-    tab.find(u - nb * total, BM, e, m0, mend);
+    int c;
+    if (n_blocks > 0) {
+      c = u / n_blocks;
+      nb = u - c * n_blocks;
+    } else {
+      nb = u / total;
+      c = u - nb * total;
+    }
+    tab.find(c, BM, e, m0, mend);
   }
   return e;
 }
@@ -392,7 +399,7 @@ __global__ __launch_bounds__(256) void ffn_mfma_kernel(const uint16_t* __restric
             const int row = m0 + mt * 16 + rq + q;
             if (row < mend) {
               const float g = acc[mt][2 * p][q] * sg, uu = acc[mt][2 * p + 1][q] * su;
-              out[(int64_t)row * I + i] = f32_to_bf16(silu_mul(g, uu));
+              out[(int64_t)row * I + i] = f32_to_bf16(silu_mul_fast(g, uu));
             }
           }
         }
@@ -417,9 +424,9 @@ __global__ __launch_bounds__(256) void ffn_mfma_kernel(const uint16_t* __restric
 }
 
 // Workgroups of one kernel that the device holds at once (its CU count times the kernel's
-// occupancy), cached per device and kernel instance.
-template <typename K>
-static int resident_workgroups(K kernel, int threads) {
+// occupancy), cached per device for each kernel (the template argument is the kernel).
+template <auto Kernel>
+static int resident_workgroups(int threads) {
   constexpr int kMaxDev = 64;
   static int cache[kMaxDev];  // 0 = not yet known; racing writers store the same value
   int dev = 0;
@@ -427,7 +434,7 @@ static int resident_workgroups(K kernel, int threads) {
   if (dev >= 0 && cache[dev] > 0) return cache[dev];
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) != hipSuccess) cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, Kernel, threads, 0) != hipSuccess) per_cu = 0;
   const int r = cus > 0 && per_cu > 0 ? cus * per_cu : 1024;
   if (dev >= 0) cache[dev] = r;
   return r;
@@ -437,11 +444,288 @@ template <int MODE, int WDT, int NS, int MT, int R>
 static void launch_mfma_t(const void* A, const int32_t* offsets, int E_loc, const void* W, const float* s0,
                           const float* s1, void* out, int Kd, int Nw, int out_ld, int n, hipStream_t stream) {
   constexpr int BM = MT * 16;
-  auto kernel = ffn_mfma_kernel<MODE, WDT, NS, MT, R>;
+  constexpr auto kernel = ffn_mfma_kernel<MODE, WDT, NS, MT, R>;
   const int n_blocks_N = (Nw / 16 + kFfnWaves * NS - 1) / (kFfnWaves * NS);
   const int64_t chunks_max = (n + (int64_t)(BM - 1) * E_loc) / BM;  // ragged worst case
-  int64_t grid = std::min<int64_t>(chunks_max * n_blocks_N, resident_workgroups(kernel, 256));
+  int64_t grid = std::min<int64_t>(chunks_max * n_blocks_N, resident_workgroups<kernel>(256));
   grid = (grid + 7) / 8 * 8;  // the XCD-aware order needs a multiple of 8
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), 0, stream, (const uint16_t*)A, offsets, E_loc,
+                     (const char*)W, s0, s1, (uint16_t*)out, Kd, Nw, out_ld, n_blocks_N, n);
+}
+
+// ------------------------------------------------------------ prefill GEMM path
+// For batches with many rows per expert the FFN is bound by the matrix cores, so the
+// kernel is built around v_mfma_f32_32x32x16_bf16 (the shape that reaches the bf16 peak
+// on gfx950) with every operand byte feeding as many MFMAs as registers allow:
+//   * unit = (128-row chunk of one expert, 256 weight columns); each of the 4 waves owns
+//     64 columns for all 128 rows (4 x 2 tiles of 32 x 32, 128 fp32 accumulators);
+//   * the activation k-tile (128 rows x 64 k, bf16) is shared by the 4 waves through a
+//     double-buffered LDS tile: each thread loads its quarter four k-steps ahead into a
+//     register ring and parks it in LDS one step ahead; the 16-byte slots of a tile row
+//     are XOR-swizzled so that the loads stay coalesced (8 rows x 128 B per instruction)
+//     and the operand reads are free of bank conflicts;
+//   * each wave loads its weight fragments four k-steps ahead straight from the packed
+//     layout into a register ring (buffer loads: a per-lane offset fixed for the unit, the
+//     k-step in a scalar register) and widens fp8 to bf16 in registers;
+//   * one wave per SIMD with a software pipeline: the activation fragments of the next
+//     k-step are read from LDS in two halves, each into the registers the current step has
+//     just consumed, between MFMA halves, so LDS latency and the per-step barrier overlap
+//     the math;
+//   * gate/up: a wave's 64 packed rows are 2 gate and 2 up strips; its column tile 0 takes
+//     the gate strips and tile 1 the matching up strips, so the SwiGLU epilogue pairs values
+//     within a lane (no cross-lane exchange);
+//   * k-permutation: in MFMA s (0..3) of a 64-wide k-step, lane half hf uses
+//     k = 32hf + 8s + q for both operands, so a lane's weight fragment for 32 columns is
+//     two 16-byte runs of the packed fp8 block (four of the bf16 block) and the sums are
+//     exact dot products over all k.
+constexpr int kGemmBM = 128;
+constexpr int kGemmWaveN = 64;
+constexpr int kGemmBN = kGemmWaveN * kFfnWaves;
+constexpr int kGemmStages = 4;  // weight register ring
+#ifndef MOE_FFN_GEMM_CHUNK_MAJOR
+#define MOE_FFN_GEMM_CHUNK_MAJOR 1
+#endif
+constexpr bool kGemmChunkMajor = MOE_FFN_GEMM_CHUNK_MAJOR != 0;
+
+// weight fragments of one k-step for a wave's 2 column tiles (as loaded)
+template <int WDT>
+struct GemmW;
+template <>
+struct GemmW<MOE_FP8_E4M3> {
+  static constexpr int kLoads = 4;
+  u32x4 raw[2][2];  // [tile][piece]: piece p holds k = 32hf + 16p + 0..15 of the lane's column
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t w, const int* voff, int soff) {
+    static_for<2>([&](auto t) {
+      raw[t()][0] = __builtin_amdgcn_raw_buffer_load_b128(w, voff[t()], soff, 0);
+      raw[t()][1] = __builtin_amdgcn_raw_buffer_load_b128(w, voff[t()] + 256, soff, 0);
+    });
+  }
+  __device__ __forceinline__ bf16x8 frag(int t, int s) const {
+    const u32x4& p = raw[t][s >> 1];
+    return (s & 1) ? e4m3x8_to_bf16(p[2], p[3]) : e4m3x8_to_bf16(p[0], p[1]);
+  }
+};
+template <>
+struct GemmW<MOE_BF16> {
+  static constexpr int kLoads = 8;
+  u32x4 raw[2][4];  // [tile][s]
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t w, const int* voff, int soff) {
+    static_for<2>([&](auto t) {
+      static_for<4>([&](auto s) {
+        // g = 2hf + s/2 and h = s%2 of the packed bf16 block; the lane's hf part is in voff
+        raw[t()][s()] = __builtin_amdgcn_raw_buffer_load_b128(w, voff[t()] + (s() & 1) * 1024 + (s() >> 1) * 256, soff, 0);
+      });
+    });
+  }
+  __device__ __forceinline__ bf16x8 frag(int t, int s) const {
+    bf16x8 r;
+    __builtin_memcpy(&r, &raw[t][s], 16);
+    return r;
+  }
+};
+
+// buffer resource over `bytes` bytes at p (gfx9 resource word 3); loads past the end read 0
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, int64_t bytes) {
+  const int n = (int)std::min<int64_t>(bytes, 0x7fffffff);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, n, 0x00020000);
+}
+
+template <int MODE, int WDT>
+__global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets,
+                                                       int E_loc, const char* __restrict__ W,
+                                                       const float* __restrict__ s0, const float* __restrict__ s1,
+                                                       uint16_t* __restrict__ out, int Kd, int Nw, int out_ld,
+                                                       int n_blocks_N, int n_rows) {
+  constexpr int S = kGemmStages;
+  constexpr int esz = WDT == MOE_FP8_E4M3 ? 1 : 2;
+  __shared__ u32x4 a_lds[2][kGemmBM * 8];  // activation k-tile, 2 stages of 16 KiB
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int KS = Kd / kBK;
+  const int64_t strip_stride = (int64_t)KS * 1024 * esz;
+  const int l32 = lane & 31, hf = lane >> 5;
+
+  const int G = gridDim.x, b = blockIdx.x, xcd = b & 7;
+  int total, u, u_end, nb = 0, e = -1, m0 = 0, mend = 0;
+  {
+    ChunkTable tab;
+    tab.build(offsets, E_loc, n_rows, kGemmBM, lane);
+    total = tab.total;
+    const int U = total * n_blocks_N;
+    u = (int)((int64_t)U * xcd / 8) + (b >> 3);
+    u_end = (int)((int64_t)U * (xcd + 1) / 8);
+    if (u < u_end) {
+      int c;
+      if (kGemmChunkMajor) {
+        c = u / n_blocks_N;
+        nb = u - c * n_blocks_N;
+      } else {
+        nb = u / total;
+        c = u - nb * total;
+      }
+      tab.find(c, kGemmBM, e, m0, mend);
+    }
+  }
+  for (; u < u_end; u += G >> 3, e = next_unit(offsets, E_loc, n_rows, kGemmBM, lane, u, u_end, total, nb, m0, mend,
+                                                kGemmChunkMajor ? n_blocks_N : 0)) {
+    if (e < 0) break;  // not reachable: the table is the same on every build
+    const int col0 = nb * kGemmBN + wv * kGemmWaveN;
+    const bool wact = col0 < Nw;        // the last column block may be partial
+    const int colw = wact ? col0 : 0;   // idle waves stream valid weights (results unused)
+    // weight lane offsets (bytes into expert e's packed matrix).  The wave's 4 strips are
+    // colw/16 + 0..3.  Gate/up: tile 0 takes the gate strips (+0, +2) and tile 1 the matching
+    // up strips (+1, +3), so a lane holds the gate and up value of one h column in its two
+    // tiles.  Down: tile t takes strips +2t, +2t+1 (32 consecutive output columns).
+    const __amdgpu_buffer_rsrc_t wrs = buffer_rsrc(W + (int64_t)e * Nw * Kd * esz, (int64_t)Nw * Kd * esz);
+    int wvo[2];
+    static_for<2>([&](auto t) {
+      const int half = l32 >> 4, r = l32 & 15;
+      const int strip = colw / 16 + (MODE == 0 ? 2 * half + t() : 2 * t() + half);
+      wvo[t()] = (int)(strip * strip_stride) + (32 * hf + r) * 16;
+    });
+    // activation DMA: instruction d of this wave fills the 16-byte slots (4wv + d)*64 + lane
+    // of a stage; slot P holds row P/8, 16-byte piece (P%8) ^ ((P/8 >> 1) & 7) of the row
+    const uint16_t* adma[4];
+    static_for<4>([&](auto d) {
+      const int P = (wv * 4 + d()) * 64 + lane, row = P >> 3, kq = (P & 7) ^ ((row >> 1) & 7);
+      const int r = min(m0 + row, mend - 1);
+      adma[d()] = A + (int64_t)r * Kd + kq * 8;
+    });
+
+    f32x16 acc[4][2];
+    static_for<4>([&](auto i) { static_for<2>([&](auto j) { acc[i()][j()] = f32x16{}; }); });
+
+    GemmW<WDT> wr[S];   // weight fragments of steps i .. i+S-1
+    u32x4 ar[4][4];     // this thread's activation pieces of steps i+1 .. i+4
+    u32x4 af[4][4];     // activation fragments [k-slice s][mt] of the step being computed
+    auto issue_a = [&](auto aslot, int ks) {
+      ks = min(ks, KS - 1);
+      static_for<4>([&](auto d) { ar[aslot()][d()] = *reinterpret_cast<const u32x4*>(adma[d()] + ks * kBK); });
+    };
+    auto issue_w = [&](auto slot, int ks) { wr[slot()].load(wrs, wvo, min(ks, KS - 1) * 1024 * esz); };
+    // park this thread's pieces of a step in LDS; the compiler waits for their loads only
+    // (loads retire in order and the weights of the same step were issued after them)
+    auto park = [&](auto aslot, auto stg) {
+      static_for<4>([&](auto d) { a_lds[stg()][(wv * 4 + d()) * 64 + lane] = ar[aslot()][d()]; });
+    };
+    auto barrier = [&]() {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    };
+    auto read = [&](auto stg, auto s_lo) {  // fragments of k-slices s_lo, s_lo + 1
+      const u32x4* tile = a_lds[stg()];
+      static_for<2>([&](auto ds) {
+        static_for<4>([&](auto mt) {
+          constexpr int ss = s_lo() + ds();
+          const int row = mt() * 32 + l32, kq = 4 * hf + ss;
+          af[ss][mt()] = tile[row * 8 + (kq ^ ((row >> 1) & 7))];
+        });
+      });
+    };
+    auto mfmas = [&](auto slot, auto s_lo) {  // MFMAs of k-slices s_lo, s_lo + 1
+      static_for<2>([&](auto ds) {
+        constexpr int ss = s_lo() + ds();
+        bf16x8 bw[2];
+        static_for<2>([&](auto t) { bw[t()] = wr[slot()].frag(t(), ss); });
+        static_for<4>([&](auto mt) {
+          bf16x8 a;
+          __builtin_memcpy(&a, &af[ss][mt()], 16);
+          static_for<2>([&](auto t) {
+            acc[mt()][t()] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bw[t()], acc[mt()][t()], 0, 0, 0);
+          });
+        });
+      });
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    // Software pipeline over k-steps i (weight and activation slot i % 4, LDS stage i % 2).
+    // Step i: MFMAs of slices 0-1 of step i; park the activation pieces of step i+1 in LDS
+    // and barrier; read slices 0-1 of step i+1 into the registers just freed; MFMAs of
+    // slices 2-3 of step i; read slices 2-3 of step i+1 (their LDS latency hides behind the
+    // first MFMAs of step i+1); issue the loads of step i+4 (activations, then weights) into
+    // the slots step i has freed.  Loads are issued in the order they are needed, so the
+    // in-order completion of loads never makes a wait drain a later step.  A unit runs a
+    // whole number of 4-step groups: steps past the contraction read clamped (valid) data and
+    // zero their activation fragments, so every step has the same branch-free body.
+    static_assert(S == 4, "weight and activation rings of 4, LDS stages of 2");
+    auto issue = [&](auto slot, int ks) {
+      issue_a(slot, ks);
+      issue_w(slot, ks);
+    };
+    static_for<4>([&](auto v) {  // same batch order as the loop, so every wait matches the steady state
+      __builtin_amdgcn_sched_barrier(0);
+      issue(v, v());
+    });
+    __builtin_amdgcn_sched_barrier(0);
+    park(I0{}, I0{});
+    barrier();
+    read(I0{}, I0{});
+    read(I0{}, I2{});
+    const int n_steps = (KS + 3) / 4 * 4;
+#pragma clang loop unroll(disable)
+    for (int it = 0; it < n_steps; it += 4) {
+      static_for<4>([&](auto v) {
+        constexpr int slot = v();
+        using SL = std::integral_constant<int, slot>;
+        using NX = std::integral_constant<int, (slot + 1) % 4>;
+        using P1 = std::integral_constant<int, (slot + 1) & 1>;
+        const int i = it + v();
+        if (i >= KS) static_for<4>([&](auto ss) { static_for<4>([&](auto mt) { af[ss()][mt()] = u32x4{}; }); });
+        mfmas(SL{}, I0{});
+        park(NX{}, P1{});
+        barrier();
+        read(P1{}, I0{});
+        mfmas(SL{}, I2{});
+        read(P1{}, I2{});
+        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch batch where it is issued
+        issue(SL{}, i + 4);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    }
+    barrier();  // the next unit's first LDS writes wait for this unit's last reads
+    if (!wact) continue;
+
+    // epilogue; accumulator v of lane l holds column l%32 and row 8(v/4) + 4(l/32) + v%4 of a
+    // tile.  The fp8 row scales of a lane's columns are read once, before the stores.
+    if (MODE == 0) {
+      const int col = col0 / 2 + l32;  // h column: gate in tile 0, up in tile 1
+      float sg = 1.f, su = 1.f;
+      if (WDT == MOE_FP8_E4M3) {
+        sg = s0[(int64_t)e * out_ld + col];
+        su = s1[(int64_t)e * out_ld + col];
+      }
+      static_for<4>([&](auto mt) {
+        static_for<16>([&](auto v) {
+          const int row = m0 + mt() * 32 + 8 * (v() >> 2) + 4 * hf + (v() & 3);
+          if (row < mend)
+            out[(int64_t)row * out_ld + col] = f32_to_bf16(silu_mul_fast(acc[mt()][0][v()] * sg, acc[mt()][1][v()] * su));
+        });
+      });
+    } else {
+      static_for<2>([&](auto t) {
+        const int col = col0 + t() * 32 + l32;
+        const float sc = WDT == MOE_FP8_E4M3 ? s0[(int64_t)e * out_ld + col] : 1.f;
+        static_for<4>([&](auto mt) {
+          static_for<16>([&](auto v) {
+            const int row = m0 + mt() * 32 + 8 * (v() >> 2) + 4 * hf + (v() & 3);
+            if (row < mend) out[(int64_t)row * out_ld + col] = f32_to_bf16(acc[mt()][t()][v()] * sc);
+          });
+        });
+      });
+    }
+  }
+}
+
+template <int MODE, int WDT>
+static void launch_gemm(const void* A, const int32_t* offsets, int E_loc, const void* W, const float* s0,
+                        const float* s1, void* out, int Kd, int Nw, int out_ld, int n, hipStream_t stream) {
+  constexpr auto kernel = ffn_gemm_kernel<MODE, WDT>;
+  const int n_blocks_N = (Nw + kGemmBN - 1) / kGemmBN;
+  const int64_t chunks_max = (n + (int64_t)(kGemmBM - 1) * E_loc) / kGemmBM;
+  int64_t grid = std::min<int64_t>(chunks_max * n_blocks_N, resident_workgroups<kernel>(256));
+  grid = (grid + 7) / 8 * 8;
   hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), 0, stream, (const uint16_t*)A, offsets, E_loc,
                      (const char*)W, s0, s1, (uint16_t*)out, Kd, Nw, out_ld, n_blocks_N, n);
 }
@@ -471,11 +755,20 @@ static int pick_mt(int n, int E_loc) {
   return mt < 2 ? 2 : (mt > 3 ? 3 : mt);
 }
 
+// Prefill-sized batches (many rows per expert) go to the MFMA-bound GEMM kernel.
+#ifndef MOE_FFN_GEMM_ROWS
+#define MOE_FFN_GEMM_ROWS 96  // mean rows per expert from which the GEMM kernel is used
+#endif
+
 template <int MODE, int WDT>
 static void launch_mfma(const void* A, const int32_t* offsets, int E_loc, const void* W, const float* s0,
                         const float* s1, void* out, int Kd, int Nw, int out_ld, int n, hipStream_t stream) {
   constexpr int NS = MODE == 0 ? MOE_FFN_NS_GU : MOE_FFN_NS_D;
   constexpr int R = MODE == 0 ? MOE_FFN_R_GU : MOE_FFN_R_D;
+  if (MOE_FFN_MT == 0 && n >= MOE_FFN_GEMM_ROWS * E_loc) {
+    launch_gemm<MODE, WDT>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, stream);
+    return;
+  }
   switch (pick_mt(n, E_loc)) {
     case 2: launch_mfma_t<MODE, WDT, NS, 2, R>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, stream); break;
     default: launch_mfma_t<MODE, WDT, NS, 3, R>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, stream); break;

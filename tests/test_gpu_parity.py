@@ -85,6 +85,12 @@ FFN_CASES = [
     ("bf16", 5, 256, 128, [0, 0, 200, 1, 16]),
     ("fp8", 3, 256, 128, [65, 3, 0]),
     ("fp8", 2, 4096, 2048, [129, 40]),
+    # >= 96 rows per expert on average: the 128-row tiled kernel, with partial row chunks,
+    # an empty expert, partial 256-column blocks and contractions of 3, 10 and 45 k-steps
+    ("bf16", 4, 512, 256, [300, 0, 5, 130]),
+    ("fp8", 3, 640, 192, [257, 1, 130]),
+    ("bf16", 2, 2880, 2880, [200, 190]),
+    ("fp8", 2, 4096, 2048, [300, 60]),
 ]
 
 
