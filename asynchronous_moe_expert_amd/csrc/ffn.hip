@@ -164,17 +164,17 @@ __device__ __forceinline__ void static_for(F&& f) {
 // Tile piece t (16 bytes) is the MFMA A-operand run of lane t%64 for row tile t/128 and
 // k-half (t/64)%2, so piece t sits at LDS byte 16t and a lane's operand read is one
 // conflict-free 16-byte access at 16*((2mt + h)*64 + lane).
-template <int MT>
+template <int MT, int NT>
 struct APart {
   static constexpr int kPieces = MT * 128;
-  static constexpr int J = (kPieces + 255) / 256;
+  static constexpr int J = (kPieces + NT - 1) / NT;  // pieces per thread (NT threads)
   u32x4 raw[J];
   __device__ __forceinline__ void load(const uint16_t* const* ap, int k0) {
     static_for<J>([&](auto j) { raw[j()] = *reinterpret_cast<const u32x4*>(ap[j()] + k0); });
   }
   __device__ __forceinline__ void store(u32x4* lds, int tid) const {
     static_for<J>([&](auto j) {
-      if (j() * 256 + tid < kPieces) lds[j() * 256 + tid] = raw[j()];
+      if (j() * NT + tid < kPieces) lds[j() * NT + tid] = raw[j()];
     });
   }
 };
@@ -271,15 +271,16 @@ __device__ __forceinline__ int next_unit(const int32_t* __restrict__ offsets, in
 // weights of the same k-step) and shared through a double-buffered LDS tile.  The grid is
 // at most what the device holds at once and strides over the units, so every unit of a
 // decode-sized batch starts in the first round and no workgroup slot goes to an idle unit.
-template <int MODE, int WDT, int NS, int MT, int R>
-__global__ __launch_bounds__(256) void ffn_mfma_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets,
+template <int MODE, int WDT, int NS, int MT, int R, int WV>
+__global__ __launch_bounds__(64 * WV) void ffn_mfma_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets,
                                                     int E_loc, const char* __restrict__ W,
                                                     const float* __restrict__ s0, const float* __restrict__ s1,
                                                     uint16_t* __restrict__ out, int Kd, int Nw, int out_ld,
                                                     int n_blocks_N, int n_rows) {
   constexpr int BM = MT * 16;
   static_assert(MODE == 1 || NS % 2 == 0, "gate/up waves own (gate, up) strip pairs");
-  __shared__ u32x4 a_lds[2][APart<MT>::kPieces];
+  using AP = APart<MT, 64 * WV>;
+  __shared__ u32x4 a_lds[2][AP::kPieces];
   constexpr int esz = WDT == MOE_FP8_E4M3 ? 1 : 2;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -309,15 +310,15 @@ __global__ __launch_bounds__(256) void ffn_mfma_kernel(const uint16_t* __restric
   }
   for (; u < u_end; u += G >> 3, e = next_unit(offsets, E_loc, n_rows, BM, lane, u, u_end, total, nb, m0, mend)) {
     if (e < 0) break;  // not reachable: the table is the same on every build
-    const int strip0 = (nb * kFfnWaves + wv) * NS;  // this wave's first strip
+    const int strip0 = (nb * WV + wv) * NS;  // this wave's first strip
     const bool wact = strip0 < n_strips;            // (the last block may be partial)
     const char* wlane = W + (int64_t)e * Nw * Kd * esz + (int64_t)(wact ? strip0 : 0) * strip_stride + lane * 16;
     // activation pieces of this thread (rows past the chunk read a copy of its last row;
     // their results are never stored)
-    const uint16_t* ap[APart<MT>::J];
+    const uint16_t* ap[AP::J];
 #pragma unroll
-    for (int j = 0; j < APart<MT>::J; ++j) {
-      const int t = min(j * 256 + tid, APart<MT>::kPieces - 1), l = t & 63;
+    for (int j = 0; j < AP::J; ++j) {
+      const int t = min(j * 64 * WV + tid, AP::kPieces - 1), l = t & 63;
       int r = m0 + (t >> 7) * 16 + (l & 15);
       r = r < mend ? r : mend - 1;
       ap[j] = A + (int64_t)r * Kd + (l >> 4) * 16 + ((t >> 6) & 1) * 8;
@@ -351,16 +352,19 @@ __global__ __launch_bounds__(256) void ffn_mfma_kernel(const uint16_t* __restric
     // result unused), park this thread's activation piece of step i in LDS, barrier, MFMAs.
     // Ring slots are compile-time indices so that every slot lives in registers.
     WTile<WDT, NS> wr[R];
-    APart<MT> ar[R];
+    AP ar[R];
+    // Every load is unconditional (an idle wave streams valid strip-0 weights and its
+    // results are never stored): a load under a branch makes the compiler's wait counts
+    // assume the branch was not taken, which drains the ring at every k-step.
     auto issue = [&](auto slot, int ks) {
       ks = min(ks, KS - 1);
-      if (wact) wr[slot()].load(wlane + ks * blk_bytes, strip_stride);
+      wr[slot()].load(wlane + ks * blk_bytes, strip_stride);
       ar[slot()].load(ap, ks * kBK);
     };
     auto step = [&](auto slot, int i) {
       ar[slot()].store(a_lds[i & 1], tid);
       wg_barrier();
-      if (wact) compute(wr[slot()], a_lds[i & 1]);
+      compute(wr[slot()], a_lds[i & 1]);
     };
     static_for<R - 1>([&](auto v) { issue(v, v()); });
     int it = 0;
@@ -440,16 +444,16 @@ static int resident_workgroups(int threads) {
   return r;
 }
 
-template <int MODE, int WDT, int NS, int MT, int R>
+template <int MODE, int WDT, int NS, int MT, int R, int WV>
 static void launch_mfma_t(const void* A, const int32_t* offsets, int E_loc, const void* W, const float* s0,
                           const float* s1, void* out, int Kd, int Nw, int out_ld, int n, hipStream_t stream) {
   constexpr int BM = MT * 16;
-  constexpr auto kernel = ffn_mfma_kernel<MODE, WDT, NS, MT, R>;
-  const int n_blocks_N = (Nw / 16 + kFfnWaves * NS - 1) / (kFfnWaves * NS);
+  constexpr auto kernel = ffn_mfma_kernel<MODE, WDT, NS, MT, R, WV>;
+  const int n_blocks_N = (Nw / 16 + WV * NS - 1) / (WV * NS);
   const int64_t chunks_max = (n + (int64_t)(BM - 1) * E_loc) / BM;  // ragged worst case
-  int64_t grid = std::min<int64_t>(chunks_max * n_blocks_N, resident_workgroups<kernel>(256));
+  int64_t grid = std::min<int64_t>(chunks_max * n_blocks_N, resident_workgroups<kernel>(64 * WV));
   grid = (grid + 7) / 8 * 8;  // the XCD-aware order needs a multiple of 8
-  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), 0, stream, (const uint16_t*)A, offsets, E_loc,
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(64 * WV), 0, stream, (const uint16_t*)A, offsets, E_loc,
                      (const char*)W, s0, s1, (uint16_t*)out, Kd, Nw, out_ld, n_blocks_N, n);
 }
 
@@ -747,6 +751,12 @@ static void launch_gemm(const void* A, const int32_t* offsets, int E_loc, const 
 #ifndef MOE_FFN_R_D
 #define MOE_FFN_R_D 4
 #endif
+#ifndef MOE_FFN_WV_GU
+#define MOE_FFN_WV_GU 4
+#endif
+#ifndef MOE_FFN_WV_D
+#define MOE_FFN_WV_D 4
+#endif
 
 static int pick_mt(int n, int E_loc) {
   if (MOE_FFN_MT > 0) return MOE_FFN_MT;
@@ -765,13 +775,14 @@ static void launch_mfma(const void* A, const int32_t* offsets, int E_loc, const 
                         const float* s1, void* out, int Kd, int Nw, int out_ld, int n, hipStream_t stream) {
   constexpr int NS = MODE == 0 ? MOE_FFN_NS_GU : MOE_FFN_NS_D;
   constexpr int R = MODE == 0 ? MOE_FFN_R_GU : MOE_FFN_R_D;
+  constexpr int WV = MODE == 0 ? MOE_FFN_WV_GU : MOE_FFN_WV_D;
   if (MOE_FFN_MT == 0 && n >= MOE_FFN_GEMM_ROWS * E_loc) {
     launch_gemm<MODE, WDT>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, stream);
     return;
   }
   switch (pick_mt(n, E_loc)) {
-    case 2: launch_mfma_t<MODE, WDT, NS, 2, R>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, stream); break;
-    default: launch_mfma_t<MODE, WDT, NS, 3, R>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, stream); break;
+    case 2: launch_mfma_t<MODE, WDT, NS, 2, R, WV>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, stream); break;
+    default: launch_mfma_t<MODE, WDT, NS, 3, R, WV>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, stream); break;
   }
 }
 
