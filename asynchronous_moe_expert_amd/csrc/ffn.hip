@@ -587,13 +587,17 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(const uint16_t* __rest
       const int strip = colw / 16 + (MODE == 0 ? 2 * half + t() : 2 * t() + half);
       wvo[t()] = (int)(strip * strip_stride) + (32 * hf + r) * 16;
     });
-    // activation DMA: instruction d of this wave fills the 16-byte slots (4wv + d)*64 + lane
-    // of a stage; slot P holds row P/8, 16-byte piece (P%8) ^ ((P/8 >> 1) & 7) of the row
-    const uint16_t* adma[4];
+    // activation loads: instruction d of this wave fills the 16-byte slots (4wv + d)*64 + lane
+    // of a stage; slot P holds row P/8, 16-byte piece (P%8) ^ ((P/8 >> 1) & 7) of the row.
+    // Buffer loads (byte offset per lane, k-step in a scalar register) like the weights:
+    // the compiler then keeps the prologue's loads in program order, so the steady-state
+    // wait counts hold from the first k-step on.
+    const __amdgpu_buffer_rsrc_t ars = buffer_rsrc(A, (int64_t)n_rows * Kd * 2);
+    int avo[4];
     static_for<4>([&](auto d) {
       const int P = (wv * 4 + d()) * 64 + lane, row = P >> 3, kq = (P & 7) ^ ((row >> 1) & 7);
       const int r = min(m0 + row, mend - 1);
-      adma[d()] = A + (int64_t)r * Kd + kq * 8;
+      avo[d()] = (r * Kd + kq * 8) * 2;
     });
 
     f32x16 acc[4][2];
@@ -604,7 +608,7 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(const uint16_t* __rest
     u32x4 af[4][4];     // activation fragments [k-slice s][mt] of the step being computed
     auto issue_a = [&](auto aslot, int ks) {
       ks = min(ks, KS - 1);
-      static_for<4>([&](auto d) { ar[aslot()][d()] = *reinterpret_cast<const u32x4*>(adma[d()] + ks * kBK); });
+      static_for<4>([&](auto d) { ar[aslot()][d()] = __builtin_amdgcn_raw_buffer_load_b128(ars, avo[d()], ks * kBK * 2, 0); });
     };
     auto issue_w = [&](auto slot, int ks) { wr[slot()].load(wrs, wvo, min(ks, KS - 1) * 1024 * esz); };
     // park this thread's pieces of a step in LDS; the compiler waits for their loads only
@@ -751,11 +755,15 @@ static void launch_gemm(const void* A, const int32_t* offsets, int E_loc, const 
 #ifndef MOE_FFN_R_D
 #define MOE_FFN_R_D 4
 #endif
+// Waves per workgroup.  A CU streams at most ~27 GB/s (its outstanding L1 misses over the
+// HBM latency), so the kernel time is set by the busiest CU: at the decode shape (8 experts,
+// 2880 x 2880) 6 waves x 2 strips (gate/up) and 3 waves x 2 strips (down) make 240 units,
+// at most one per CU, where 4-wave units made 360 (two on some CUs) and 184.
 #ifndef MOE_FFN_WV_GU
-#define MOE_FFN_WV_GU 4
+#define MOE_FFN_WV_GU 6
 #endif
 #ifndef MOE_FFN_WV_D
-#define MOE_FFN_WV_D 4
+#define MOE_FFN_WV_D 3
 #endif
 
 static int pick_mt(int n, int E_loc) {
