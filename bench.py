@@ -12,6 +12,12 @@ before the timed region; every step therefore releases all of its tokens.
 Prints one JSON line with the step throughput (expert tokens/s), the roofline of the
 dominant kernel (the gate/up GEMM, timed with HIP events on the launch stream) and the
 CPU oracle timed on a bounded sample on the host.
+
+--workload prefill times the prefill-shaped rank share instead (256 experts, top-8, 32
+local experts, hidden 4096, intermediate 2048, fp8 e4m3 weights with bf16 activations,
+16384 pairs with Zipf(1.0) routing arriving in four waves of 6554/4915/3277/1638, each
+its own step).  Its line reports the FFN against the bf16 MFMA peak and the gather and
+combine against the HBM peak.
 """
 from __future__ import annotations
 
@@ -109,6 +115,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle CPU-baseline budget (0 = skip)")
+    ap.add_argument("--workload", choices=["decode", "prefill"], default="decode")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="copy 256 MiB device to device once before the warm-up (reference dispatch for "
                          "rocprofv3 byte counters)")
@@ -118,6 +125,8 @@ def main() -> int:
               "of this build (use --gpus 1)", file=sys.stderr)
         return 2
 
+    if args.workload == "prefill":
+        return run_prefill(args)
     import torch
 
     import asynchronous_moe_expert_amd as M
@@ -234,6 +243,119 @@ def main() -> int:
         out["cpu_baseline"] = cpu_baseline(b, wts, args.cpu_seconds)
     else:
         out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def cpu_baseline_prefill(setup, b, seconds: float) -> dict:
+    """The oracle's FFN (fp64) on a seeded sample of the first wave's rows, for `seconds`."""
+    import threadpoolctl
+
+    import oracle as O
+
+    info = threadpoolctl.threadpool_info()
+    cores = max([i.get("num_threads", 1) for i in info] or [1])
+    rng = np.random.default_rng(7)
+    rows, reps = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        pick = rng.choice(b.n, 16, replace=False)
+        x = O.decode(b.pool[b.slot[pick]], "bf16")
+        O.ffn_rows(x, b.expert[pick] - b.expert_base, setup.weights)
+        rows += len(pick)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": rows / el, "unit": "expert tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{rows} seeded rows of prefill wave 0 ({reps} draws of 16), fp64 SwiGLU FFN only "
+                      f"(assemble and combine are a small share of the oracle's time), {el:.1f} s"}
+
+
+def run_prefill(args) -> int:
+    """Prefill-shaped rank share: each of the four waves is one step (assemble, FFN,
+    combine of the local result into tokens whose 7 remote results were delivered first)."""
+    import torch
+
+    import asynchronous_moe_expert_amd as M
+    import workloads as W
+    from workloads.device import batch_tensors, weight_tensors
+
+    M.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    setup = W.c4_prefill_setup()
+    waves = [W.c4_wave(setup, w) for w in range(4)]
+    E, H, I, K, P = setup.weights.E, setup.weights.H, setup.weights.I, waves[0].K, waves[0].P
+    n_max = max(b.n for b in waves)
+    wt = weight_tensors(setup.weights)
+    st = M.ExpertStep(E, H, I, K, M.MOE_BF16, M.MOE_FP8_E4M3, n_max, P)
+    st.load_weights(wt["wg"], wt["wu"], wt["wd"], wt["s_gate"], wt["s_up"], wt["s_down"])
+    del wt
+    pool = batch_tensors(waves[0])["pool"]
+    dw = []
+    for b in waves:
+        d = batch_tensors(b)
+        d.pop("pool")
+        dw.append(d)
+    ev = HipEvents()
+    stream = torch.cuda.current_stream().cuda_stream
+    reps = max(1, args.steps // 4)
+    W_reps = max(1, args.warmup // 4)
+    names = ["assemble", "gate_up", "down", "combine"]
+    times = {w: {k: [] for k in names} for w in range(4)}
+    evs = [ev.create() for _ in range(5)]
+    for rep in range(W_reps + reps):
+        for w, b in enumerate(waves):
+            d = dw[w]
+            M.moe_state_reset(st.state, 0)
+            st.combine(d["r_rows"], d["r_idx"], d["r_tok"], d["r_kslot"], d["r_w"], d["r_gen"])
+            ev.record(evs[0], stream)
+            st.assemble(d["slot"], d["expert"], b.expert_base, pool, n=b.n)
+            ev.record(evs[1], stream)
+            st.ffn(b.n, ev_mid=evs[2])
+            ev.record(evs[3], stream)
+            st.combine(st.y, st.pos, d["tok"], d["kslot"], d["w"], d["gen"], m=b.n, n_rows=b.n)
+            ev.record(evs[4], stream)
+            torch.cuda.synchronize()
+            assert int(st.err.item()) == 0 and int(st.rel_count.item()) == b.n, "prefill step did not release"
+            if rep >= W_reps:
+                for k, nm in enumerate(names):
+                    times[w][nm].append(ev.ms(evs[k], evs[k + 1]))
+    med = {w: {nm: float(np.median(times[w][nm])) for nm in names} for w in range(4)}
+    step_ms = sum(sum(med[w].values()) for w in range(4))
+    n_tot = sum(b.n for b in waves)
+    value = n_tot / (step_ms * 1e-3)
+    per_wave = []
+    for w, b in enumerate(waves):
+        m = med[w]
+        n = b.n
+        fl_gu, fl_dn = 4.0 * n * H * I, 2.0 * n * H * I
+        g_bytes = 2 * n * H * 2 + 16 * n                 # gather: read + write rows, metadata
+        c_bytes = n * H * 2 + n * H * (4 + 2) + 24 * n   # combine: result rows, held sums, released rows
+        per_wave.append({"pairs": n, "us": {k: round(v * 1e3, 2) for k, v in m.items()},
+                         "ffn_mfma_frac": round((fl_gu + fl_dn) / ((m["gate_up"] + m["down"]) * 1e-3) / 1e12
+                                                / BF16_PEAK_TFLOPS, 4),
+                         "assemble_hbm_frac": round(g_bytes / (m["assemble"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "combine_hbm_frac": round(c_bytes / (m["combine"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+    b0, m0 = waves[0], med[0]
+    gu_tf = 4.0 * b0.n * H * I / (m0["gate_up"] * 1e-3) / 1e12
+    out = {
+        "metric": "expert tokens/sec per GPU (assemble+FFN+combine)",
+        "value": round(value, 1), "unit": "expert tokens/s", "n_gpus": 1, "steps": reps * 4, "warmup": W_reps * 4,
+        "ms_per_step": round(step_ms / 4, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 activations, fp8 e4m3 weights, fp32 accumulate", "data": "synthetic (seeded; random-init expert weights)",
+        "config": {"workload": "prefill-shaped EP rank share: 32 of 256 experts, top-8, hidden 4096, SwiGLU "
+                               "intermediate 2048, 16384 pairs (Zipf 1.0) in waves of 6554/4915/3277/1638",
+                   "E_loc": E, "K": K, "H": H, "I": I, "pairs": n_tot, "pool_slots": P},
+        "roofline": {"bound": "mfma", "kernel": "ffn gate/up GEMM, wave 0 (6554 pairs)", "achieved": round(gu_tf, 1),
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(gu_tf / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None},
+        "waves": per_wave,
+        "note": "per-stage medians of HIP-event intervals on the launch stream; each step is timed alone "
+                "(state reset and remote delivery untimed before it)",
+    }
+    out["cpu_baseline"] = cpu_baseline_prefill(setup, waves[0], args.cpu_seconds) if args.cpu_seconds > 0 else None
     print(json.dumps(out), flush=True)
     return 0
 
