@@ -40,7 +40,8 @@ class PackArgs(C.Structure):
 class FfnArgs(C.Structure):
     _fields_ = [("n", _i32), ("E_loc", _i32), ("H", _i32), ("I", _i32), ("act_dtype", _i32), ("w_dtype", _i32),
                 ("xb", _p), ("offsets", _p), ("w_gu", _p), ("w_d", _p), ("s_gate", _p), ("s_up", _p),
-                ("s_down", _p), ("y", _p), ("workspace", _p), ("workspace_bytes", C.c_size_t), ("ev_mid", _p)]
+                ("s_down", _p), ("y", _p), ("workspace", _p), ("workspace_bytes", C.c_size_t), ("ev_mid", _p),
+                ("perm", _p), ("slot", _p), ("pool", _p), ("P", _i64), ("pool_pitch", _i64)]
 
 
 class StateC(C.Structure):
@@ -144,8 +145,9 @@ def moe_ffn_workspace_size(n_max: int, E_loc: int, H: int, I: int, act_dtype: in
 def moe_assemble(slot, expert, expert_base: int, E_loc: int, pool, perm, pos, counts, offsets, xb, err,
                  n: int | None = None, stream=None) -> None:
     """pool: [P][pitch] (f32 or bf16); xb: [>= n][H] of the same dtype."""
+    H = pool.shape[1] if xb is None else xb.shape[1]
     a = AssembleArgs(int(slot.numel() if n is None else n), _ptr(slot), _ptr(expert), expert_base, E_loc,
-                     _ptr(pool), pool.shape[0], pool.stride(0), xb.shape[1], dtype_code(pool), _ptr(perm),
+                     _ptr(pool), pool.shape[0], pool.stride(0), H, dtype_code(pool), _ptr(perm),
                      _ptr(pos), _ptr(counts), _ptr(offsets), _ptr(xb), _ptr(err))
     _check(load().moe_assemble(C.byref(a), _stream(stream)), "moe_assemble")
 
@@ -158,10 +160,16 @@ def moe_pack_ffn_weights(wg, wu, wd, w_gu, w_d, w_dtype: int, stream=None) -> No
 
 def moe_expert_ffn_grouped(n: int, E_loc: int, H: int, I: int, act_dtype: int, w_dtype: int, xb, offsets, w_gu,
                            w_d, y, workspace, s_gate=None, s_up=None, s_down=None, ev_mid: int | None = None,
-                           stream=None) -> None:
+                           stream=None, gather=None) -> None:
+    """gather=(perm, slot, pool): read batch rows from the pool (gather-on-load); xb may be None."""
+    perm = slot = pool = None
+    P = pitch = 0
+    if gather is not None:
+        perm, slot, pool = gather
+        P, pitch = pool.shape[0], pool.stride(0)
     a = FfnArgs(n, E_loc, H, I, act_dtype, w_dtype, _ptr(xb), _ptr(offsets), _ptr(w_gu), _ptr(w_d),
                 _ptr(s_gate), _ptr(s_up), _ptr(s_down), _ptr(y), _ptr(workspace),
-                workspace.numel() * workspace.element_size(), ev_mid)
+                workspace.numel() * workspace.element_size(), ev_mid, _ptr(perm), _ptr(slot), _ptr(pool), P, pitch)
     _check(load().moe_expert_ffn_grouped(C.byref(a), _stream(stream)), "moe_expert_ffn_grouped")
 
 

@@ -158,12 +158,12 @@ extern "C" int moe_assemble(const moe_assemble_args* a, hipStream_t stream) {
   const int64_t pitch_bytes = a->pool_pitch * esz;
   if (row_bytes % 16 || pitch_bytes % 16) return MOE_EINVAL_ALIGN;
   if (a->n > 0) {
-    if (!a->slot || !a->expert || !a->perm || !a->pool || !a->xb) return MOE_EINVAL_NULL;
-    if (!aligned16(a->pool) || !aligned16(a->xb)) return MOE_EINVAL_ALIGN;
+    if (!a->slot || !a->expert || !a->perm || !a->pool) return MOE_EINVAL_NULL;
+    if (!aligned16(a->pool) || (a->xb && !aligned16(a->xb))) return MOE_EINVAL_ALIGN;
   }
   hipLaunchKernelGGL(assemble_index_kernel, dim3(1), dim3(kAsmThreads), 0, stream, a->n, a->slot, a->expert,
                      a->expert_base, a->E_loc, a->P, a->perm, a->pos, a->counts, a->offsets, a->err);
-  if (a->n == 0) return launch_status();
+  if (a->n == 0 || !a->xb) return launch_status();  // no xb: the FFN gathers on load
   const int cpr = row_bytes / 16;
   const int64_t work = (int64_t)a->n * cpr;
   int64_t blocks = (work + 255) / 256;

@@ -58,6 +58,25 @@ __global__ __launch_bounds__(256) void pack_kernel(const T* __restrict__ src, T*
   }
 }
 
+// ------------------------------------------------------------- gather-on-load rows
+// Where batch row r's activations live.  Without a gather (perm == nullptr) they are row r
+// of the batch matrix A ([n][Kd]).  With one, A is the token pool and row r is pool row
+// slot[perm[r]] (clamped into [0, P): a pair moe_assemble rejected has no batch row, so
+// the clamps only guard against inconsistent inputs), pitch `pitch` elements.
+struct GatherRows {
+  const int32_t* perm;
+  const int32_t* slot;
+  int64_t pitch;
+  int64_t P;
+  __device__ __forceinline__ int64_t row_offset(int r, int Kd) const {
+    if (perm == nullptr) return (int64_t)r * Kd;
+    const int q = perm[r];
+    int64_t s = slot[q < 0 ? 0 : q];
+    s = s < 0 ? 0 : (s >= P ? P - 1 : s);
+    return s * pitch;
+  }
+};
+
 // --------------------------------------------------------------- expert lookup helpers
 __device__ __forceinline__ int expert_of_row(const int32_t* __restrict__ offsets, int E_loc, int r) {
   for (int e = 0; e < E_loc; ++e)
@@ -75,7 +94,7 @@ __device__ __forceinline__ float silu_mul_fast(float g, float u) {
 // Small-shape path (fp32 activations and weights): one thread per output element.
 __global__ __launch_bounds__(256) void gateup_f32_kernel(const float* __restrict__ xb, const int32_t* __restrict__ offsets,
                                                          int E_loc, int n, int H, int I, const float* __restrict__ wgu,
-                                                         float* __restrict__ h) {
+                                                         float* __restrict__ h, GatherRows gr) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int r = (int)(idx / I), i = (int)(idx - (int64_t)r * I);
   if (r >= n || r >= offsets[E_loc]) return;
@@ -83,9 +102,10 @@ __global__ __launch_bounds__(256) void gateup_f32_kernel(const float* __restrict
   if (e < 0) return;
   const float* w = wgu + (int64_t)e * 2 * I * H;
   const int64_t rg = gu_packed_row(i, false), ru = gu_packed_row(i, true);
+  const float* xr = xb + gr.row_offset(r, H);
   float g = 0.f, u = 0.f;
   for (int k = 0; k < H; ++k) {
-    const float x = xb[(int64_t)r * H + k];
+    const float x = xr[k];
     g = fmaf(x, w[packed_index(rg, k, H, 4)], g);
     u = fmaf(x, w[packed_index(ru, k, H, 4)], u);
   }
@@ -276,7 +296,7 @@ __global__ __launch_bounds__(64 * WV) void ffn_mfma_kernel(const uint16_t* __res
                                                     int E_loc, const char* __restrict__ W,
                                                     const float* __restrict__ s0, const float* __restrict__ s1,
                                                     uint16_t* __restrict__ out, int Kd, int Nw, int out_ld,
-                                                    int n_blocks_N, int n_rows) {
+                                                    int n_blocks_N, int n_rows, GatherRows gr) {
   constexpr int BM = MT * 16;
   static_assert(MODE == 1 || NS % 2 == 0, "gate/up waves own (gate, up) strip pairs");
   using AP = APart<MT, 64 * WV>;
@@ -321,7 +341,7 @@ __global__ __launch_bounds__(64 * WV) void ffn_mfma_kernel(const uint16_t* __res
       const int t = min(j * 64 * WV + tid, AP::kPieces - 1), l = t & 63;
       int r = m0 + (t >> 7) * 16 + (l & 15);
       r = r < mend ? r : mend - 1;
-      ap[j] = A + (int64_t)r * Kd + (l >> 4) * 16 + ((t >> 6) & 1) * 8;
+      ap[j] = A + gr.row_offset(r, Kd) + (l >> 4) * 16 + ((t >> 6) & 1) * 8;
     }
 
     f32x4 acc[MT][NS];
@@ -446,7 +466,8 @@ static int resident_workgroups(int threads) {
 
 template <int MODE, int WDT, int NS, int MT, int R, int WV>
 static void launch_mfma_t(const void* A, const int32_t* offsets, int E_loc, const void* W, const float* s0,
-                          const float* s1, void* out, int Kd, int Nw, int out_ld, int n, hipStream_t stream) {
+                          const float* s1, void* out, int Kd, int Nw, int out_ld, int n, GatherRows gr,
+                          hipStream_t stream) {
   constexpr int BM = MT * 16;
   constexpr auto kernel = ffn_mfma_kernel<MODE, WDT, NS, MT, R, WV>;
   const int n_blocks_N = (Nw / 16 + WV * NS - 1) / (WV * NS);
@@ -454,7 +475,7 @@ static void launch_mfma_t(const void* A, const int32_t* offsets, int E_loc, cons
   int64_t grid = std::min<int64_t>(chunks_max * n_blocks_N, resident_workgroups<kernel>(64 * WV));
   grid = (grid + 7) / 8 * 8;  // the XCD-aware order needs a multiple of 8
   hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(64 * WV), 0, stream, (const uint16_t*)A, offsets, E_loc,
-                     (const char*)W, s0, s1, (uint16_t*)out, Kd, Nw, out_ld, n_blocks_N, n);
+                     (const char*)W, s0, s1, (uint16_t*)out, Kd, Nw, out_ld, n_blocks_N, n, gr);
 }
 
 // ------------------------------------------------------------ prefill GEMM path
@@ -539,7 +560,7 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(const uint16_t* __rest
                                                        int E_loc, const char* __restrict__ W,
                                                        const float* __restrict__ s0, const float* __restrict__ s1,
                                                        uint16_t* __restrict__ out, int Kd, int Nw, int out_ld,
-                                                       int n_blocks_N, int n_rows) {
+                                                       int n_blocks_N, int n_rows, GatherRows gr) {
   constexpr int S = kGemmStages;
   constexpr int esz = WDT == MOE_FP8_E4M3 ? 1 : 2;
   __shared__ u32x4 a_lds[2][kGemmBM * 8];  // activation k-tile, 2 stages of 16 KiB
@@ -592,12 +613,14 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(const uint16_t* __rest
     // Buffer loads (byte offset per lane, k-step in a scalar register) like the weights:
     // the compiler then keeps the prologue's loads in program order, so the steady-state
     // wait counts hold from the first k-step on.
-    const __amdgpu_buffer_rsrc_t ars = buffer_rsrc(A, (int64_t)n_rows * Kd * 2);
+    // (with a gather, A is the pool: the host checks that it spans under 2 GiB)
+    const __amdgpu_buffer_rsrc_t ars =
+        buffer_rsrc(A, gr.perm ? gr.P * gr.pitch * 2 : (int64_t)n_rows * Kd * 2);
     int avo[4];
     static_for<4>([&](auto d) {
       const int P = (wv * 4 + d()) * 64 + lane, row = P >> 3, kq = (P & 7) ^ ((row >> 1) & 7);
       const int r = min(m0 + row, mend - 1);
-      avo[d()] = (r * Kd + kq * 8) * 2;
+      avo[d()] = (int)((gr.row_offset(r, Kd) + kq * 8) * 2);
     });
 
     f32x16 acc[4][2];
@@ -728,14 +751,15 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(const uint16_t* __rest
 
 template <int MODE, int WDT>
 static void launch_gemm(const void* A, const int32_t* offsets, int E_loc, const void* W, const float* s0,
-                        const float* s1, void* out, int Kd, int Nw, int out_ld, int n, hipStream_t stream) {
+                        const float* s1, void* out, int Kd, int Nw, int out_ld, int n, GatherRows gr,
+                        hipStream_t stream) {
   constexpr auto kernel = ffn_gemm_kernel<MODE, WDT>;
   const int n_blocks_N = (Nw + kGemmBN - 1) / kGemmBN;
   const int64_t chunks_max = (n + (int64_t)(kGemmBM - 1) * E_loc) / kGemmBM;
   int64_t grid = std::min<int64_t>(chunks_max * n_blocks_N, resident_workgroups<kernel>(256));
   grid = (grid + 7) / 8 * 8;
   hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), 0, stream, (const uint16_t*)A, offsets, E_loc,
-                     (const char*)W, s0, s1, (uint16_t*)out, Kd, Nw, out_ld, n_blocks_N, n);
+                     (const char*)W, s0, s1, (uint16_t*)out, Kd, Nw, out_ld, n_blocks_N, n, gr);
 }
 
 // Row-chunk height: tall enough that an average expert group fits one chunk with room for
@@ -780,17 +804,20 @@ static int pick_mt(int n, int E_loc) {
 
 template <int MODE, int WDT>
 static void launch_mfma(const void* A, const int32_t* offsets, int E_loc, const void* W, const float* s0,
-                        const float* s1, void* out, int Kd, int Nw, int out_ld, int n, hipStream_t stream) {
+                        const float* s1, void* out, int Kd, int Nw, int out_ld, int n, GatherRows gr,
+                        hipStream_t stream) {
   constexpr int NS = MODE == 0 ? MOE_FFN_NS_GU : MOE_FFN_NS_D;
   constexpr int R = MODE == 0 ? MOE_FFN_R_GU : MOE_FFN_R_D;
   constexpr int WV = MODE == 0 ? MOE_FFN_WV_GU : MOE_FFN_WV_D;
-  if (MOE_FFN_MT == 0 && n >= MOE_FFN_GEMM_ROWS * E_loc) {
-    launch_gemm<MODE, WDT>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, stream);
+  // (the GEMM kernel addresses its activation operand with 32-bit byte offsets)
+  const int64_t a_bytes = gr.perm ? gr.P * gr.pitch * 2 : (int64_t)n * Kd * 2;
+  if (MOE_FFN_MT == 0 && n >= MOE_FFN_GEMM_ROWS * E_loc && a_bytes < ((int64_t)1 << 31)) {
+    launch_gemm<MODE, WDT>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, gr, stream);
     return;
   }
   switch (pick_mt(n, E_loc)) {
-    case 2: launch_mfma_t<MODE, WDT, NS, 2, R, WV>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, stream); break;
-    default: launch_mfma_t<MODE, WDT, NS, 3, R, WV>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, stream); break;
+    case 2: launch_mfma_t<MODE, WDT, NS, 2, R, WV>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, gr, stream); break;
+    default: launch_mfma_t<MODE, WDT, NS, 3, R, WV>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, gr, stream); break;
   }
 }
 
@@ -847,9 +874,22 @@ extern "C" int moe_expert_ffn_grouped(const moe_ffn_args* a, hipStream_t stream)
     if (a->ev_mid) (void)hipEventRecord(a->ev_mid, stream);
     return MOE_OK;
   }
-  if (!a->xb || !a->w_gu || !a->w_d || !a->y) return MOE_EINVAL_NULL;
+  // the rows the gate/up projection reads: the batch xb, or pool rows through the queue
+  GatherRows gr{nullptr, nullptr, 0, 0};
+  const void* x_src = a->xb;
+  if (a->perm) {
+    const int esz = dtype_size(a->act_dtype);
+    if (!a->slot || !a->pool) return MOE_EINVAL_NULL;
+    if (a->P < 1 || a->pool_pitch < a->H) return MOE_EINVAL_SIZE;
+    if (!f32 && (double)a->P * (double)a->pool_pitch * esz >= 2147483648.0) return MOE_EINVAL_SIZE;
+    if (!aligned16(a->pool) || (a->pool_pitch * esz) % 16) return MOE_EINVAL_ALIGN;
+    gr = GatherRows{a->perm, a->slot, a->pool_pitch, a->P};
+    x_src = a->pool;
+  }
+  if (!x_src || !a->w_gu || !a->w_d || !a->y) return MOE_EINVAL_NULL;
   if (f8 && (!a->s_gate || !a->s_up || !a->s_down)) return MOE_EINVAL_NULL;
-  if (!aligned16(a->xb) || !aligned16(a->w_gu) || !aligned16(a->w_d) || !aligned16(a->y)) return MOE_EINVAL_ALIGN;
+  if (!aligned16(x_src) || !aligned16(a->w_gu) || !aligned16(a->w_d) || !aligned16(a->y)) return MOE_EINVAL_ALIGN;
+  const GatherRows none{nullptr, nullptr, 0, 0};
   const size_t ws = moe_ffn_workspace_size(a->n, a->E_loc, a->H, a->I, a->act_dtype);
   if (!a->workspace || a->workspace_bytes < ws) return MOE_EWORKSPACE;
   if (!aligned16(a->workspace)) return MOE_EINVAL_ALIGN;
@@ -857,21 +897,22 @@ extern "C" int moe_expert_ffn_grouped(const moe_ffn_args* a, hipStream_t stream)
   if (f32) {
     const int64_t t1 = (int64_t)n * I, t2 = (int64_t)n * H;
     hipLaunchKernelGGL(gateup_f32_kernel, dim3((unsigned)((t1 + 255) / 256)), dim3(256), 0, stream,
-                       (const float*)a->xb, a->offsets, E, n, H, I, (const float*)a->w_gu, (float*)a->workspace);
+                       (const float*)x_src, a->offsets, E, n, H, I, (const float*)a->w_gu, (float*)a->workspace, gr);
     if (a->ev_mid) (void)hipEventRecord(a->ev_mid, stream);
     hipLaunchKernelGGL(down_f32_kernel, dim3((unsigned)((t2 + 255) / 256)), dim3(256), 0, stream,
                        (const float*)a->workspace, a->offsets, E, n, H, I, (const float*)a->w_d, (float*)a->y);
     return launch_status();
   }
   if (bf) {
-    launch_mfma<0, MOE_BF16>(a->xb, a->offsets, E, a->w_gu, nullptr, nullptr, a->workspace, H, 2 * I, I, n, stream);
+    launch_mfma<0, MOE_BF16>(x_src, a->offsets, E, a->w_gu, nullptr, nullptr, a->workspace, H, 2 * I, I, n, gr, stream);
     if (a->ev_mid) (void)hipEventRecord(a->ev_mid, stream);
-    launch_mfma<1, MOE_BF16>(a->workspace, a->offsets, E, a->w_d, nullptr, nullptr, a->y, I, H, H, n, stream);
+    launch_mfma<1, MOE_BF16>(a->workspace, a->offsets, E, a->w_d, nullptr, nullptr, a->y, I, H, H, n, none, stream);
   } else {
-    launch_mfma<0, MOE_FP8_E4M3>(a->xb, a->offsets, E, a->w_gu, a->s_gate, a->s_up, a->workspace, H, 2 * I, I, n,
+    launch_mfma<0, MOE_FP8_E4M3>(x_src, a->offsets, E, a->w_gu, a->s_gate, a->s_up, a->workspace, H, 2 * I, I, n, gr,
                                  stream);
     if (a->ev_mid) (void)hipEventRecord(a->ev_mid, stream);
-    launch_mfma<1, MOE_FP8_E4M3>(a->workspace, a->offsets, E, a->w_d, a->s_down, nullptr, a->y, I, H, H, n, stream);
+    launch_mfma<1, MOE_FP8_E4M3>(a->workspace, a->offsets, E, a->w_d, a->s_down, nullptr, a->y, I, H, H, n, none,
+                                 stream);
   }
   return launch_status();
 }

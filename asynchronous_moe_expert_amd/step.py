@@ -4,6 +4,10 @@ torch only allocates device memory here; every stage runs in libmoestep's kernel
   moe_assemble -> moe_expert_ffn_grouped -> moe_combine_release
 The local results are combined straight from the FFN output: arrival i of the combine is
 queue entry i, whose result row is pos[i] (the batch row moe_assemble gave it).
+
+With gather_on_load (the default) moe_assemble only builds the index (perm, pos, counts,
+offsets) and the FFN reads each batch row straight from the token pool through
+slot[perm[r]]; the contiguous batch is never written out.
 """
 from __future__ import annotations
 
@@ -16,7 +20,7 @@ _TORCH = {N.MOE_F32: torch.float32, N.MOE_BF16: torch.bfloat16, N.MOE_FP8_E4M3: 
 
 class ExpertStep:
     def __init__(self, E_loc: int, H: int, I: int, K: int, act_dtype: int, w_dtype: int, n_max: int, T_cap: int,
-                 device="cuda"):
+                 device="cuda", gather_on_load: bool = True):
         self.E_loc, self.H, self.I, self.K = E_loc, H, I, K
         self.act_dtype, self.w_dtype, self.n_max, self.T_cap = act_dtype, w_dtype, n_max, T_cap
         dev = torch.device(device)
@@ -38,6 +42,8 @@ class ExpertStep:
         self.cmb_ws = torch.empty(N.moe_combine_workspace_size(self.cmb_ws_m), dtype=torch.uint8, device=dev)
         self.out = torch.empty((T_cap, H), dtype=adt, device=dev)
         self.w_gu = self.w_d = None
+        self.gather_on_load = gather_on_load
+        self._gather = None  # (perm, slot, pool) of the last assemble when gathering on load
         self.s_gate = self.s_up = self.s_down = None
         N.moe_state_reset(self.state, 0)
 
@@ -50,13 +56,15 @@ class ExpertStep:
         self.s_gate, self.s_up, self.s_down = s_gate, s_up, s_down
 
     def assemble(self, slot, expert, expert_base: int, pool, n: int | None = None, stream=None) -> None:
+        xb = None if self.gather_on_load else self.xb
         N.moe_assemble(slot, expert, expert_base, self.E_loc, pool, self.perm, self.pos, self.counts, self.offsets,
-                       self.xb, self.err, n=n, stream=stream)
+                       xb, self.err, n=n, stream=stream)
+        self._gather = (self.perm, slot, pool) if self.gather_on_load else None
 
     def ffn(self, n: int, ev_mid: int | None = None, stream=None) -> None:
         N.moe_expert_ffn_grouped(n, self.E_loc, self.H, self.I, self.act_dtype, self.w_dtype, self.xb, self.offsets,
                                  self.w_gu, self.w_d, self.y, self.workspace, self.s_gate, self.s_up, self.s_down,
-                                 ev_mid=ev_mid, stream=stream)
+                                 ev_mid=ev_mid, stream=stream, gather=self._gather)
 
     def combine(self, rows, row_idx, tok, kslot, w, gen, m: int | None = None, n_rows: int | None = None,
                 stream=None) -> None:

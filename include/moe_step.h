@@ -87,6 +87,8 @@ typedef enum moe_status {
  *   perm[r]     = queue index of the pair at batch row r; -1 for r >= offsets[E_loc] (int32 [n])
  *   pos[i]      = batch row of queue entry i, or -1 if it was rejected (int32 [n]; may be NULL)
  *   xb[r][:]    = byte copy of pool row slot[perm[r]]                  ([n][H] act_dtype, pitch H)
+ * xb may be NULL: then no rows are copied and moe_expert_ffn_grouped reads them from the
+ * pool itself (gather-on-load, see moe_ffn_args.perm).
  * A pair is rejected (no row, flag raised) if slot is outside [0, P) or
  * expert - expert_base is outside [0, E_loc).
  * Limits: 0 <= n <= 2^24, 1 <= E_loc <= 256, act_dtype F32 or BF16, H * element size a
@@ -107,7 +109,7 @@ typedef struct moe_assemble_args {
   int32_t* pos;            /* out [n], optional */
   int32_t* counts;         /* out [E_loc] */
   int32_t* offsets;        /* out [E_loc + 1] */
-  void* xb;                /* out [n][H] */
+  void* xb;                /* out [n][H], optional */
   uint32_t* err;           /* device error word (OR-ed) */
 } moe_assemble_args;
 
@@ -151,7 +153,16 @@ int moe_pack_ffn_weights(const moe_pack_args* args, hipStream_t stream);
  * Limits: 1 <= E_loc <= 256, H % 64 == 0, I % 64 == 0, 0 <= n <= 2^24; 16-byte aligned
  * buffers.  The workspace must hold moe_ffn_workspace_size(...) bytes.
  * ev_mid: optional hipEvent_t recorded on the stream between the gate/up kernel and
- * the down kernel (for timing); pass NULL otherwise. */
+ * the down kernel (for timing); pass NULL otherwise.
+ *
+ * Gather-on-load ([SEP] section 6 fuses the gather of scattered token vectors into the
+ * computation that consumes them): when perm != NULL the gate/up projection reads batch
+ * row r straight from the token pool, row slot[perm[r]] (P rows, pitch pool_pitch
+ * elements), and xb is not read (it may be NULL).  perm and slot are those of the
+ * moe_assemble call for the same queue (which may then skip its copy, xb = NULL); a slot
+ * outside [0, P) is clamped into range (moe_assemble gives such pairs no batch row).
+ * The pool must be 16-byte aligned with pool_pitch * element size a multiple of 16, and
+ * for bf16 activations P * pool_pitch * 2 < 2^31 (MOE_EINVAL_SIZE otherwise). */
 typedef struct moe_ffn_args {
   int32_t n, E_loc, H, I;
   int32_t act_dtype, w_dtype;
@@ -166,6 +177,11 @@ typedef struct moe_ffn_args {
   void* workspace;
   size_t workspace_bytes;
   hipEvent_t ev_mid;       /* optional */
+  const int32_t* perm;     /* optional gather-on-load: [n] batch row -> queue index */
+  const int32_t* slot;     /* [n_queue] pool slot of each queue entry */
+  const void* pool;        /* [P][pool_pitch] token pool (act_dtype) */
+  int64_t P;               /* pool rows */
+  int64_t pool_pitch;      /* elements between pool rows */
 } moe_ffn_args;
 
 size_t moe_ffn_workspace_size(int32_t n_max, int32_t E_loc, int32_t H, int32_t I, int32_t act_dtype);

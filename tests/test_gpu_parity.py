@@ -385,3 +385,50 @@ def test_c4_prefill_wave0_sampled():
     eo = row_rel_err(decode_tensor(st.out[torch.as_tensor(toks, device="cuda").long()]), np.array(refs))
     _say(f"  sampled Y row err {ey:.3e}, combined row err {eo:.3e}")
     assert ey <= TOL["fp8"] and eo <= TOL["fp8"]
+
+
+GATHER_CASES = [
+    # (act/weight dtype, E, H, I, n, P): streaming kernel, 128-row GEMM kernel, fp32 path
+    ("bf16", 8, 2880, 2880, 256, 4096),
+    ("fp8", 3, 640, 192, 700, 900),
+    ("bf16", 4, 512, 256, 600, 1000),
+    ("f32", 3, 64, 128, 40, 64),
+]
+
+
+@pytest.mark.parametrize("case", GATHER_CASES, ids=[f"{c[0]}_E{c[1]}_H{c[2]}_n{c[4]}" for c in GATHER_CASES])
+def test_gather_on_load_matches_explicit_gather(case):
+    """The FFN reading pool rows through slot[perm[r]] gives the same bits as the FFN on the
+    batch moe_assemble copied out, and both match the oracle; queue entries with invalid
+    slots or non-local experts are rejected the same way."""
+    wdt, E, H, I, n, P = case
+    _say("gather-on-load case", case)
+    rng = np.random.default_rng(n + H)
+    act = "f32" if wdt == "f32" else "bf16"
+    wts = W.make_layer_weights(rng, E, H, I, 0.05, wdt)
+    pool_raw = rng.standard_normal((P, H)).astype(np.float32)
+    pool_np = pool_raw if act == "f32" else W.to_bf16_bits(pool_raw)
+    slot = rng.integers(0, P, n).astype(np.int32)
+    expert = rng.integers(0, E, n).astype(np.int32)
+    slot[:: 17] = P + 3          # rejected: slot out of range
+    expert[5:: 29] = E + 1       # rejected: non-local expert
+    codes = {"f32": M.MOE_F32, "bf16": M.MOE_BF16, "fp8": M.MOE_FP8_E4M3}
+    wt = weight_tensors(wts)
+    pool = dev(pool_np, act)
+    ys = []
+    for gol in (True, False):
+        st = M.ExpertStep(E, H, I, 2, codes[act], codes[wdt], n, 4, gather_on_load=gol)
+        st.load_weights(wt["wg"], wt["wu"], wt["wd"], wt.get("s_gate"), wt.get("s_up"), wt.get("s_down"))
+        st.assemble(dev(slot), dev(expert), 0, pool)
+        st.ffn(n)
+        assert sync_err(st.err) == (M.ERR_SLOT_RANGE | M.ERR_EXPERT_NONLOCAL)
+        ys.append(to_numpy_bits(st.y))
+        offsets = st.offsets.cpu().numpy()
+    nv = int(offsets[-1])
+    assert np.array_equal(ys[0][:nv], ys[1][:nv]), "gather-on-load differs from the explicit gather"
+    a = O.assemble(slot, expert, 0, E, P)
+    assert np.array_equal(offsets, a["offsets"])
+    y_ref = O.expert_ffn(O.decode(O.gather_rows(pool_np, slot, a["perm"], nv), act), a["offsets"], wts)
+    err = row_rel_err(O.decode(ys[0][:nv], act), y_ref)
+    _say(f"  row rel err {err:.3e}")
+    assert err <= TOL[wdt]
