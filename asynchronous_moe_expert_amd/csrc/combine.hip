@@ -21,6 +21,18 @@
 //      release flag; otherwise it stores the partial sum back into acc[t].
 //   3. release: one workgroup compacts the release flags into rel_list in ascending token
 //      order (16 flags per thread per pass) and clears them.
+//
+// Calls of up to kPlanMax arrivals (every decode step) take a two-kernel path instead,
+// with the same results bit for bit:
+//   1. plan: one workgroup validates the arrivals, sorts them by (token, arrival index) in
+//      LDS (bitonic), accepts top-k positions in index order per token, updates mask and
+//      generation, and writes the release list (the sorted segments are already in token
+//      order) and one segment record per touched token;
+//   2. apply: one workgroup per segment sums held partial + w_a * row_a in index order and
+//      writes the released row or the new partial sum.
+// No linked lists, no per-token flag scan over the whole state, one launch fewer.
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace moe {
@@ -282,6 +294,231 @@ __global__ __launch_bounds__(256) void state_reset_kernel(float* __restrict__ ac
   for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < nf; x += stride) rflag[x] = 0;
 }
 
+
+// ------------------------------------------------------------------ two-kernel path
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanMax = 4096;            // arrivals a single planning workgroup sorts in LDS
+constexpr int kPlanTokLimit = 1 << 20;    // states under 2^20 tokens: key = token << 12 | arrival
+constexpr uint32_t kNoTok = 0xfffffu;     // token field of a rejected arrival's key
+// workspace of the plan path (int32): [0] segment count, [4 + 4s ...] segment s =
+// (token, first list entry, accepted arrivals, flags: 1 complete, 2 held a partial sum),
+// then list[m] of (row index, weight bits): each segment's accepted arrivals in
+// arrival-index order.
+__host__ __device__ constexpr int64_t plan_list_offset(int m) { return 4 + 4 * (int64_t)m; }
+
+// exclusive prefix sum over the workgroup (kPlanThreads threads); *total gets the sum
+__device__ __forceinline__ int block_exclusive_scan(int v, int* s_wsum, int& total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int x = __shfl_up(incl, d);
+    if (lane >= d) incl += x;
+  }
+  __syncthreads();  // s_wsum is free (earlier users are done)
+  if (lane == 63) s_wsum[wv] = incl;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kPlanThreads / 64; ++w) {
+    const int c = s_wsum[w];
+    before += w < wv ? c : 0;
+    total += c;
+  }
+  return before + incl - v;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void combine_plan_kernel(
+    int m, int K, int64_t n_rows, const int32_t* __restrict__ row_idx, const int32_t* __restrict__ tok,
+    const int32_t* __restrict__ kslot, const float* __restrict__ wgt, const uint32_t* __restrict__ gen,
+    uint32_t* __restrict__ tgen, uint32_t* __restrict__ mask, int T_cap, int32_t* __restrict__ ws,
+    int32_t* __restrict__ rel_list, int32_t* __restrict__ rel_count, uint32_t* __restrict__ err) {
+  __shared__ uint32_t key[kPlanMax];
+  __shared__ int2 s_rw[kPlanMax];      // (row index, weight bits) of each arrival
+  __shared__ uint32_t s_mask[kPlanMax];  // mask of the arrival's token before the call
+  __shared__ uint8_t s_j[kPlanMax];
+  __shared__ int s_wsum[kPlanThreads / 64];
+  __shared__ unsigned s_err;
+  const int tid = threadIdx.x;
+  int N = 1;
+  while (N < m) N <<= 1;
+  if (tid == 0) s_err = 0u;
+  // 1. validation, with the token's generation and mask fetched in the same round trip;
+  //    key = token << 12 | arrival for an accepted candidate, kNoTok << 12 | arrival for a
+  //    rejected one or padding: every key is distinct and the rejected ones sort last
+  unsigned flags = 0u;
+  for (int i = tid; i < N; i += kPlanThreads) {
+    uint32_t k = (kNoTok << 12) | (uint32_t)i;
+    if (i < m) {
+      const int t = tok[i], j = kslot[i];
+      const int64_t r = row_idx[i];
+      const float w = wgt[i];
+      const uint32_t g = gen[i];
+      unsigned f = 0u;
+      if (t < 0 || t >= T_cap) f |= MOE_ERR_TOKEN_RANGE;
+      if (j < 0 || j >= K) f |= MOE_ERR_KSLOT_RANGE;
+      if (r < 0 || r >= n_rows) f |= MOE_ERR_ROW_RANGE;
+      if (!f) {
+        const uint32_t tg = tgen[t], mk = mask[t];
+        if (g != tg) f |= MOE_ERR_STALE_GEN;
+        s_mask[i] = mk;
+      }
+      if (!f) {
+        k = ((uint32_t)t << 12) | (uint32_t)i;
+        s_j[i] = (uint8_t)j;
+        s_rw[i] = make_int2((int)r, __float_as_int(w));
+      }
+      flags |= f;
+    }
+    key[i] = k;
+  }
+  __syncthreads();
+  // 2. sort key[0, N) ascending (by token, then arrival index).  Keys are distinct, so for
+  //    N <= kPlanThreads each key's position is the number of smaller keys (one pass over
+  //    LDS, two barriers); larger calls use a bitonic network.
+  if (N <= kPlanThreads) {
+    const uint32_t k = tid < N ? key[tid] : 0u;
+    int rank = 0;
+    if (tid < N) {
+      if (N >= 4) {  // N is a power of two
+        const uint4* k4 = reinterpret_cast<const uint4*>(key);
+        for (int x = 0; x < N / 4; ++x) {
+          const uint4 v = k4[x];
+          rank += (v.x < k) + (v.y < k) + (v.z < k) + (v.w < k);
+        }
+      } else {
+        for (int x = 0; x < N; ++x) rank += key[x] < k;
+      }
+    }
+    __syncthreads();
+    if (tid < N) key[rank] = k;
+  } else {
+    for (int size = 2; size <= N; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        __syncthreads();
+        for (int x = tid; x < (N >> 1); x += kPlanThreads) {
+          const int lo = 2 * x - (x & (stride - 1)), hi = lo + stride;
+          const uint32_t a = key[lo], b = key[hi];
+          if ((a > b) == ((lo & size) == 0)) {
+            key[lo] = b;
+            key[hi] = a;
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // 3.-5. segments, in rounds of kPlanThreads sorted positions (one per thread, so that
+  // every segment's state load is in flight at once): a position whose token differs from
+  // its predecessor's heads a segment; its thread accepts the segment's positions in
+  // arrival order, updates the token's state and writes the segment record; completed
+  // tokens go to the release list in segment (= ascending token) order.
+  const uint32_t full = K >= 32 ? 0xffffffffu : ((1u << K) - 1u);
+  int32_t* seg_rec = ws + 4;
+  int2* list2 = reinterpret_cast<int2*>(ws + plan_list_offset(m));
+  int n_seg = 0, n_rel = 0;
+  for (int p0 = 0; p0 < N; p0 += kPlanThreads) {
+    const int p = p0 + tid;
+    bool head = false;
+    uint32_t t = 0u;
+    if (p < N && (key[p] >> 12) != kNoTok) {
+      t = key[p] >> 12;
+      head = p == 0 || (key[p - 1] >> 12) != t;
+    }
+    uint32_t mk = head ? s_mask[key[p] & 4095u] : 0u;
+    int round_seg = 0, round_rel = 0;
+    const int seg = n_seg + block_exclusive_scan(head ? 1 : 0, s_wsum, round_seg);
+    bool complete = false;
+    if (head) {
+      const bool started = mk != 0u;
+      int na = 0;
+      for (int x = p; x < N && (key[x] >> 12) == t; ++x) {
+        const int a = (int)(key[x] & 4095u);
+        const uint32_t bit = 1u << s_j[a];
+        if (mk & bit) {
+          flags |= MOE_ERR_DUPLICATE;
+        } else {
+          mk |= bit;
+          list2[p + na++] = s_rw[a];
+        }
+      }
+      complete = mk == full;
+      reinterpret_cast<int4*>(seg_rec)[seg] = make_int4((int)t, p, na, (complete ? 1 : 0) | (started ? 2 : 0));
+      if (complete) {
+        mask[t] = 0u;
+        tgen[t] = tgen[t] + 1u;
+      } else {
+        mask[t] = mk;
+      }
+    }
+    const int o = n_rel + block_exclusive_scan(complete ? 1 : 0, s_wsum, round_rel);
+    if (complete) rel_list[o] = (int)t;
+    n_seg += round_seg;
+    n_rel += round_rel;
+  }
+  if (flags) atomicOr(&s_err, flags);
+  __syncthreads();
+  if (tid == 0) {
+    ws[0] = n_seg;
+    *rel_count = n_rel;
+    if (s_err) atomicOr(err, s_err);
+  }
+}
+
+// One workgroup per segment of the plan: held partial sum (if any) plus the accepted
+// arrivals' w_a * row_a in arrival-index order, fp32 (the same order and operations as the
+// merge kernel, so both paths give the same bits).
+template <typename TR, typename TO>
+__global__ __launch_bounds__(kCmbThreads) void combine_apply_kernel(int H, const TR* __restrict__ rows,
+                                                                    int64_t row_pitch, float* __restrict__ acc,
+                                                                    const int32_t* __restrict__ ws, int m,
+                                                                    TO* __restrict__ out, int64_t out_pitch) {
+  __shared__ float s_w[32];
+  __shared__ int64_t s_row[32];
+  const int sidx = blockIdx.x, tid = threadIdx.x;
+  if (sidx >= ws[0]) return;
+  const int4 sg = reinterpret_cast<const int4*>(ws + 4)[sidx];
+  const int t = sg.x, na = sg.z;
+  const bool complete = sg.w & 1, started = sg.w & 2;
+  if (tid < na) {
+    const int2 rw = reinterpret_cast<const int2*>(ws + plan_list_offset(m))[sg.y + tid];
+    s_row[tid] = rw.x;
+    s_w[tid] = __int_as_float(rw.y);
+  }
+  __syncthreads();
+  float* at = acc + (int64_t)t * H;
+  TO* o = out + (int64_t)t * out_pitch;
+  const int nv = H >> 3;
+  for (int v = tid; v < nv; v += kCmbThreads) {
+    float sum[8];
+    if (started) {
+      RowIO<float>::load8(at + v * 8, sum);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sum[k] = 0.f;
+    }
+    for (int q = 0; q < na; ++q) {
+      float x[8];
+      RowIO<TR>::load8(rows + s_row[q] * row_pitch + v * 8, x);
+      const float w = s_w[q];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sum[k] = fmaf(w, x[k], sum[k]);
+    }
+    if (complete) RowIO<TO>::store8(o + v * 8, sum);
+    else RowIO<float>::store8(at + v * 8, sum);
+  }
+}
+
+template <typename TR, typename TO>
+static void launch_apply(const moe_combine_args* a, hipStream_t stream) {
+  const moe_combine_state& s = a->state;
+  const int grid = std::min(a->m, s.T_cap);
+  hipLaunchKernelGGL((combine_apply_kernel<TR, TO>), dim3((unsigned)grid), dim3(kCmbThreads), 0, stream, s.H,
+                     (const TR*)a->rows, a->row_pitch, s.acc, (const int32_t*)a->workspace, a->m,
+                     (TO*)a->out, a->out_pitch);
+}
+
 template <typename TR, typename TO>
 static void launch_merge(const moe_combine_args* a, hipStream_t stream) {
   const moe_combine_state& s = a->state;
@@ -303,7 +540,10 @@ static int check_state(const moe_combine_state* s) {
 using namespace moe;
 
 extern "C" size_t moe_combine_workspace_size(int32_t m_max) {
-  return m_max <= 0 ? 16 : ((size_t)m_max * 4 + 15) / 16 * 16;
+  // the larger of the two paths' needs: next[m] (list path) and the plan records
+  if (m_max <= 0) return 16;
+  const size_t plan = (size_t)plan_list_offset(m_max) * 4 + (size_t)m_max * 8;
+  return (std::max(plan, (size_t)m_max * 4) + 15) / 16 * 16;
 }
 
 extern "C" int moe_state_reset(const moe_combine_state* st, uint32_t gen0, hipStream_t stream) {
@@ -335,8 +575,21 @@ extern "C" int moe_combine_release(const moe_combine_args* a, hipStream_t stream
         (a->rows && !aligned16(a->rows)))
       return MOE_EINVAL_ALIGN;
     if (!a->workspace || a->workspace_bytes < moe_combine_workspace_size(a->m)) return MOE_EWORKSPACE;
-    const bool rb = a->row_dtype == MOE_BF16, ob = a->out_dtype == MOE_BF16;
-    const moe_combine_state& s = a->state;
+    if (!aligned16(a->workspace)) return MOE_EINVAL_ALIGN;
+  }
+  const bool rb = a->row_dtype == MOE_BF16, ob = a->out_dtype == MOE_BF16;
+  const moe_combine_state& s = a->state;
+  if (a->m <= kPlanMax && s.T_cap < kPlanTokLimit && a->m > 0) {
+    hipLaunchKernelGGL(combine_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a->m, a->K, a->n_rows,
+                       a->row_idx, a->tok, a->kslot, a->w, a->gen, s.tgen, s.mask, s.T_cap, (int32_t*)a->workspace,
+                       a->rel_list, a->rel_count, a->err);
+    if (rb && ob) launch_apply<uint16_t, uint16_t>(a, stream);
+    else if (rb) launch_apply<uint16_t, float>(a, stream);
+    else if (ob) launch_apply<float, uint16_t>(a, stream);
+    else launch_apply<float, float>(a, stream);
+    return launch_status();
+  }
+  if (a->m > 0) {
     hipLaunchKernelGGL(combine_link_kernel, dim3((unsigned)((a->m + 255) / 256)), dim3(256), 0, stream, a->m, a->K,
                        a->n_rows, a->row_idx, a->tok, a->kslot, a->gen, s.tgen, s.T_cap, s.head,
                        (int32_t*)a->workspace, a->err);

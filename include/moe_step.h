@@ -229,7 +229,10 @@ int moe_state_reset(const moe_combine_state* st, uint32_t gen0, hipStream_t stre
  * Tokens still missing results keep their partial sums.
  * Limits: 1 <= K <= 32, 0 <= m <= 2^24, H % 8 == 0, rows/out dtypes F32 or BF16,
  * rel_list holds at least min(m, T_cap) entries; the workspace (device memory, 16-byte
- * aligned) holds moe_combine_workspace_size(m) bytes. */
+ * aligned) holds moe_combine_workspace_size(m) bytes (16 + 24 m, rounded up to 16).
+ * Calls of at most 4096 arrivals on a state of fewer than 2^20 tokens are planned by
+ * one workgroup (sort by token and arrival index, then one workgroup per token); others
+ * link per-token arrival lists.  Both give the same bits. */
 typedef struct moe_combine_args {
   int32_t m;               /* arrivals */
   int32_t K;               /* results per token (top-k) */

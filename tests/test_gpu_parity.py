@@ -432,3 +432,58 @@ def test_gather_on_load_matches_explicit_gather(case):
     err = row_rel_err(O.decode(ys[0][:nv], act), y_ref)
     _say(f"  row rel err {err:.3e}")
     assert err <= TOL[wdt]
+
+
+def test_combine_plan_and_list_paths_agree():
+    """Calls of up to 4096 arrivals on states under 2^20 tokens take the two-kernel plan
+    path; other calls take the linked-list path.  The same calls on a small state (plan
+    path) and on a 2^20-token state (list path) give the same bits: error words, release
+    lists, released rows, partial sums and token state, including retries, stale and
+    out-of-range arrivals and one token with more arrivals than a merge pass takes."""
+    _say("combine plan vs list path")
+    rng = np.random.default_rng(21)
+    K, H, T_small = 4, 64, 300
+    rows_np = rng.standard_normal((2000, H)).astype(np.float32)
+    rows_t = dev(rows_np)
+    sts = [M.ExpertStep(1, H, 64, K, M.MOE_F32, M.MOE_F32, 1, T) for T in (T_small, 1 << 20)]
+    calls = []
+    for c in range(3):
+        m = int(rng.integers(200, 900))
+        tok = rng.integers(0, 250, m)
+        ks = rng.integers(0, K, m)
+        gen = np.where(rng.random(m) < 0.03, 5, 0)              # stale
+        row = rng.integers(0, 2000, m)
+        row[rng.random(m) < 0.02] = 2500                          # row out of range
+        ks[rng.random(m) < 0.02] = K + 2                          # position out of range
+        if c == 1:                                                # a long chain for token 7
+            tok[:150], ks[:150] = 7, np.arange(150) % K
+        calls.append((row, tok, ks, rng.random(m).astype(np.float32), gen))
+    res = []
+    for st in sts:
+        out = []
+        for (row, tok, ks, w, gen) in calls:
+            # generations advance as tokens release; re-tag the non-stale arrivals to the
+            # token's current generation so that most arrivals are live
+            tg = st.state.tgen.cpu().numpy().view(np.uint32)
+            g = np.where(gen == 0, tg[tok], tg[tok] + 5).astype(np.uint32)
+            st.err.zero_()
+            st.combine(rows_t, dev(row.astype(np.int32)), dev(tok.astype(np.int32)), dev(ks.astype(np.int32)),
+                       dev(w), dev(g))
+            e = sync_err(st.err)
+            n = int(st.rel_count.item())
+            rel = st.rel_list[:n].cpu().numpy().copy()
+            o = st.out[torch.as_tensor(rel, device="cuda").long()].cpu().numpy().copy() if n else np.zeros((0, H))
+            out.append((e, rel, o))
+        acc = st.state.acc[:T_small].cpu().numpy()
+        mask = st.state.mask[:T_small].cpu().numpy()
+        tgen = st.state.tgen[:T_small].cpu().numpy()
+        res.append((out, acc, mask, tgen))
+    (oa, acc_a, mask_a, tg_a), (ob, acc_b, mask_b, tg_b) = res
+    for (ea, ra, xa), (eb, rb, xb) in zip(oa, ob):
+        assert ea == eb and ea != 0
+        assert np.array_equal(ra, rb) and len(ra) > 0
+        assert np.array_equal(xa.view(np.uint32), xb.view(np.uint32))
+    assert np.array_equal(mask_a, mask_b) and np.array_equal(tg_a, tg_b)
+    held = mask_a != 0
+    assert held.any()
+    assert np.array_equal(acc_a[held].view(np.uint32), acc_b[held].view(np.uint32))

@@ -59,7 +59,8 @@ def test_workspace_size(lib):
     assert M.moe_ffn_workspace_size(64, 8, 64, 128, M.MOE_F32) == 64 * 128 * 4
     assert M.moe_ffn_workspace_size(3, 1, 64, 64, M.MOE_BF16) == 512  # rounded up to 256 B
     assert M.moe_ffn_workspace_size(1, 1, 64, 64, 7) == 0
-    assert M.moe_combine_workspace_size(256) == 1024 and M.moe_combine_workspace_size(3) == 16
+    # plan path: a 16-byte header, a 16-byte record and an 8-byte list entry per arrival
+    assert M.moe_combine_workspace_size(256) == 6160 and M.moe_combine_workspace_size(3) == 96
 
 
 def test_host_validation_rejects_bad_arguments(lib):
