@@ -57,8 +57,8 @@ class CombineArgs(C.Structure):
 
 _STRUCTS = [AssembleArgs, PackArgs, FfnArgs, StateC, CombineArgs]
 EXPORTS = ["moe_assemble", "moe_pack_ffn_weights", "moe_ffn_workspace_size", "moe_expert_ffn_grouped",
-           "moe_state_reset", "moe_combine_release", "moe_combine_workspace_size", "moe_strerror", "moe_version",
-           "moe_struct_size"]
+           "moe_state_reset", "moe_combine_release", "moe_combine_plan", "moe_combine_apply",
+           "moe_combine_workspace_size", "moe_strerror", "moe_version", "moe_struct_size"]
 
 
 class MoeError(RuntimeError):
@@ -82,6 +82,8 @@ def load(path: str = LIB_PATH) -> C.CDLL:
                        ("moe_expert_ffn_grouped", [C.POINTER(FfnArgs), _p]),
                        ("moe_state_reset", [C.POINTER(StateC), C.c_uint32, _p]),
                        ("moe_combine_release", [C.POINTER(CombineArgs), _p]),
+                       ("moe_combine_plan", [C.POINTER(CombineArgs), _p]),
+                       ("moe_combine_apply", [C.POINTER(CombineArgs), _p]),
                        ("moe_version", []), ("moe_strerror", [C.c_int])]:
         f = getattr(lib, name)
         f.argtypes = args
@@ -198,11 +200,19 @@ def moe_combine_workspace_size(m_max: int) -> int:
     return load().moe_combine_workspace_size(m_max)
 
 
+def _combine_args(rows, row_idx, tok, kslot, w, gen, K, state, out, rel_list, rel_count, err, workspace, m, n_rows):
+    return CombineArgs(int(tok.numel() if m is None else m), K, _ptr(rows), dtype_code(rows), rows.stride(0),
+                       rows.shape[0] if n_rows is None else n_rows, _ptr(row_idx), _ptr(tok), _ptr(kslot), _ptr(w),
+                       _ptr(gen), state.c(), _ptr(out), dtype_code(out), out.stride(0), _ptr(rel_list),
+                       _ptr(rel_count), _ptr(err), _ptr(workspace), workspace.numel() * workspace.element_size())
+
+
 def moe_combine_release(rows, row_idx, tok, kslot, w, gen, K: int, state: CombineState, out, rel_list, rel_count,
-                        err, workspace, m: int | None = None, n_rows: int | None = None, stream=None) -> None:
-    """rows: [n_rows][pitch] f32/bf16 result rows; out: [T_cap][pitch] f32/bf16."""
-    a = CombineArgs(int(tok.numel() if m is None else m), K, _ptr(rows), dtype_code(rows), rows.stride(0),
-                    rows.shape[0] if n_rows is None else n_rows, _ptr(row_idx), _ptr(tok), _ptr(kslot), _ptr(w),
-                    _ptr(gen), state.c(), _ptr(out), dtype_code(out), out.stride(0), _ptr(rel_list),
-                    _ptr(rel_count), _ptr(err), _ptr(workspace), workspace.numel() * workspace.element_size())
-    _check(load().moe_combine_release(C.byref(a), _stream(stream)), "moe_combine_release")
+                        err, workspace, m: int | None = None, n_rows: int | None = None, stream=None,
+                        part: str = "release") -> None:
+    """rows: [n_rows][pitch] f32/bf16 result rows; out: [T_cap][pitch] f32/bf16.
+    part = "plan" / "apply" calls moe_combine_plan / moe_combine_apply instead."""
+    a = _combine_args(rows, row_idx, tok, kslot, w, gen, K, state, out, rel_list, rel_count, err, workspace, m,
+                      n_rows)
+    fn = {"release": "moe_combine_release", "plan": "moe_combine_plan", "apply": "moe_combine_apply"}[part]
+    _check(getattr(load(), fn)(C.byref(a), _stream(stream)), fn)

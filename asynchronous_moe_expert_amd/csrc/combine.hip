@@ -22,10 +22,10 @@
 //   3. release: one workgroup compacts the release flags into rel_list in ascending token
 //      order (16 flags per thread per pass) and clears them.
 //
-// Calls of up to kPlanMax arrivals (every decode step) take a two-kernel path instead,
+// Calls of up to kPlanMax (1024) arrivals (every decode step) take a two-kernel path instead,
 // with the same results bit for bit:
 //   1. plan: one workgroup validates the arrivals, sorts them by (token, arrival index) in
-//      LDS (bitonic), accepts top-k positions in index order per token, updates mask and
+//      LDS (rank sort), accepts top-k positions in index order per token, updates mask and
 //      generation, and writes the release list (the sorted segments are already in token
 //      order) and one segment record per touched token;
 //   2. apply: one workgroup per segment sums held partial + w_a * row_a in index order and
@@ -297,7 +297,10 @@ __global__ __launch_bounds__(256) void state_reset_kernel(float* __restrict__ ac
 
 // ------------------------------------------------------------------ two-kernel path
 constexpr int kPlanThreads = 1024;
-constexpr int kPlanMax = 4096;            // arrivals a single planning workgroup sorts in LDS
+// Arrivals a single planning workgroup takes: up to 1024 the one-pass rank sort applies;
+// above that a bitonic network over 2048-4096 keys costs more (30-50 us on prefill waves)
+// than the linked-list path it replaces.
+constexpr int kPlanMax = 1024;
 constexpr int kPlanTokLimit = 1 << 20;    // states under 2^20 tokens: key = token << 12 | arrival
 constexpr uint32_t kNoTok = 0xfffffu;     // token field of a rejected arrival's key
 // workspace of the plan path (int32): [0] segment count, [4 + 4s ...] segment s =
@@ -374,10 +377,10 @@ __global__ __launch_bounds__(kPlanThreads) void combine_plan_kernel(
     key[i] = k;
   }
   __syncthreads();
-  // 2. sort key[0, N) ascending (by token, then arrival index).  Keys are distinct, so for
-  //    N <= kPlanThreads each key's position is the number of smaller keys (one pass over
-  //    LDS, two barriers); larger calls use a bitonic network.
-  if (N <= kPlanThreads) {
+  // 2. sort key[0, N) ascending (by token, then arrival index).  Keys are distinct, so each
+  //    key's place is the number of smaller keys: one pass over LDS per thread.
+  static_assert(kPlanMax <= kPlanThreads, "one key per thread");
+  {
     const uint32_t k = tid < N ? key[tid] : 0u;
     int rank = 0;
     if (tid < N) {
@@ -393,20 +396,6 @@ __global__ __launch_bounds__(kPlanThreads) void combine_plan_kernel(
     }
     __syncthreads();
     if (tid < N) key[rank] = k;
-  } else {
-    for (int size = 2; size <= N; size <<= 1) {
-      for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        __syncthreads();
-        for (int x = tid; x < (N >> 1); x += kPlanThreads) {
-          const int lo = 2 * x - (x & (stride - 1)), hi = lo + stride;
-          const uint32_t a = key[lo], b = key[hi];
-          if ((a > b) == ((lo & size) == 0)) {
-            key[lo] = b;
-            key[hi] = a;
-          }
-        }
-      }
-    }
   }
   __syncthreads();
   // 3.-5. segments, in rounds of kPlanThreads sorted positions (one per thread, so that
@@ -558,7 +547,8 @@ extern "C" int moe_state_reset(const moe_combine_state* st, uint32_t gen0, hipSt
   return launch_status();
 }
 
-extern "C" int moe_combine_release(const moe_combine_args* a, hipStream_t stream) {
+// Argument checks shared by the combine entry points (host side, before any launch).
+static int check_combine(const moe_combine_args* a) {
   if (!a) return MOE_EINVAL_NULL;
   const int rc = check_state(&a->state);
   if (rc != MOE_OK) return rc;
@@ -577,12 +567,34 @@ extern "C" int moe_combine_release(const moe_combine_args* a, hipStream_t stream
     if (!a->workspace || a->workspace_bytes < moe_combine_workspace_size(a->m)) return MOE_EWORKSPACE;
     if (!aligned16(a->workspace)) return MOE_EINVAL_ALIGN;
   }
-  const bool rb = a->row_dtype == MOE_BF16, ob = a->out_dtype == MOE_BF16;
+  return MOE_OK;
+}
+
+static bool plan_path(const moe_combine_args* a) {
+  return a->m > 0 && a->m <= kPlanMax && a->state.T_cap < kPlanTokLimit;
+}
+
+extern "C" int moe_combine_plan(const moe_combine_args* a, hipStream_t stream) {
+  const int rc = check_combine(a);
+  if (rc != MOE_OK) return rc;
   const moe_combine_state& s = a->state;
-  if (a->m <= kPlanMax && s.T_cap < kPlanTokLimit && a->m > 0) {
+  if (plan_path(a)) {
     hipLaunchKernelGGL(combine_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a->m, a->K, a->n_rows,
                        a->row_idx, a->tok, a->kslot, a->w, a->gen, s.tgen, s.mask, s.T_cap, (int32_t*)a->workspace,
                        a->rel_list, a->rel_count, a->err);
+  } else if (a->m > 0) {
+    hipLaunchKernelGGL(combine_link_kernel, dim3((unsigned)((a->m + 255) / 256)), dim3(256), 0, stream, a->m, a->K,
+                       a->n_rows, a->row_idx, a->tok, a->kslot, a->gen, s.tgen, s.T_cap, s.head,
+                       (int32_t*)a->workspace, a->err);
+  }
+  return launch_status();
+}
+
+extern "C" int moe_combine_apply(const moe_combine_args* a, hipStream_t stream) {
+  const int rc = check_combine(a);
+  if (rc != MOE_OK) return rc;
+  const bool rb = a->row_dtype == MOE_BF16, ob = a->out_dtype == MOE_BF16;
+  if (plan_path(a)) {
     if (rb && ob) launch_apply<uint16_t, uint16_t>(a, stream);
     else if (rb) launch_apply<uint16_t, float>(a, stream);
     else if (ob) launch_apply<float, uint16_t>(a, stream);
@@ -590,9 +602,6 @@ extern "C" int moe_combine_release(const moe_combine_args* a, hipStream_t stream
     return launch_status();
   }
   if (a->m > 0) {
-    hipLaunchKernelGGL(combine_link_kernel, dim3((unsigned)((a->m + 255) / 256)), dim3(256), 0, stream, a->m, a->K,
-                       a->n_rows, a->row_idx, a->tok, a->kslot, a->gen, s.tgen, s.T_cap, s.head,
-                       (int32_t*)a->workspace, a->err);
     if (rb && ob) launch_merge<uint16_t, uint16_t>(a, stream);
     else if (rb) launch_merge<uint16_t, float>(a, stream);
     else if (ob) launch_merge<float, uint16_t>(a, stream);
@@ -601,4 +610,10 @@ extern "C" int moe_combine_release(const moe_combine_args* a, hipStream_t stream
   hipLaunchKernelGGL(combine_release_kernel, dim3(1), dim3(kRelThreads), 0, stream, a->state.T_cap, a->state.rflag,
                      a->rel_list, a->rel_count);
   return launch_status();
+}
+
+extern "C" int moe_combine_release(const moe_combine_args* a, hipStream_t stream) {
+  const int rc = moe_combine_plan(a, stream);
+  if (rc != MOE_OK) return rc;
+  return moe_combine_apply(a, stream);
 }

@@ -8,6 +8,13 @@ queue entry i, whose result row is pos[i] (the batch row moe_assemble gave it).
 With gather_on_load (the default) moe_assemble only builds the index (perm, pos, counts,
 offsets) and the FFN reads each batch row straight from the token pool through
 slot[perm[r]]; the contiguous batch is never written out.
+
+With overlap, run() puts the first half of the combine (moe_combine_plan: it reads only
+the arrival metadata and the token state) on a side stream, where it runs while the FFN
+streams the expert weights; moe_combine_apply then waits for it on the main stream.  The
+side stream has the default priority.  Off by default: on the decode step the two
+cross-stream event waits cost more than the ~8 us plan kernel they hide (97.5 us per step
+in order, 101 us overlapped).
 """
 from __future__ import annotations
 
@@ -20,7 +27,7 @@ _TORCH = {N.MOE_F32: torch.float32, N.MOE_BF16: torch.bfloat16, N.MOE_FP8_E4M3: 
 
 class ExpertStep:
     def __init__(self, E_loc: int, H: int, I: int, K: int, act_dtype: int, w_dtype: int, n_max: int, T_cap: int,
-                 device="cuda", gather_on_load: bool = True):
+                 device="cuda", gather_on_load: bool = True, overlap: bool = False):
         self.E_loc, self.H, self.I, self.K = E_loc, H, I, K
         self.act_dtype, self.w_dtype, self.n_max, self.T_cap = act_dtype, w_dtype, n_max, T_cap
         dev = torch.device(device)
@@ -44,6 +51,9 @@ class ExpertStep:
         self.w_gu = self.w_d = None
         self.gather_on_load = gather_on_load
         self._gather = None  # (perm, slot, pool) of the last assemble when gathering on load
+        self.side = torch.cuda.Stream(device=dev) if overlap else None
+        self._ev_asm = torch.cuda.Event() if overlap else None
+        self._ev_plan = torch.cuda.Event() if overlap else None
         self.s_gate = self.s_up = self.s_down = None
         N.moe_state_reset(self.state, 0)
 
@@ -67,7 +77,7 @@ class ExpertStep:
                                  ev_mid=ev_mid, stream=stream, gather=self._gather)
 
     def combine(self, rows, row_idx, tok, kslot, w, gen, m: int | None = None, n_rows: int | None = None,
-                stream=None) -> None:
+                stream=None, part: str = "release") -> None:
         m = int(tok.numel() if m is None else m)
         if m > self.cmb_ws_m:  # plumbing: grow the caller-owned scratch (outside any timed loop)
             self.cmb_ws_m = m
@@ -75,12 +85,24 @@ class ExpertStep:
         if m > self.rel_list.numel():
             self.rel_list = torch.empty(m, dtype=torch.int32, device=self.rel_list.device)
         N.moe_combine_release(rows, row_idx, tok, kslot, w, gen, self.K, self.state, self.out, self.rel_list,
-                              self.rel_count, self.err, self.cmb_ws, m=m, n_rows=n_rows, stream=stream)
+                              self.rel_count, self.err, self.cmb_ws, m=m, n_rows=n_rows, stream=stream, part=part)
 
     def run(self, slot, expert, expert_base: int, pool, tok, kslot, w, gen, n: int | None = None,
             ev_mid: int | None = None, stream=None) -> None:
         """The whole step on one batch: assemble, FFN, combine of the local results."""
         n = int(slot.numel() if n is None else n)
         self.assemble(slot, expert, expert_base, pool, n=n, stream=stream)
-        self.ffn(n, ev_mid=ev_mid, stream=stream)
-        self.combine(self.y, self.pos, tok, kslot, w, gen, m=n, n_rows=n, stream=stream)
+        if self.side is None:
+            self.ffn(n, ev_mid=ev_mid, stream=stream)
+            self.combine(self.y, self.pos, tok, kslot, w, gen, m=n, n_rows=n, stream=stream)
+            return
+        main = torch.cuda.current_stream() if stream is None else stream
+        self._ev_asm.record(main)
+        self.side.wait_event(self._ev_asm)
+        for t in (tok, kslot, w, gen):
+            t.record_stream(self.side)  # the allocator keeps them until the side stream is done
+        self.combine(self.y, self.pos, tok, kslot, w, gen, m=n, n_rows=n, stream=self.side, part="plan")
+        self._ev_plan.record(self.side)
+        self.ffn(n, ev_mid=ev_mid, stream=main)
+        main.wait_event(self._ev_plan)
+        self.combine(self.y, self.pos, tok, kslot, w, gen, m=n, n_rows=n, stream=main, part="apply")

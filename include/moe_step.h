@@ -230,7 +230,7 @@ int moe_state_reset(const moe_combine_state* st, uint32_t gen0, hipStream_t stre
  * Limits: 1 <= K <= 32, 0 <= m <= 2^24, H % 8 == 0, rows/out dtypes F32 or BF16,
  * rel_list holds at least min(m, T_cap) entries; the workspace (device memory, 16-byte
  * aligned) holds moe_combine_workspace_size(m) bytes (16 + 24 m, rounded up to 16).
- * Calls of at most 4096 arrivals on a state of fewer than 2^20 tokens are planned by
+ * Calls of at most 1024 arrivals on a state of fewer than 2^20 tokens are planned by
  * one workgroup (sort by token and arrival index, then one workgroup per token); others
  * link per-token arrival lists.  Both give the same bits. */
 typedef struct moe_combine_args {
@@ -259,6 +259,19 @@ typedef struct moe_combine_args {
 size_t moe_combine_workspace_size(int32_t m_max);
 
 int moe_combine_release(const moe_combine_args* args, hipStream_t stream);
+
+/* moe_combine_release in two halves, for a caller that overlaps the first with other work
+ * on another stream (the arrivals of an expert step are known before its FFN runs):
+ *   moe_combine_plan   reads the arrival metadata and the token state only (validation,
+ *                      per-token acceptance, state update, release list);
+ *   moe_combine_apply  reads the result rows and writes the combined rows.
+ * Call both with the same arguments, apply ordered after plan (same stream, or an event),
+ * and change neither the arguments, the state nor the workspace in between; rel_list,
+ * rel_count and err are final only after apply.  moe_combine_release(args, s) is
+ * moe_combine_plan(args, s) followed by moe_combine_apply(args, s).  Both validate the
+ * arguments as moe_combine_release does. */
+int moe_combine_plan(const moe_combine_args* args, hipStream_t stream);
+int moe_combine_apply(const moe_combine_args* args, hipStream_t stream);
 
 /* ---------------------------------------------------------------------- helpers -- */
 const char* moe_strerror(int status);

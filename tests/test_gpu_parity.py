@@ -241,12 +241,12 @@ def test_combine_k_extremes(K):
 
 
 # --------------------------------------------------------------------- whole configs
-def _run_config_step(b, wts, act_code, w_code, check_rows=True, sample_rows=None, T_cap=None):
+def _run_config_step(b, wts, act_code, w_code, check_rows=True, sample_rows=None, T_cap=None, overlap=False):
     """Deliver the remote results (one call), then run the step on the local pairs.
     Returns the GPU step and the oracle pieces for comparison."""
     d = batch_tensors(b)
     wt = weight_tensors(wts)
-    st = M.ExpertStep(b.E_loc, b.H, wts.I, b.K, act_code, w_code, b.n, T_cap or b.T)
+    st = M.ExpertStep(b.E_loc, b.H, wts.I, b.K, act_code, w_code, b.n, T_cap or b.T, overlap=overlap)
     st.load_weights(wt["wg"], wt["wu"], wt["wd"], wt.get("s_gate"), wt.get("s_up"), wt.get("s_down"))
     if "r_rows" in d:
         st.combine(d["r_rows"], d["r_idx"], d["r_tok"], d["r_kslot"], d["r_w"], d["r_gen"])
@@ -304,6 +304,15 @@ def test_c1_decode_full_step():
     _say("C1 decode bf16 step")
     b, wts = W.c1_decode()
     st, e = _run_config_step(b, wts, M.MOE_BF16, M.MOE_BF16)
+    a, y = _oracle_step(b, wts)
+    _check_step(st, e, b, wts, a, y, TOL["bf16"])
+
+
+def test_c1_decode_overlapped_step():
+    """The same step with the combine's plan half on a side stream during the FFN."""
+    _say("C1 decode bf16 step, plan overlapped with the FFN")
+    b, wts = W.c1_decode()
+    st, e = _run_config_step(b, wts, M.MOE_BF16, M.MOE_BF16, overlap=True)
     a, y = _oracle_step(b, wts)
     _check_step(st, e, b, wts, a, y, TOL["bf16"])
 
@@ -435,7 +444,7 @@ def test_gather_on_load_matches_explicit_gather(case):
 
 
 def test_combine_plan_and_list_paths_agree():
-    """Calls of up to 4096 arrivals on states under 2^20 tokens take the two-kernel plan
+    """Calls of up to 1024 arrivals on states under 2^20 tokens take the two-kernel plan
     path; other calls take the linked-list path.  The same calls on a small state (plan
     path) and on a 2^20-token state (list path) give the same bits: error words, release
     lists, released rows, partial sums and token state, including retries, stale and
