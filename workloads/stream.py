@@ -16,10 +16,17 @@ stragglers per source message, §2 and §8):
     as one message per (source, attention pick), after ceil(lognormal(0, 1)) time units;
     the result rows are rows of a seeded N(0,1) bank, taken round-robin.
   * Time advances by one unit per expert batch.  Each step first delivers the messages
-    that are due, then picks the queue with the most entries among A_0, X_0, A_1, X_1, ...
-    (most tokens first; ties go to the earliest queue in that order).  An expert pick
-    takes up to `cap` pairs in FIFO order.  If every queue is empty, time jumps to the next
-    message.
+    that are due, then picks a non-empty queue of the chain A_0, X_0, A_1, X_1, ... by the
+    configured policy (ties go to the earliest queue of the chain):
+      - "mtfs"   most tokens first: the deepest queue ([SEP] §4);
+      - "flfs"   first layer first: the earliest non-empty queue of the chain ([SEP] §4);
+      - "defrag" the defragmenting score of [SEP] §4,
+                 S(s) = Q(s) + sum_{j=1..W} delta^j [Q(s_j) + H(s_j)],
+                 with Q the queue depth, s_j the queue j places after s on the chain
+                 (places past the last layer do not exist unless `wrap`), H(q) the tokens
+                 drained from q over the last `hist` scheduling steps.
+    An expert pick takes up to `cap` pairs in FIFO order.  If every queue is empty, time
+    jumps to the next message.
   * A released token moves from layer l to A_{l+1} (after the last layer, to A_0); its
     generation, like the combine state's, advances by one per release.
 """
@@ -49,6 +56,11 @@ class StreamConfig:
     row_bank: int = 16384   # remote-result rows
     x_bank: int = 8192      # attention-output rows
     seed: int = BASE_SEED + 3
+    policy: str = "mtfs"    # "mtfs", "flfs" or "defrag"
+    window: int = 2         # defrag lookahead W
+    delta: float = 0.5      # defrag decay
+    hist: int = 4           # defrag history: scheduling steps summed into H
+    wrap: bool = False      # defrag lookahead wraps from the last layer to the first
 
 
 @dataclass
@@ -97,6 +109,9 @@ class StreamSim:
         self.msgs: list = []
         self.seq = 0
         self.bank_ptr = 0
+        self.recent: deque = deque()                 # (chain position, tokens drained) per pick
+        self.entered = np.zeros(c.tokens, np.int64)  # step at which a token entered its layer
+        self.latency: list = []                      # steps from entering a layer to release
 
     # --------------------------------------------------------------------- banks
     def banks(self):
@@ -143,6 +158,7 @@ class StreamSim:
             heapq.heappush(self.msgs, (msg.due, msg.seq, msg))
             self.seq += 1
         self.log.append(("A", l, len(toks)))
+        self.note_drain("A", l, len(toks))
         return toks
 
     def due(self) -> list:
@@ -151,14 +167,49 @@ class StreamSim:
             out.append(heapq.heappop(self.msgs)[2])
         return out
 
-    def pick(self):
-        """Most entries first over A_0, X_0, A_1, X_1, ...; None if all are empty."""
-        best, arg = 0, None
+    def chain(self):
+        """Queues in chain order A_0, X_0, A_1, X_1, ... as ((kind, layer), queue)."""
         for l in range(self.cfg.layers):
-            for kind, q in (("A", self.A[l]), ("X", self.X[l])):
-                if len(q) > best:
-                    best, arg = len(q), (kind, l)
+            yield ("A", l), self.A[l]
+            yield ("X", l), self.X[l]
+
+    def drained(self) -> np.ndarray:
+        """H per chain position: tokens drained over the last `hist` scheduling steps."""
+        h = np.zeros(2 * self.cfg.layers, np.int64)
+        for pos, cnt in self.recent:
+            h[pos] += cnt
+        return h
+
+    def pick(self):
+        """The configured policy's queue over A_0, X_0, A_1, X_1, ...; None if all are empty."""
+        c = self.cfg
+        if c.policy == "flfs":
+            for key, q in self.chain():
+                if q:
+                    return key
+            return None
+        if c.policy == "defrag":
+            depth = [len(q) for _, q in self.chain()]
+            h = self.drained()
+            best, arg = None, None
+            for pos, (key, q) in enumerate(self.chain()):
+                if not q:
+                    continue
+                sc = defrag_score(depth, h, pos, c.window, c.delta, c.wrap)
+                if best is None or sc > best:
+                    best, arg = sc, key
+            return arg
+        best, arg = 0, None
+        for key, q in self.chain():
+            if len(q) > best:
+                best, arg = len(q), key
         return arg
+
+    def note_drain(self, kind: str, l: int, count: int) -> None:
+        """Records one scheduling step's drain for the defrag history."""
+        self.recent.append((2 * l + (kind == "X"), count))
+        while len(self.recent) > self.cfg.hist:
+            self.recent.popleft()
 
     def take(self, l: int) -> ExpertBatch:
         q = self.X[l]
@@ -167,11 +218,14 @@ class StreamSim:
                         np.array([x[0] for x in items], np.int32), np.array([x[1] for x in items], np.int32),
                         np.array([x[3] for x in items], np.float32), np.array([x[4] for x in items], np.uint32))
         self.log.append(("X", l, b.n))
+        self.note_drain("X", l, b.n)
         return b
 
     def release(self, toks) -> None:
         """Released tokens (ascending) move to the next layer's attention queue."""
         for t in np.asarray(toks, np.int64):
+            self.latency.append(self.tau - self.entered[t])
+            self.entered[t] = self.tau
             self.layer[t] += 1
             self.gen[t] += 1
             if self.layer[t] == self.cfg.layers:
@@ -184,6 +238,22 @@ class StreamSim:
             return False
         self.tau = max(self.tau, self.msgs[0][0])
         return True
+
+
+def defrag_score(depth, drained, pos: int, window: int, delta: float, wrap: bool = False) -> float:
+    """S(s) of the defragmenting scheduler ([SEP] §4) for the queue at chain position
+    `pos`: depth[pos] + sum_{j=1..window} delta^j (depth[pos+j] + drained[pos+j]); chain
+    positions past the end are absent unless `wrap`."""
+    n = len(depth)
+    score = float(depth[pos])
+    for j in range(1, window + 1):
+        q = pos + j
+        if q >= n:
+            if not wrap:
+                break
+            q %= n
+        score += delta ** j * (depth[q] + drained[q])
+    return score
 
 
 def merge_messages(msgs: list) -> Message:
