@@ -80,3 +80,17 @@ def test_fp8_weight_quantisation_round_trip():
     assert lw.sg.shape == (2, 32) and lw.sd.shape == (2, 64)
     assert np.all((codes & 0x7F) != 0x7F)  # never NaN
     assert np.any((codes & 0x7F) == 0x7E)  # each row's amax maps to 448
+
+
+def test_merged_prefill_waves_keep_every_pair_and_remote_row():
+    s = W.c4_prefill_setup(with_weights=False)
+    a = [W.c4_wave(s, w) for w in (2, 3)]
+    m = W.merge_batches(a)
+    assert m.n == a[0].n + a[1].n and m.remote.m == a[0].remote.m + a[1].remote.m
+    assert np.array_equal(m.tok, np.concatenate([a[0].tok, a[1].tok]))
+    r0, r1, r = a[0].remote, a[1].remote, m.remote
+    for k in (0, r0.m - 1, r0.m, r.m - 1):
+        src, i = (r0, k) if k < r0.m else (r1, k - r0.m)
+        assert np.array_equal(r.rows[r.row_idx[k]], src.rows[src.row_idx[i]])
+        assert (r.tok[k], r.kslot[k], r.w[k]) == (src.tok[i], src.kslot[i], src.w[i])
+    assert W.merge_batches([a[0]]) is a[0]

@@ -23,6 +23,7 @@ from .gen import (  # noqa: F401
     c4_prefill_setup,
     c4_wave,
     make_layer_weights,
+    merge_batches,
     to_bf16_bits,
     to_e4m3_codes,
     zipf_probs,

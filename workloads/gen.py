@@ -325,3 +325,21 @@ def c4_wave(setup: C4Setup, wave: int, with_remote: bool = True) -> Batch:
     return Batch("bf16", c["H"], c["K"], c["E_loc"], 0, c["P"], setup.pool, toks.copy(),
                  setup.expert[toks].copy(), toks.copy(), setup.jl[toks].copy(),
                  setup.w[toks, setup.jl[toks]].astype(np.float32), np.zeros(n, np.uint32), c["P"], rem)
+
+
+def merge_batches(batches: list) -> Batch:
+    """Ready batches over one pool, concatenated in order into one batch (their queues back
+    to back, remote results renumbered into one row block).  A single batch is returned as is."""
+    if len(batches) == 1:
+        return batches[0]
+    b0 = batches[0]
+    cat = lambda f: np.concatenate([getattr(b, f) for b in batches])  # noqa: E731
+    rem = None
+    if all(b.remote is not None for b in batches):
+        offs = np.cumsum([0] + [b.remote.rows.shape[0] for b in batches[:-1]])
+        rcat = lambda f: np.concatenate([getattr(b.remote, f) for b in batches])  # noqa: E731
+        rem = Arrivals(b0.remote.dtype, rcat("rows"),
+                       np.concatenate([b.remote.row_idx + o for b, o in zip(batches, offs)]).astype(np.int32),
+                       rcat("tok"), rcat("kslot"), rcat("w"), rcat("gen"))
+    return Batch(b0.act, b0.H, b0.K, b0.E_loc, b0.expert_base, b0.P, b0.pool, cat("slot"), cat("expert"),
+                 cat("tok"), cat("kslot"), cat("w"), cat("gen"), b0.T, rem)
