@@ -29,4 +29,4 @@ from ._native import (  # noqa: F401
     moe_strerror,
     moe_version,
 )
-from .step import ExpertStep  # noqa: F401
+from .step import ExpertStep, SharedExpert  # noqa: F401

@@ -106,3 +106,37 @@ class ExpertStep:
         self.ffn(n, ev_mid=ev_mid, stream=main)
         main.wait_event(self._ev_plan)
         self.combine(self.y, self.pos, tok, kslot, w, gen, m=n, n_rows=n, stream=main, part="apply")
+
+
+class SharedExpert:
+    """A shared expert at the home rank ([SEP] section 3: models with a shared expert run
+    it locally on the home rank after attention, before the routed experts' results come
+    back).  Every home token goes through the same dense SwiGLU; its result joins the
+    token's combine as one more position, `kslot` (K of the routed top-K), with weight 1,
+    so the released row is y = sum_j w_j E_j(x) + E_shared(x) and a token is released only
+    once its routed results and its shared result have all arrived.
+
+    The three calls are the step's own: moe_assemble (one local expert), the grouped FFN
+    (a single group) and moe_combine_release into the routed step's combine state."""
+
+    def __init__(self, H: int, I: int, act_dtype: int, w_dtype: int, n_max: int, device="cuda"):
+        self.step = ExpertStep(1, H, I, 1, act_dtype, w_dtype, n_max, 1, device=device)
+        self.n_max = n_max
+        dev = torch.device(device)
+        self._zero = torch.zeros(max(n_max, 1), dtype=torch.int32, device=dev)
+        self._one = torch.ones(max(n_max, 1), dtype=torch.float32, device=dev)
+        self._kslot = torch.empty(max(n_max, 1), dtype=torch.int32, device=dev)
+
+    def load_weights(self, wg, wu, wd, s_gate=None, s_up=None, s_down=None, stream=None) -> None:
+        """wg, wu: [1][I][H], wd: [1][H][I] (one expert)."""
+        self.step.load_weights(wg, wu, wd, s_gate, s_up, s_down, stream=stream)
+
+    def run(self, owner: ExpertStep, slot, pool, tok, gen, kslot: int, n: int | None = None, stream=None) -> None:
+        """Shared-expert results of the n home tokens at pool rows `slot` (state indices
+        `tok`, generations `gen`) into `owner`'s combine state at position `kslot`."""
+        n = int(slot.numel() if n is None else n)
+        s = self.step
+        s.assemble(slot, self._zero[:n], 0, pool, n=n, stream=stream)
+        s.ffn(n, stream=stream)
+        self._kslot[:n].fill_(kslot)
+        owner.combine(s.y, s.pos, tok, self._kslot[:n], self._one[:n], gen, m=n, n_rows=n, stream=stream)

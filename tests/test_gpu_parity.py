@@ -496,3 +496,66 @@ def test_combine_plan_and_list_paths_agree():
     held = mask_a != 0
     assert held.any()
     assert np.array_equal(acc_a[held].view(np.uint32), acc_b[held].view(np.uint32))
+
+
+@pytest.mark.parametrize("shared_first", [False, True])
+def test_shared_expert_joins_the_combine(shared_first):
+    """Decode step with a shared expert at the home rank: every home token also goes through
+    a dense SwiGLU whose result is combine position K with weight 1.  No token is released
+    before both its routed and its shared results are in; the released rows match the
+    oracle's sum_j w_j E_j(x) + E_shared(x); the order of the two calls does not matter."""
+    _say("shared expert", "first" if shared_first else "last")
+    b, wts = W.c1_decode()
+    K, H, T = b.K, b.H, b.T
+    rng = np.random.default_rng(77)
+    sw = W.make_layer_weights(rng, 1, H, 1536, 0.02, "bf16")
+    d = batch_tensors(b)
+    wt, swt = weight_tensors(wts), weight_tensors(sw)
+    st = M.ExpertStep(b.E_loc, H, wts.I, K + 1, M.MOE_BF16, M.MOE_BF16, b.n, T)
+    st.load_weights(wt["wg"], wt["wu"], wt["wd"])
+    sh = M.SharedExpert(H, 1536, M.MOE_BF16, M.MOE_BF16, T)
+    sh.load_weights(swt["wg"], swt["wu"], swt["wd"])
+    # the home tokens: one pool slot per token index
+    t_slot = np.zeros(T, np.int32)
+    t_slot[b.tok] = b.slot
+    toks = np.arange(T, dtype=np.int32)
+    gens = np.zeros(T, np.uint32)
+    st.combine(d["r_rows"], d["r_idx"], d["r_tok"], d["r_kslot"], d["r_w"], d["r_gen"])
+    torch.cuda.synchronize()
+    assert int(st.rel_count.item()) == 0
+
+    def shared():
+        sh.run(st, dev(t_slot), d["pool"], dev(toks), dev(gens), kslot=K)
+        torch.cuda.synchronize()
+        return int(st.rel_count.item())
+
+    def routed():
+        st.run(d["slot"], d["expert"], b.expert_base, d["pool"], d["tok"], d["kslot"], d["w"], d["gen"])
+        torch.cuda.synchronize()
+        return int(st.rel_count.item())
+
+    first, second = (shared, routed) if shared_first else (routed, shared)
+    assert first() == 0          # a result is still missing for every token
+    n_rel = second()
+    assert n_rel == T and sync_err(st.err) == 0 and sync_err(sh.step.err) == 0
+    assert np.array_equal(st.rel_list[:n_rel].cpu().numpy(), toks)
+    # oracle: routed results, remote results, shared result at position K with weight 1
+    a, y = _oracle_step(b, wts)
+    y_sh = O.expert_ffn(O.decode(b.pool[t_slot], "bf16"), np.array([0, T]), sw)
+    ocs = O.CombineState(T, K + 1)
+    r = b.remote
+    O.combine_release(ocs, O.decode(r.rows, r.dtype), r.row_idx, r.tok, r.kslot, r.w, r.gen)
+    calls = [(y, a["pos"], b.tok, b.kslot, b.w, b.gen),
+             (y_sh, toks, toks, np.full(T, K, np.int32), np.ones(T, np.float32), gens)]
+    if shared_first:
+        calls.reverse()
+    out = {}
+    for args_ in calls:
+        o, rel, err = O.combine_release(ocs, *args_)
+        assert err == 0
+        out.update(o)
+    assert sorted(out) == list(range(T))
+    g = decode_tensor(st.out[:T])
+    err = row_rel_err(g, np.array([out[t] for t in range(T)]))
+    _say(f"  combined rows with the shared expert: err {err:.3e}")
+    assert err <= TOL["bf16"]
