@@ -6,11 +6,11 @@
 // grouped FFN sees one contiguous row range per expert.
 //
 // Two kernels:
-//   1. index kernel (one 1024-thread workgroup): per-expert histogram in LDS, a wave scan
+//   1. index kernel (one workgroup of 1024 threads, 256 for small queues): per-expert histogram in LDS, a wave scan
 //      for the exclusive offsets, then a stable scatter of queue indices.  Stability
-//      inside each 1024-pair chunk comes from a 9-bit wave "match" (ballot per key bit)
-//      giving each pair its rank among equal keys of lower lanes, plus per-wave counts
-//      scanned across the 16 waves.  Integer-only, so the result is deterministic.
+//      inside each chunk of one pair per thread comes from a 9-bit wave "match" (ballot per
+//      key bit) giving each pair its rank among equal keys of lower lanes, plus per-wave
+//      counts scanned across the waves.  Integer-only, so the result is deterministic.
 //   2. row gather: one 16-byte vector per thread, flattened over rows x 16-byte chunks so
 //      that consecutive lanes copy consecutive bytes of a row (fully coalesced reads of each
 //      pool row and writes of each batch row).
@@ -18,14 +18,16 @@
 
 namespace moe {
 
-constexpr int kAsmThreads = 1024;
-constexpr int kAsmWaves = kAsmThreads / kWave;
 constexpr int kMaxElocAsm = 256;
 
+// kAsmThreads threads: 1024, or 256 for queues of at most 256 pairs (every decode step),
+// where a quarter of the waves makes each workgroup barrier cheaper.
+template <int kAsmThreads>
 __global__ __launch_bounds__(kAsmThreads) void assemble_index_kernel(
     int n, const int32_t* __restrict__ slot, const int32_t* __restrict__ expert, int base, int E_loc, int64_t P,
     int32_t* __restrict__ perm, int32_t* __restrict__ pos, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, uint32_t* __restrict__ err) {
+  constexpr int kAsmWaves = kAsmThreads / kWave;
   __shared__ int s_run[kMaxElocAsm];
   __shared__ int s_wcnt[kAsmWaves][kMaxElocAsm + 1];
   __shared__ int s_total;
@@ -82,7 +84,7 @@ __global__ __launch_bounds__(kAsmThreads) void assemble_index_kernel(
   }
   __syncthreads();
 
-  // pass 2: stable scatter, one chunk of 1024 queue entries at a time
+  // pass 2: stable scatter, one chunk of kAsmThreads queue entries at a time
   for (int c0 = 0; c0 < n; c0 += kAsmThreads) {
     const int i = c0 + tid;
     int key = kMaxElocAsm;  // "rejected / past the end" key
@@ -161,8 +163,12 @@ extern "C" int moe_assemble(const moe_assemble_args* a, hipStream_t stream) {
     if (!a->slot || !a->expert || !a->perm || !a->pool) return MOE_EINVAL_NULL;
     if (!aligned16(a->pool) || (a->xb && !aligned16(a->xb))) return MOE_EINVAL_ALIGN;
   }
-  hipLaunchKernelGGL(assemble_index_kernel, dim3(1), dim3(kAsmThreads), 0, stream, a->n, a->slot, a->expert,
-                     a->expert_base, a->E_loc, a->P, a->perm, a->pos, a->counts, a->offsets, a->err);
+  if (a->n <= 256)
+    hipLaunchKernelGGL(assemble_index_kernel<256>, dim3(1), dim3(256), 0, stream, a->n, a->slot, a->expert,
+                       a->expert_base, a->E_loc, a->P, a->perm, a->pos, a->counts, a->offsets, a->err);
+  else
+    hipLaunchKernelGGL(assemble_index_kernel<1024>, dim3(1), dim3(1024), 0, stream, a->n, a->slot, a->expert,
+                       a->expert_base, a->E_loc, a->P, a->perm, a->pos, a->counts, a->offsets, a->err);
   if (a->n == 0 || !a->xb) return launch_status();  // no xb: the FFN gathers on load
   const int cpr = row_bytes / 16;
   const int64_t work = (int64_t)a->n * cpr;

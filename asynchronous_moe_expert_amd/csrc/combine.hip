@@ -309,7 +309,8 @@ constexpr uint32_t kNoTok = 0xfffffu;     // token field of a rejected arrival's
 // arrival-index order.
 __host__ __device__ constexpr int64_t plan_list_offset(int m) { return 4 + 4 * (int64_t)m; }
 
-// exclusive prefix sum over the workgroup (kPlanThreads threads); *total gets the sum
+// exclusive prefix sum over the workgroup (T threads); *total gets the sum
+template <int T>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* s_wsum, int& total) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   int incl = v;
@@ -324,7 +325,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_wsum, int& tot
   int before = 0;
   total = 0;
 #pragma unroll
-  for (int w = 0; w < kPlanThreads / 64; ++w) {
+  for (int w = 0; w < T / 64; ++w) {
     const int c = s_wsum[w];
     before += w < wv ? c : 0;
     total += c;
@@ -332,16 +333,20 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_wsum, int& tot
   return before + incl - v;
 }
 
-__global__ __launch_bounds__(kPlanThreads) void combine_plan_kernel(
+// T threads: kPlanThreads, or 256 for calls of at most 256 arrivals (every decode step), where a
+// quarter of the waves makes each workgroup barrier cheaper.  Takes m <= T arrivals.
+template <int T>
+__global__ __launch_bounds__(T) void combine_plan_kernel(
     int m, int K, int64_t n_rows, const int32_t* __restrict__ row_idx, const int32_t* __restrict__ tok,
     const int32_t* __restrict__ kslot, const float* __restrict__ wgt, const uint32_t* __restrict__ gen,
     uint32_t* __restrict__ tgen, uint32_t* __restrict__ mask, int T_cap, int32_t* __restrict__ ws,
     int32_t* __restrict__ rel_list, int32_t* __restrict__ rel_count, uint32_t* __restrict__ err) {
-  __shared__ uint32_t key[kPlanMax];
-  __shared__ int2 s_rw[kPlanMax];      // (row index, weight bits) of each arrival
-  __shared__ uint32_t s_mask[kPlanMax];  // mask of the arrival's token before the call
-  __shared__ uint8_t s_j[kPlanMax];
-  __shared__ int s_wsum[kPlanThreads / 64];
+  static_assert(T <= kPlanMax, "arrival index fits the key's 12 bits");
+  __shared__ uint32_t key[T];
+  __shared__ int2 s_rw[T];      // (row index, weight bits) of each arrival
+  __shared__ uint32_t s_mask[T];  // mask of the arrival's token before the call
+  __shared__ uint8_t s_j[T];
+  __shared__ int s_wsum[T / 64];
   __shared__ unsigned s_err;
   const int tid = threadIdx.x;
   int N = 1;
@@ -351,7 +356,7 @@ __global__ __launch_bounds__(kPlanThreads) void combine_plan_kernel(
   //    key = token << 12 | arrival for an accepted candidate, kNoTok << 12 | arrival for a
   //    rejected one or padding: every key is distinct and the rejected ones sort last
   unsigned flags = 0u;
-  for (int i = tid; i < N; i += kPlanThreads) {
+  for (int i = tid; i < N; i += T) {
     uint32_t k = (kNoTok << 12) | (uint32_t)i;
     if (i < m) {
       const int t = tok[i], j = kslot[i];
@@ -379,7 +384,6 @@ __global__ __launch_bounds__(kPlanThreads) void combine_plan_kernel(
   __syncthreads();
   // 2. sort key[0, N) ascending (by token, then arrival index).  Keys are distinct, so each
   //    key's place is the number of smaller keys: one pass over LDS per thread.
-  static_assert(kPlanMax <= kPlanThreads, "one key per thread");
   {
     const uint32_t k = tid < N ? key[tid] : 0u;
     int rank = 0;
@@ -398,7 +402,7 @@ __global__ __launch_bounds__(kPlanThreads) void combine_plan_kernel(
     if (tid < N) key[rank] = k;
   }
   __syncthreads();
-  // 3.-5. segments, in rounds of kPlanThreads sorted positions (one per thread, so that
+  // 3.-5. segments, in rounds of T sorted positions (one per thread, so that
   // every segment's state load is in flight at once): a position whose token differs from
   // its predecessor's heads a segment; its thread accepts the segment's positions in
   // arrival order, updates the token's state and writes the segment record; completed
@@ -407,7 +411,7 @@ __global__ __launch_bounds__(kPlanThreads) void combine_plan_kernel(
   int32_t* seg_rec = ws + 4;
   int2* list2 = reinterpret_cast<int2*>(ws + plan_list_offset(m));
   int n_seg = 0, n_rel = 0;
-  for (int p0 = 0; p0 < N; p0 += kPlanThreads) {
+  for (int p0 = 0; p0 < N; p0 += T) {
     const int p = p0 + tid;
     bool head = false;
     uint32_t t = 0u;
@@ -417,7 +421,7 @@ __global__ __launch_bounds__(kPlanThreads) void combine_plan_kernel(
     }
     uint32_t mk = head ? s_mask[key[p] & 4095u] : 0u;
     int round_seg = 0, round_rel = 0;
-    const int seg = n_seg + block_exclusive_scan(head ? 1 : 0, s_wsum, round_seg);
+    const int seg = n_seg + block_exclusive_scan<T>(head ? 1 : 0, s_wsum, round_seg);
     bool complete = false;
     if (head) {
       const bool started = mk != 0u;
@@ -441,7 +445,7 @@ __global__ __launch_bounds__(kPlanThreads) void combine_plan_kernel(
         mask[t] = mk;
       }
     }
-    const int o = n_rel + block_exclusive_scan(complete ? 1 : 0, s_wsum, round_rel);
+    const int o = n_rel + block_exclusive_scan<T>(complete ? 1 : 0, s_wsum, round_rel);
     if (complete) rel_list[o] = (int)t;
     n_seg += round_seg;
     n_rel += round_rel;
@@ -579,9 +583,14 @@ extern "C" int moe_combine_plan(const moe_combine_args* a, hipStream_t stream) {
   if (rc != MOE_OK) return rc;
   const moe_combine_state& s = a->state;
   if (plan_path(a)) {
-    hipLaunchKernelGGL(combine_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a->m, a->K, a->n_rows,
-                       a->row_idx, a->tok, a->kslot, a->w, a->gen, s.tgen, s.mask, s.T_cap, (int32_t*)a->workspace,
-                       a->rel_list, a->rel_count, a->err);
+    if (a->m <= 256)
+      hipLaunchKernelGGL(combine_plan_kernel<256>, dim3(1), dim3(256), 0, stream, a->m, a->K, a->n_rows, a->row_idx,
+                         a->tok, a->kslot, a->w, a->gen, s.tgen, s.mask, s.T_cap, (int32_t*)a->workspace,
+                         a->rel_list, a->rel_count, a->err);
+    else
+      hipLaunchKernelGGL(combine_plan_kernel<kPlanThreads>, dim3(1), dim3(kPlanThreads), 0, stream, a->m, a->K,
+                         a->n_rows, a->row_idx, a->tok, a->kslot, a->w, a->gen, s.tgen, s.mask, s.T_cap,
+                         (int32_t*)a->workspace, a->rel_list, a->rel_count, a->err);
   } else if (a->m > 0) {
     hipLaunchKernelGGL(combine_link_kernel, dim3((unsigned)((a->m + 255) / 256)), dim3(256), 0, stream, a->m, a->K,
                        a->n_rows, a->row_idx, a->tok, a->kslot, a->gen, s.tgen, s.T_cap, s.head,
