@@ -261,23 +261,15 @@ __device__ __forceinline__ void wg_barrier() {
 constexpr int kFfnWaves = 4;
 
 // expert (or -1), column block and rows of unit u of the batch, when u < u_end.  Units are
-// numbered column-block-major (u = nb * total + chunk) or, with n_blocks > 0, chunk-major
-// (u = chunk * n_blocks + nb).
+// numbered column-block-major (u = nb * total + chunk).
 __device__ __forceinline__ int next_unit(const int32_t* __restrict__ offsets, int E_loc, int n_rows, int BM, int lane,
-                                         int u, int u_end, int total, int& nb, int& m0, int& mend, int n_blocks = 0) {
+                                         int u, int u_end, int total, int& nb, int& m0, int& mend) {
   int e = -1;
   if (u < u_end) {
     ChunkTable tab;
     tab.build(offsets, E_loc, n_rows, BM, lane);
-    int c;
-    if (n_blocks > 0) {
-      c = u / n_blocks;
-      nb = u - c * n_blocks;
-    } else {
-      nb = u / total;
-      c = u - nb * total;
-    }
-    tab.find(c, BM, e, m0, mend);
+    nb = u / total;
+    tab.find(u - nb * total, BM, e, m0, mend);
   }
   return e;
 }
@@ -555,12 +547,121 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, int
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, n, 0x00020000);
 }
 
+// Balancing the last round.  Each XCD takes a contiguous range of n units and runs them on
+// its Gx = G/8 workgroups, R = n / Gx full rounds and a tail of T = n % Gx units.  A tail
+// of at most Gx/2 units would leave most CUs idle for a whole unit time, so each tail unit
+// is split along the contraction into S = min(Gx / T, 8, KS / 4) pieces of whole k-steps:
+// workgroup j of the XCD takes piece j % S of tail unit j / S and writes its raw fp32
+// accumulators to partial slot b = 8 j + xcd (one 128 KiB tile per workgroup); a finalize
+// launch then sums each tail unit's S partial tiles in piece order and applies the
+// epilogue.  With no partial area (or S < 2) the tail units run whole.
+constexpr int kGemmAccRegs = 4 * 2 * 16;                         // fp32 accumulators per thread
+constexpr int64_t kGemmPartFloats = (int64_t)kGemmAccRegs * 256;  // one partial tile
+constexpr int kGemmSplitSlots = 256;                              // partial tiles in the workspace
+constexpr int kGemmMaxSplit = 8;
+
+struct GemmSplit {
+  int u0, Gx, R, T, S;
+  __device__ __forceinline__ void init(int U, int G, int xcd, int KS, bool enabled) {
+    Gx = G >> 3;
+    u0 = (int)((int64_t)U * xcd / 8);
+    const int n = (int)((int64_t)U * (xcd + 1) / 8) - u0;
+    R = n / Gx;
+    T = n - R * Gx;
+    S = 1;
+    if (enabled && T > 0) S = min(min(Gx / T, kGemmMaxSplit), KS / 4);
+    if (S < 2) S = 1;
+  }
+};
+
+// chunk and column block of unit u (units are chunk-major or column-block-major)
+__device__ __forceinline__ void gemm_unit_coords(int u, int total, int n_blocks_N, int& c, int& nb) {
+  if (kGemmChunkMajor) {
+    c = u / n_blocks_N;
+    nb = u - c * n_blocks_N;
+  } else {
+    nb = u / total;
+    c = u - nb * total;
+  }
+}
+
+// Epilogue of a 128 x 256 unit; accumulator v of lane l holds column l%32 and row
+// 8(v/4) + 4(l/32) + v%4 of a tile.  gemm_store_group writes accumulators 4g .. 4g+3 of row
+// tile mt of both column tiles (t = 0: a[], t = 1: b[]); for gate/up these are the gate and
+// the up value of one h column.  sc0, sc1: the fp8 row scales of the lane's columns.
+template <int MODE>
+__device__ __forceinline__ void gemm_store_group(const float (&a)[4], const float (&b)[4], int mt, int g, int m0,
+                                                 int mend, int col0, int hf, int l32, float sc0, float sc1,
+                                                 uint16_t* __restrict__ out, int out_ld) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int row = m0 + mt * 32 + 8 * g + 4 * hf + k;
+    if (row >= mend) continue;
+    if (MODE == 0) {
+      out[(int64_t)row * out_ld + col0 / 2 + l32] = f32_to_bf16(silu_mul_fast(a[k] * sc0, b[k] * sc1));
+    } else {
+      out[(int64_t)row * out_ld + col0 + l32] = f32_to_bf16(a[k] * sc0);
+      out[(int64_t)row * out_ld + col0 + 32 + l32] = f32_to_bf16(b[k] * sc1);
+    }
+  }
+}
+
+// the lane's two fp8 row scales (1 for bf16 weights): gate/up: gate and up scale of h
+// column col0/2 + l32; down: output columns col0 + l32 and col0 + 32 + l32
+template <int MODE, int WDT>
+__device__ __forceinline__ void gemm_scales(int e, int col0, int l32, const float* __restrict__ s0,
+                                            const float* __restrict__ s1, int out_ld, float& sc0, float& sc1) {
+  sc0 = sc1 = 1.f;
+  if (WDT != MOE_FP8_E4M3) return;
+  if (MODE == 0) {
+    sc0 = s0[(int64_t)e * out_ld + col0 / 2 + l32];
+    sc1 = s1[(int64_t)e * out_ld + col0 / 2 + l32];
+  } else {
+    sc0 = s0[(int64_t)e * out_ld + col0 + l32];
+    sc1 = s0[(int64_t)e * out_ld + col0 + 32 + l32];
+  }
+}
+
+template <int MODE, int WDT>
+__device__ __forceinline__ void gemm_epilogue(const f32x16 (&acc)[4][2], int e, int m0, int mend, int col0, int hf,
+                                              int l32, const float* __restrict__ s0, const float* __restrict__ s1,
+                                              uint16_t* __restrict__ out, int out_ld) {
+  float sc0, sc1;
+  gemm_scales<MODE, WDT>(e, col0, l32, s0, s1, out_ld, sc0, sc1);
+  static_for<4>([&](auto mt) {
+    static_for<4>([&](auto g) {
+      float a[4], b[4];
+      static_for<4>([&](auto k) {
+        a[k()] = acc[mt()][0][4 * g() + k()];
+        b[k()] = acc[mt()][1][4 * g() + k()];
+      });
+      gemm_store_group<MODE>(a, b, mt(), g(), m0, mend, col0, hf, l32, sc0, sc1, out, out_ld);
+    });
+  });
+}
+
+// Partial tile layout: accumulator group q = 4 (2 mt + t) + v/4 of thread tid at
+// part[1024 q + 4 tid .. + 3] (each wave stores and loads 1 KiB runs).
+__device__ __forceinline__ void store_partial(const f32x16 (&acc)[4][2], float* __restrict__ part, int tid) {
+  static_for<4>([&](auto mt) {
+    static_for<2>([&](auto t) {
+      static_for<4>([&](auto g) {
+        constexpr int q = 4 * (2 * mt() + t()) + g();
+        const float4 v = make_float4(acc[mt()][t()][4 * g()], acc[mt()][t()][4 * g() + 1], acc[mt()][t()][4 * g() + 2],
+                                     acc[mt()][t()][4 * g() + 3]);
+        *reinterpret_cast<float4*>(part + 1024 * q + 4 * tid) = v;
+      });
+    });
+  });
+}
+
 template <int MODE, int WDT>
 __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets,
                                                        int E_loc, const char* __restrict__ W,
                                                        const float* __restrict__ s0, const float* __restrict__ s1,
                                                        uint16_t* __restrict__ out, int Kd, int Nw, int out_ld,
-                                                       int n_blocks_N, int n_rows, GatherRows gr) {
+                                                       int n_blocks_N, int n_rows, GatherRows gr,
+                                                       float* __restrict__ parts) {
   constexpr int S = kGemmStages;
   constexpr int esz = WDT == MOE_FP8_E4M3 ? 1 : 2;
   __shared__ u32x4 a_lds[2][kGemmBM * 8];  // activation k-tile, 2 stages of 16 KiB
@@ -570,30 +671,31 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(const uint16_t* __rest
   const int64_t strip_stride = (int64_t)KS * 1024 * esz;
   const int l32 = lane & 31, hf = lane >> 5;
 
-  const int G = gridDim.x, b = blockIdx.x, xcd = b & 7;
-  int total, u, u_end, nb = 0, e = -1, m0 = 0, mend = 0;
-  {
-    ChunkTable tab;
-    tab.build(offsets, E_loc, n_rows, kGemmBM, lane);
-    total = tab.total;
-    const int U = total * n_blocks_N;
-    u = (int)((int64_t)U * xcd / 8) + (b >> 3);
-    u_end = (int)((int64_t)U * (xcd + 1) / 8);
-    if (u < u_end) {
-      int c;
-      if (kGemmChunkMajor) {
-        c = u / n_blocks_N;
-        nb = u - c * n_blocks_N;
-      } else {
-        nb = u / total;
-        c = u - nb * total;
-      }
-      tab.find(c, kGemmBM, e, m0, mend);
+  const int b = blockIdx.x, xcd = b & 7, j = b >> 3;
+  ChunkTable tab;
+  tab.build(offsets, E_loc, n_rows, kGemmBM, lane);
+  const int total = tab.total;
+  GemmSplit sp;
+  sp.init(total * n_blocks_N, gridDim.x, xcd, KS, parts != nullptr);
+  // this workgroup's items: R full units (one more if the tail runs whole), then its piece
+  const int n_full = sp.R + (sp.S == 1 && j < sp.T ? 1 : 0);
+  const int n_items = n_full + (sp.S > 1 && j < sp.T * sp.S ? 1 : 0);
+#pragma clang loop unroll(disable)
+  for (int item = 0; item < n_items; ++item) {
+    int u, k0 = 0, k1 = KS;
+    const bool piece = item >= n_full;
+    if (!piece) {
+      u = sp.u0 + item * sp.Gx + j;
+    } else {
+      u = sp.u0 + sp.R * sp.Gx + j / sp.S;
+      const int pc = j % sp.S;
+      k0 = pc * KS / sp.S;
+      k1 = (pc + 1) * KS / sp.S;
     }
-  }
-  for (; u < u_end; u += G >> 3, e = next_unit(offsets, E_loc, n_rows, kGemmBM, lane, u, u_end, total, nb, m0, mend,
-                                                kGemmChunkMajor ? n_blocks_N : 0)) {
-    if (e < 0) break;  // not reachable: the table is the same on every build
+    int c, nb, e, m0, mend;
+    gemm_unit_coords(u, total, n_blocks_N, c, nb);
+    tab.find(c, kGemmBM, e, m0, mend);
+    if (e < 0) break;  // not reachable: every unit id below U names a chunk
     const int col0 = nb * kGemmBN + wv * kGemmWaveN;
     const bool wact = col0 < Nw;        // the last column block may be partial
     const int colw = wact ? col0 : 0;   // idle waves stream valid weights (results unused)
@@ -624,16 +726,16 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(const uint16_t* __rest
     });
 
     f32x16 acc[4][2];
-    static_for<4>([&](auto i) { static_for<2>([&](auto j) { acc[i()][j()] = f32x16{}; }); });
+    static_for<4>([&](auto i) { static_for<2>([&](auto jj) { acc[i()][jj()] = f32x16{}; }); });
 
     GemmW<WDT> wr[S];   // weight fragments of steps i .. i+S-1
     u32x4 ar[4][4];     // this thread's activation pieces of steps i+1 .. i+4
     u32x4 af[4][4];     // activation fragments [k-slice s][mt] of the step being computed
     auto issue_a = [&](auto aslot, int ks) {
-      ks = min(ks, KS - 1);
+      ks = min(ks, k1 - 1);
       static_for<4>([&](auto d) { ar[aslot()][d()] = __builtin_amdgcn_raw_buffer_load_b128(ars, avo[d()], ks * kBK * 2, 0); });
     };
-    auto issue_w = [&](auto slot, int ks) { wr[slot()].load(wrs, wvo, min(ks, KS - 1) * 1024 * esz); };
+    auto issue_w = [&](auto slot, int ks) { wr[slot()].load(wrs, wvo, min(ks, k1 - 1) * 1024 * esz); };
     // park this thread's pieces of a step in LDS; the compiler waits for their loads only
     // (loads retire in order and the weights of the same step were issued after them)
     auto park = [&](auto aslot, auto stg) {
@@ -669,17 +771,17 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(const uint16_t* __rest
       });
     };
     using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
-    // Software pipeline over k-steps i (weight and activation slot i % 4, LDS stage i % 2).
-    // Step i: MFMAs of slices 0-1 of step i; park the activation pieces of step i+1 in LDS
-    // and barrier; read slices 0-1 of step i+1 into the registers just freed; MFMAs of
-    // slices 2-3 of step i; read slices 2-3 of step i+1 (their LDS latency hides behind the
-    // first MFMAs of step i+1); issue the loads of step i+4 (activations, then weights) into
-    // the slots step i has freed.  Loads are issued in the order they are needed, so the
-    // in-order completion of loads never makes a wait drain a later step.  A unit runs a
-    // whole number of 4-step groups: steps past the contraction read clamped (valid) data and
-    // zero their activation fragments, so every step has the same branch-free body.
+    // Software pipeline over k-steps i = k0, k0+1, ... (weight and activation slot
+    // (i - k0) % 4, LDS stage (i - k0) % 2).  Step i: MFMAs of slices 0-1 of step i; park the
+    // activation pieces of step i+1 in LDS and barrier; read slices 0-1 of step i+1 into the
+    // registers just freed; MFMAs of slices 2-3 of step i; read slices 2-3 of step i+1
+    // (their LDS latency hides behind the first MFMAs of step i+1); issue the loads of step
+    // i+4 (activations, then weights) into the slots step i has freed.  Loads are issued in
+    // the order they are needed, so the in-order completion of loads never makes a wait
+    // drain a later step.  An item runs a whole number of 4-step groups: steps past k1 read
+    // clamped (valid) data and zero their activation fragments, so every step has the same
+    // branch-free body.
     static_assert(S == 4, "weight and activation rings of 4, LDS stages of 2");
     auto issue = [&](auto slot, int ks) {
       issue_a(slot, ks);
@@ -687,14 +789,14 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(const uint16_t* __rest
     };
     static_for<4>([&](auto v) {  // same batch order as the loop, so every wait matches the steady state
       __builtin_amdgcn_sched_barrier(0);
-      issue(v, v());
+      issue(v, k0 + v());
     });
     __builtin_amdgcn_sched_barrier(0);
     park(I0{}, I0{});
     barrier();
     read(I0{}, I0{});
     read(I0{}, I2{});
-    const int n_steps = (KS + 3) / 4 * 4;
+    const int n_steps = (k1 - k0 + 3) / 4 * 4;
 #pragma clang loop unroll(disable)
     for (int it = 0; it < n_steps; it += 4) {
       static_for<4>([&](auto v) {
@@ -702,8 +804,8 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(const uint16_t* __rest
         using SL = std::integral_constant<int, slot>;
         using NX = std::integral_constant<int, (slot + 1) % 4>;
         using P1 = std::integral_constant<int, (slot + 1) & 1>;
-        const int i = it + v();
-        if (i >= KS) static_for<4>([&](auto ss) { static_for<4>([&](auto mt) { af[ss()][mt()] = u32x4{}; }); });
+        const int i = k0 + it + v();
+        if (i >= k1) static_for<4>([&](auto ss) { static_for<4>([&](auto mt) { af[ss()][mt()] = u32x4{}; }); });
         mfmas(SL{}, I0{});
         park(NX{}, P1{});
         barrier();
@@ -715,51 +817,81 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(const uint16_t* __rest
         __builtin_amdgcn_sched_barrier(0);
       });
     }
-    barrier();  // the next unit's first LDS writes wait for this unit's last reads
+    barrier();  // the next item's first LDS writes wait for this item's last reads
     if (!wact) continue;
-
-    // epilogue; accumulator v of lane l holds column l%32 and row 8(v/4) + 4(l/32) + v%4 of a
-    // tile.  The fp8 row scales of a lane's columns are read once, before the stores.
-    if (MODE == 0) {
-      const int col = col0 / 2 + l32;  // h column: gate in tile 0, up in tile 1
-      float sg = 1.f, su = 1.f;
-      if (WDT == MOE_FP8_E4M3) {
-        sg = s0[(int64_t)e * out_ld + col];
-        su = s1[(int64_t)e * out_ld + col];
-      }
-      static_for<4>([&](auto mt) {
-        static_for<16>([&](auto v) {
-          const int row = m0 + mt() * 32 + 8 * (v() >> 2) + 4 * hf + (v() & 3);
-          if (row < mend)
-            out[(int64_t)row * out_ld + col] = f32_to_bf16(silu_mul_fast(acc[mt()][0][v()] * sg, acc[mt()][1][v()] * su));
-        });
-      });
-    } else {
-      static_for<2>([&](auto t) {
-        const int col = col0 + t() * 32 + l32;
-        const float sc = WDT == MOE_FP8_E4M3 ? s0[(int64_t)e * out_ld + col] : 1.f;
-        static_for<4>([&](auto mt) {
-          static_for<16>([&](auto v) {
-            const int row = m0 + mt() * 32 + 8 * (v() >> 2) + 4 * hf + (v() & 3);
-            if (row < mend) out[(int64_t)row * out_ld + col] = f32_to_bf16(acc[mt()][t()][v()] * sc);
-          });
-        });
-      });
-    }
+    if (piece)
+      store_partial(acc, parts + (int64_t)b * kGemmPartFloats, tid);
+    else
+      gemm_epilogue<MODE, WDT>(acc, e, m0, mend, col0, hf, l32, s0, s1, out, out_ld);
   }
 }
 
+// Sums each split tail unit's partial tiles in piece order and applies the epilogue.  One
+// workgroup per (XCD, tail unit t, row tile mt, accumulator group g): its threads load the
+// two float4 groups q = 8 mt + g (column tile 0) and 8 mt + 4 + g (tile 1) of all S pieces
+// at once, so the whole pass is about one memory round trip.  Workgroup b: XCD b & 7,
+// t = b >> 7, (mt, g) = (b >> 3) & 15 (a split needs T <= Gx/2, so 8 G workgroups cover
+// every tail unit); the bookkeeping is the GEMM launch's with the same grid G.
+template <int MODE, int WDT>
+__global__ __launch_bounds__(256) void ffn_gemm_finalize_kernel(const int32_t* __restrict__ offsets, int E_loc,
+                                                                int n_rows, int n_blocks_N, int KS, int G,
+                                                                const float* __restrict__ parts,
+                                                                const float* __restrict__ s0,
+                                                                const float* __restrict__ s1,
+                                                                uint16_t* __restrict__ out, int Nw, int out_ld) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int b = blockIdx.x, xcd = b & 7, t = b >> 7, mt = (b >> 5) & 3, g = (b >> 3) & 3;
+  ChunkTable tab;
+  tab.build(offsets, E_loc, n_rows, kGemmBM, lane);
+  GemmSplit sp;
+  sp.init(tab.total * n_blocks_N, G, xcd, KS, true);
+  if (sp.S < 2 || t >= sp.T) return;
+  int c, nb, e, m0, mend;
+  gemm_unit_coords(sp.u0 + sp.R * sp.Gx + t, tab.total, n_blocks_N, c, nb);
+  tab.find(c, kGemmBM, e, m0, mend);
+  const int col0 = nb * kGemmBN + wv * kGemmWaveN;
+  if (e < 0 || col0 >= Nw || m0 + mt * 32 >= mend) return;  // (no barriers: waves leave independently)
+  float4 v[kGemmMaxSplit][2];
+#pragma unroll
+  for (int pc = 0; pc < kGemmMaxSplit; ++pc) {
+    if (pc < sp.S) {
+      const float* part = parts + (int64_t)(((t * sp.S + pc) << 3) | xcd) * kGemmPartFloats + 4 * tid;
+      v[pc][0] = *reinterpret_cast<const float4*>(part + 1024 * (8 * mt + g));
+      v[pc][1] = *reinterpret_cast<const float4*>(part + 1024 * (8 * mt + 4 + g));
+    }
+  }
+  float a[4] = {0.f, 0.f, 0.f, 0.f}, bb[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int pc = 0; pc < kGemmMaxSplit; ++pc) {
+    if (pc < sp.S) {
+      a[0] += v[pc][0].x; a[1] += v[pc][0].y; a[2] += v[pc][0].z; a[3] += v[pc][0].w;
+      bb[0] += v[pc][1].x; bb[1] += v[pc][1].y; bb[2] += v[pc][1].z; bb[3] += v[pc][1].w;
+    }
+  }
+  float sc0, sc1;
+  gemm_scales<MODE, WDT>(e, col0, l32, s0, s1, out_ld, sc0, sc1);
+  gemm_store_group<MODE>(a, bb, mt, g, m0, mend, col0, hf, l32, sc0, sc1, out, out_ld);
+}
+
+// parts: kGemmSplitSlots partial tiles of workspace, or nullptr (tail units run whole)
 template <int MODE, int WDT>
 static void launch_gemm(const void* A, const int32_t* offsets, int E_loc, const void* W, const float* s0,
-                        const float* s1, void* out, int Kd, int Nw, int out_ld, int n, GatherRows gr,
+                        const float* s1, void* out, int Kd, int Nw, int out_ld, int n, GatherRows gr, float* parts,
                         hipStream_t stream) {
   constexpr auto kernel = ffn_gemm_kernel<MODE, WDT>;
   const int n_blocks_N = (Nw + kGemmBN - 1) / kGemmBN;
   const int64_t chunks_max = (n + (int64_t)(kGemmBM - 1) * E_loc) / kGemmBM;
   int64_t grid = std::min<int64_t>(chunks_max * n_blocks_N, resident_workgroups<kernel>(256));
   grid = (grid + 7) / 8 * 8;
+  if (grid > kGemmSplitSlots) parts = nullptr;
   hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), 0, stream, (const uint16_t*)A, offsets, E_loc,
-                     (const char*)W, s0, s1, (uint16_t*)out, Kd, Nw, out_ld, n_blocks_N, n, gr);
+                     (const char*)W, s0, s1, (uint16_t*)out, Kd, Nw, out_ld, n_blocks_N, n, gr, parts);
+  if (parts)
+    hipLaunchKernelGGL((ffn_gemm_finalize_kernel<MODE, WDT>), dim3((unsigned)(8 * grid)), dim3(256), 0, stream, offsets,
+                       E_loc, n, n_blocks_N, Kd / kBK, (int)grid, (const float*)parts, s0, s1, (uint16_t*)out, Nw,
+                       out_ld);
 }
 
 // Row-chunk height: tall enough that an average expert group fits one chunk with room for
@@ -804,7 +936,7 @@ static int pick_mt(int n, int E_loc) {
 
 template <int MODE, int WDT>
 static void launch_mfma(const void* A, const int32_t* offsets, int E_loc, const void* W, const float* s0,
-                        const float* s1, void* out, int Kd, int Nw, int out_ld, int n, GatherRows gr,
+                        const float* s1, void* out, int Kd, int Nw, int out_ld, int n, GatherRows gr, float* parts,
                         hipStream_t stream) {
   constexpr int NS = MODE == 0 ? MOE_FFN_NS_GU : MOE_FFN_NS_D;
   constexpr int R = MODE == 0 ? MOE_FFN_R_GU : MOE_FFN_R_D;
@@ -812,7 +944,7 @@ static void launch_mfma(const void* A, const int32_t* offsets, int E_loc, const 
   // (the GEMM kernel addresses its activation operand with 32-bit byte offsets)
   const int64_t a_bytes = gr.perm ? gr.P * gr.pitch * 2 : (int64_t)n * Kd * 2;
   if (MOE_FFN_MT == 0 && n >= MOE_FFN_GEMM_ROWS * E_loc && a_bytes < ((int64_t)1 << 31)) {
-    launch_gemm<MODE, WDT>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, gr, stream);
+    launch_gemm<MODE, WDT>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, gr, parts, stream);
     return;
   }
   switch (pick_mt(n, E_loc)) {
@@ -825,12 +957,17 @@ static void launch_mfma(const void* A, const int32_t* offsets, int E_loc, const 
 
 using namespace moe;
 
+static size_t h_bytes(int64_t n, int I, int esz) { return ((size_t)n * (size_t)I * esz + 255) / 256 * 256; }
+static constexpr size_t kPartAreaBytes = (size_t)kGemmSplitSlots * kGemmPartFloats * sizeof(float);
+
+// h [n_max][I], then (for batches that can take the GEMM path) the partial tiles of its
+// split tail units
 extern "C" size_t moe_ffn_workspace_size(int32_t n_max, int32_t E_loc, int32_t H, int32_t I, int32_t act_dtype) {
-  (void)E_loc;
   (void)H;
   const int esz = dtype_size(act_dtype);
   if (n_max < 0 || I < 0 || esz == 0) return 0;
-  return ((size_t)n_max * (size_t)I * esz + 255) / 256 * 256;
+  const bool gemm = act_dtype == MOE_BF16 && E_loc >= 1 && (int64_t)n_max >= (int64_t)MOE_FFN_GEMM_ROWS * E_loc;
+  return h_bytes(n_max, I, esz) + (gemm ? kPartAreaBytes : 0);
 }
 
 extern "C" int moe_pack_ffn_weights(const moe_pack_args* a, hipStream_t stream) {
@@ -890,10 +1027,17 @@ extern "C" int moe_expert_ffn_grouped(const moe_ffn_args* a, hipStream_t stream)
   if (f8 && (!a->s_gate || !a->s_up || !a->s_down)) return MOE_EINVAL_NULL;
   if (!aligned16(x_src) || !aligned16(a->w_gu) || !aligned16(a->w_d) || !aligned16(a->y)) return MOE_EINVAL_ALIGN;
   const GatherRows none{nullptr, nullptr, 0, 0};
-  const size_t ws = moe_ffn_workspace_size(a->n, a->E_loc, a->H, a->I, a->act_dtype);
-  if (!a->workspace || a->workspace_bytes < ws) return MOE_EWORKSPACE;
+  // h is required; the partial area after it is optional (see below)
+  if (!a->workspace || a->workspace_bytes < h_bytes(a->n, a->I, dtype_size(a->act_dtype))) return MOE_EWORKSPACE;
   if (!aligned16(a->workspace)) return MOE_EINVAL_ALIGN;
   const int n = a->n, H = a->H, I = a->I, E = a->E_loc;
+  // partial tiles for the GEMM path's split tail, when the workspace has room for them
+  // (it does when sized by moe_ffn_workspace_size for a batch of at least n rows)
+  float* parts = nullptr;
+  {
+    const size_t off = h_bytes(n, I, dtype_size(a->act_dtype));
+    if (a->workspace_bytes >= off + kPartAreaBytes) parts = (float*)((char*)a->workspace + off);
+  }
   if (f32) {
     const int64_t t1 = (int64_t)n * I, t2 = (int64_t)n * H;
     hipLaunchKernelGGL(gateup_f32_kernel, dim3((unsigned)((t1 + 255) / 256)), dim3(256), 0, stream,
@@ -904,15 +1048,17 @@ extern "C" int moe_expert_ffn_grouped(const moe_ffn_args* a, hipStream_t stream)
     return launch_status();
   }
   if (bf) {
-    launch_mfma<0, MOE_BF16>(x_src, a->offsets, E, a->w_gu, nullptr, nullptr, a->workspace, H, 2 * I, I, n, gr, stream);
+    launch_mfma<0, MOE_BF16>(x_src, a->offsets, E, a->w_gu, nullptr, nullptr, a->workspace, H, 2 * I, I, n, gr, parts,
+                             stream);
     if (a->ev_mid) (void)hipEventRecord(a->ev_mid, stream);
-    launch_mfma<1, MOE_BF16>(a->workspace, a->offsets, E, a->w_d, nullptr, nullptr, a->y, I, H, H, n, none, stream);
+    launch_mfma<1, MOE_BF16>(a->workspace, a->offsets, E, a->w_d, nullptr, nullptr, a->y, I, H, H, n, none, parts,
+                             stream);
   } else {
     launch_mfma<0, MOE_FP8_E4M3>(x_src, a->offsets, E, a->w_gu, a->s_gate, a->s_up, a->workspace, H, 2 * I, I, n, gr,
-                                 stream);
+                                 parts, stream);
     if (a->ev_mid) (void)hipEventRecord(a->ev_mid, stream);
     launch_mfma<1, MOE_FP8_E4M3>(a->workspace, a->offsets, E, a->w_d, a->s_down, nullptr, a->y, I, H, H, n, none,
-                                 stream);
+                                 parts, stream);
   }
   return launch_status();
 }

@@ -151,7 +151,12 @@ int moe_pack_ffn_weights(const moe_pack_args* args, hipStream_t stream);
  * Supported (act, weight) pairs: (F32, F32), (BF16, BF16), (BF16, FP8_E4M3).  For fp8 the
  * three scale arrays are required: s_gate, s_up [E_loc][I], s_down [E_loc][H].
  * Limits: 1 <= E_loc <= 256, H % 64 == 0, I % 64 == 0, 0 <= n <= 2^24; 16-byte aligned
- * buffers.  The workspace must hold moe_ffn_workspace_size(...) bytes.
+ * buffers.  The workspace must hold moe_ffn_workspace_size(...) bytes: h ([n][I] in
+ * act_dtype, rounded up to 256 bytes) and, for batches that can take the tiled path for
+ * many rows per expert (bf16 activations, n_max >= 96 E_loc), 32 MiB of fp32 partial tiles
+ * for the k-split of each XCD's last partial round of work units.  With a workspace sized
+ * for h alone the call still runs, with those units computed whole (same values up to
+ * rounding order).  Results are deterministic for a given device and workspace size.
  * ev_mid: optional hipEvent_t recorded on the stream between the gate/up kernel and
  * the down kernel (for timing); pass NULL otherwise.
  *

@@ -559,3 +559,76 @@ def test_shared_expert_joins_the_combine(shared_first):
     err = row_rel_err(g, np.array([out[t] for t in range(T)]))
     _say(f"  combined rows with the shared expert: err {err:.3e}")
     assert err <= TOL["bf16"]
+
+
+def _gemm_split_plan(counts, Nw, Kd, G_res):
+    """Host model of the tiled kernel's work split (128-row chunks, 256 columns, 8 XCD ranges
+    of chunk-major units, a tail of T <= Gx/2 units split into S k-ranges): the tail units'
+    chunks of each XCD, with S, or an empty list when no tail is split."""
+    E, n = len(counts), int(sum(counts))
+    nbN = -(-Nw // 256)
+    U = sum(-(-c // 128) for c in counts) * nbN
+    G = min((n + 127 * E) // 128 * nbN, G_res)
+    G = -(-G // 8) * 8
+    Gx, KS = G // 8, Kd // 64
+    out = []
+    for x in range(8):
+        u0 = U * x // 8
+        nx = U * (x + 1) // 8 - u0
+        R, T = divmod(nx, Gx)
+        S = max(1, min(Gx // T, 8, KS // 4)) if T else 1
+        if S > 1:
+            out += [((u0 + R * Gx + t) // nbN, S) for t in range(T)]
+    return out
+
+
+@pytest.mark.parametrize("wdt", ["fp8", "bf16"])
+def test_gemm_split_tail_matches_whole_units(wdt):
+    """Tiled FFN kernel with each XCD's last partial round split along the contraction: the
+    result is deterministic, matches the run with whole tail units (workspace without the
+    partial area) to rounding, and matches the oracle on rows of the split units."""
+    E, H, I = 8, 1024, 512
+    counts = [2550, 1900, 1250, 1000, 850, 600, 380, 200]   # 70 chunks: 35 units per XCD
+    n = int(sum(counts))
+    _say("gemm split case", wdt, counts)
+    rng = np.random.default_rng(4242)
+    wts = W.make_layer_weights(rng, E, H, I, 0.05, wdt)
+    x_np = W.to_bf16_bits(rng.standard_normal((n, H)).astype(np.float32))
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    code = {"bf16": M.MOE_BF16, "fp8": M.MOE_FP8_E4M3}[wdt]
+    st = M.ExpertStep(E, H, I, 2, M.MOE_BF16, code, n, 4)
+    wt = weight_tensors(wts)
+    st.load_weights(wt["wg"], wt["wu"], wt["wd"], wt.get("s_gate"), wt.get("s_up"), wt.get("s_down"))
+    st.xb[:n].copy_(dev(x_np, "bf16"))
+    st.offsets.copy_(dev(offsets))
+    h_bytes = (n * I * 2 + 255) // 256 * 256
+    assert st.workspace.numel() >= h_bytes + 256 * 128 * 1024
+    ys = []
+    for ws in (st.workspace, st.workspace, st.workspace[:h_bytes]):
+        st.y.zero_()
+        M.moe_expert_ffn_grouped(n, E, H, I, M.MOE_BF16, code, st.xb, st.offsets, st.w_gu, st.w_d, st.y, ws,
+                                 st.s_gate, st.s_up, st.s_down)
+        torch.cuda.synchronize()
+        ys.append(to_numpy_bits(st.y[:n]))
+    assert np.array_equal(ys[0], ys[1]), "split run is not deterministic"
+    d = row_rel_err(O.decode_bf16(ys[0]), O.decode_bf16(ys[2]))
+    _say(f"  split vs whole-unit row rel diff {d:.3e}")
+    assert d <= 1e-2
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    plan = _gemm_split_plan(counts, 2 * I, H, cus)
+    if plan and cus == 256:
+        assert not np.array_equal(ys[0], ys[2]), "no split was taken where the launch model predicts one"
+    # oracle on rows of the split units' chunks (gate/up plan) plus a random sample
+    starts = np.concatenate([[0], np.cumsum([-(-c // 128) for c in counts])])
+    rows = list(rng.choice(n, 24, replace=False))
+    for c, _S in plan[::3]:
+        e = int(np.searchsorted(starts, c, side="right") - 1)
+        r0 = offsets[e] + (c - starts[e]) * 128
+        r1 = min(r0 + 128, offsets[e + 1])
+        rows += [r0, (r0 + r1) // 2, r1 - 1]
+    rows = np.unique(np.array(rows, dtype=np.int64))
+    le = np.searchsorted(offsets, rows, side="right") - 1
+    y_ref = O.ffn_rows(O.decode(x_np[rows], "bf16"), le, wts)
+    err = row_rel_err(O.decode_bf16(ys[0][rows]), y_ref)
+    _say(f"  {len(plan)} split tail units; oracle row rel err on {len(rows)} rows {err:.3e}")
+    assert err <= TOL[wdt]
