@@ -498,7 +498,14 @@ static void launch_mfma_t(const void* A, const int32_t* offsets, int E_loc, cons
 constexpr int kGemmBM = 128;
 constexpr int kGemmWaveN = 64;
 constexpr int kGemmBN = kGemmWaveN * kFfnWaves;
-constexpr int kGemmStages = 4;  // weight register ring
+// register-ring depth (k-steps of loads in flight + 1).  A 6-deep ring for fp8 weights
+// (500 VGPRs; 8 spills) measured no faster than 4: the CU's outstanding-request limit, not
+// the wave's prefetch distance, bounds the loads in flight
+#ifndef MOE_FFN_GEMM_STAGES_FP8
+#define MOE_FFN_GEMM_STAGES_FP8 4
+#endif
+template <int WDT>
+constexpr int gemm_stages() { return WDT == MOE_FP8_E4M3 ? MOE_FFN_GEMM_STAGES_FP8 : 4; }
 #ifndef MOE_FFN_GEMM_CHUNK_MAJOR
 #define MOE_FFN_GEMM_CHUNK_MAJOR 1
 #endif
@@ -662,7 +669,7 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(const uint16_t* __rest
                                                        uint16_t* __restrict__ out, int Kd, int Nw, int out_ld,
                                                        int n_blocks_N, int n_rows, GatherRows gr,
                                                        float* __restrict__ parts) {
-  constexpr int S = kGemmStages;
+  constexpr int S = gemm_stages<WDT>();
   constexpr int esz = WDT == MOE_FP8_E4M3 ? 1 : 2;
   __shared__ u32x4 a_lds[2][kGemmBM * 8];  // activation k-tile, 2 stages of 16 KiB
   const int tid = threadIdx.x, lane = tid & 63;
@@ -729,7 +736,7 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(const uint16_t* __rest
     static_for<4>([&](auto i) { static_for<2>([&](auto jj) { acc[i()][jj()] = f32x16{}; }); });
 
     GemmW<WDT> wr[S];   // weight fragments of steps i .. i+S-1
-    u32x4 ar[4][4];     // this thread's activation pieces of steps i+1 .. i+4
+    u32x4 ar[S][4];     // this thread's activation pieces of steps i+1 .. i+S
     u32x4 af[4][4];     // activation fragments [k-slice s][mt] of the step being computed
     auto issue_a = [&](auto aslot, int ks) {
       ks = min(ks, k1 - 1);
@@ -773,21 +780,21 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(const uint16_t* __rest
     using I0 = std::integral_constant<int, 0>;
     using I2 = std::integral_constant<int, 2>;
     // Software pipeline over k-steps i = k0, k0+1, ... (weight and activation slot
-    // (i - k0) % 4, LDS stage (i - k0) % 2).  Step i: MFMAs of slices 0-1 of step i; park the
+    // (i - k0) % S, LDS stage (i - k0) % 2).  Step i: MFMAs of slices 0-1 of step i; park the
     // activation pieces of step i+1 in LDS and barrier; read slices 0-1 of step i+1 into the
     // registers just freed; MFMAs of slices 2-3 of step i; read slices 2-3 of step i+1
     // (their LDS latency hides behind the first MFMAs of step i+1); issue the loads of step
-    // i+4 (activations, then weights) into the slots step i has freed.  Loads are issued in
+    // i+S (activations, then weights) into the slots step i has freed.  Loads are issued in
     // the order they are needed, so the in-order completion of loads never makes a wait
-    // drain a later step.  An item runs a whole number of 4-step groups: steps past k1 read
+    // drain a later step.  An item runs a whole number of S-step groups: steps past k1 read
     // clamped (valid) data and zero their activation fragments, so every step has the same
     // branch-free body.
-    static_assert(S == 4, "weight and activation rings of 4, LDS stages of 2");
+    static_assert(S % 2 == 0, "an even ring keeps the LDS stage parity of each slot fixed");
     auto issue = [&](auto slot, int ks) {
       issue_a(slot, ks);
       issue_w(slot, ks);
     };
-    static_for<4>([&](auto v) {  // same batch order as the loop, so every wait matches the steady state
+    static_for<S>([&](auto v) {  // same batch order as the loop, so every wait matches the steady state
       __builtin_amdgcn_sched_barrier(0);
       issue(v, k0 + v());
     });
@@ -796,13 +803,13 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(const uint16_t* __rest
     barrier();
     read(I0{}, I0{});
     read(I0{}, I2{});
-    const int n_steps = (k1 - k0 + 3) / 4 * 4;
+    const int n_steps = (k1 - k0 + S - 1) / S * S;
 #pragma clang loop unroll(disable)
-    for (int it = 0; it < n_steps; it += 4) {
-      static_for<4>([&](auto v) {
+    for (int it = 0; it < n_steps; it += S) {
+      static_for<S>([&](auto v) {
         constexpr int slot = v();
         using SL = std::integral_constant<int, slot>;
-        using NX = std::integral_constant<int, (slot + 1) % 4>;
+        using NX = std::integral_constant<int, (slot + 1) % S>;
         using P1 = std::integral_constant<int, (slot + 1) & 1>;
         const int i = k0 + it + v();
         if (i >= k1) static_for<4>([&](auto ss) { static_for<4>([&](auto mt) { af[ss()][mt()] = u32x4{}; }); });
@@ -813,7 +820,7 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(const uint16_t* __rest
         mfmas(SL{}, I2{});
         read(P1{}, I2{});
         __builtin_amdgcn_sched_barrier(0);  // keep the prefetch batch where it is issued
-        issue(SL{}, i + 4);
+        issue(SL{}, i + S);
         __builtin_amdgcn_sched_barrier(0);
       });
     }
