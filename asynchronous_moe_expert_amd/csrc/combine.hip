@@ -76,6 +76,10 @@ struct RowIO<uint16_t> {
 };
 
 constexpr int kCmbThreads = 256;
+#ifndef MOE_MERGE_THREADS
+#define MOE_MERGE_THREADS 256
+#endif
+constexpr int kMergeThreads = MOE_MERGE_THREADS;  // merge workgroup (one per arrival)
 constexpr int kMaxChain = 64;  // arrivals of one token handled per pass of the merge
 
 // Kernel 1: one thread per arrival.  Range and generation checks, then a push onto the
@@ -112,7 +116,7 @@ __global__ __launch_bounds__(256) void combine_link_kernel(int m, int K, int64_t
 // order in fp32, so results do not depend on scheduling.  acc[t] is only read while the
 // token holds earlier results (mask != 0): a fresh token starts from zero.
 template <typename TR, typename TO>
-__global__ __launch_bounds__(kCmbThreads) void combine_merge_kernel(
+__global__ __launch_bounds__(kMergeThreads) void combine_merge_kernel(
     int K, int H, const TR* __restrict__ rows, int64_t row_pitch, const int32_t* __restrict__ row_idx,
     const int32_t* __restrict__ tok, const int32_t* __restrict__ kslot, const float* __restrict__ wgt,
     float* __restrict__ acc, uint32_t* __restrict__ mask, uint32_t* __restrict__ tgen,
@@ -124,13 +128,56 @@ __global__ __launch_bounds__(kCmbThreads) void combine_merge_kernel(
   __shared__ uint32_t s_mask0, s_mask1;
   const int tid = threadIdx.x;
   const int i = blockIdx.x;
-  if (next[i] == -2) return;  // rejected by the range/generation checks
+  // everything indexed by the arrival in one round trip (all in range: i < m)
+  const int nx = next[i];
   const int t = tok[i];
+  const int j_i = kslot[i];
+  const float w_i = wgt[i];
+  const int64_t r_i = row_idx[i];
+  if (nx == -2) return;       // rejected by the range/generation checks
   if (head[t] != i) return;   // another arrival owns this token
   const uint32_t full = K >= 32 ? 0xffffffffu : ((1u << K) - 1u);
   float* a = acc + (int64_t)t * H;
   TO* o = out + (int64_t)t * out_pitch;
   const int nv = H >> 3;
+  if (nx == -1) {
+    // the token's only arrival of this call (every token of a prefill wave): no list to
+    // walk or sort, the same accept rule and the same fp32 operations as below
+    const uint32_t m_old = mask[t], bit = 1u << j_i;
+    const bool dup = (m_old & bit) != 0u;
+    const uint32_t m_new = m_old | bit;
+    const bool complete = !dup && m_new == full;
+    if (!dup) {
+      const bool started = m_old != 0u;
+      const TR* x_row = rows + r_i * row_pitch;
+      for (int v = tid; v < nv; v += kMergeThreads) {
+        float sum[8], x[8];
+        if (started) {
+          RowIO<float>::load8(a + v * 8, sum);
+        } else {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) sum[k] = 0.f;
+        }
+        RowIO<TR>::load8(x_row + v * 8, x);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sum[k] = fmaf(w_i, x[k], sum[k]);
+        if (complete) RowIO<TO>::store8(o + v * 8, sum);
+        else RowIO<float>::store8(a + v * 8, sum);
+      }
+    }
+    if (tid == 0) {
+      if (dup) atomicOr(err, MOE_ERR_DUPLICATE);
+      head[t] = -1;
+      if (complete) {
+        mask[t] = 0u;
+        tgen[t] = tgen[t] + 1u;
+        rflag[t] = 1;
+      } else {
+        mask[t] = m_new;
+      }
+    }
+    return;
+  }
   const int cursor = i;  // list head
   int lo = -1;      // arrivals with index <= lo are already merged
   bool have = false;  // acc values of this call live in `a` (not yet in registers)
@@ -190,7 +237,7 @@ __global__ __launch_bounds__(kCmbThreads) void combine_merge_kernel(
     const bool more = s_more;
     const uint32_t m_new = s_mask1;
     const bool complete = !more && m_new == full;
-    for (int v = tid; v < nv; v += kCmbThreads) {
+    for (int v = tid; v < nv; v += kMergeThreads) {
       float sum[8];
       if (started || have) {
         RowIO<float>::load8(a + v * 8, sum);
@@ -515,7 +562,7 @@ static void launch_apply(const moe_combine_args* a, hipStream_t stream) {
 template <typename TR, typename TO>
 static void launch_merge(const moe_combine_args* a, hipStream_t stream) {
   const moe_combine_state& s = a->state;
-  hipLaunchKernelGGL((combine_merge_kernel<TR, TO>), dim3((unsigned)a->m), dim3(kCmbThreads), 0, stream, a->K, s.H,
+  hipLaunchKernelGGL((combine_merge_kernel<TR, TO>), dim3((unsigned)a->m), dim3(kMergeThreads), 0, stream, a->K, s.H,
                      (const TR*)a->rows, a->row_pitch, a->row_idx, a->tok, a->kslot, a->w, s.acc, s.mask, s.tgen,
                      s.rflag, s.head, (const int32_t*)a->workspace, (TO*)a->out, a->out_pitch, a->err);
 }

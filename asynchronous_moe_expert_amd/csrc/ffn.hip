@@ -511,6 +511,14 @@ constexpr int gemm_stages() { return WDT == MOE_FP8_E4M3 ? MOE_FFN_GEMM_STAGES_F
 #endif
 constexpr bool kGemmChunkMajor = MOE_FFN_GEMM_CHUNK_MAJOR != 0;
 
+// s_waitcnt vmcnt(N) alone (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt
+// at their no-wait maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit count");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // weight fragments of one k-step for a wave's 2 column tiles (as loaded)
 template <int WDT>
 struct GemmW;
@@ -671,7 +679,17 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(const uint16_t* __rest
                                                        float* __restrict__ parts) {
   constexpr int S = gemm_stages<WDT>();
   constexpr int esz = WDT == MOE_FP8_E4M3 ? 1 : 2;
-  __shared__ u32x4 a_lds[2][kGemmBM * 8];  // activation k-tile, 2 stages of 16 KiB
+  // activation k-tiles, S stages of 16 KiB.  One array per stage: the compiler then tells
+  // the stages apart and makes an LDS read wait only for the copy into its own stage (with
+  // a single array it waits for every copy in flight, draining the load pipeline each step)
+  static_assert(S <= 4, "four stage arrays");
+  __shared__ u32x4 a_lds0[kGemmBM * 8], a_lds1[kGemmBM * 8], a_lds2[kGemmBM * 8], a_lds3[kGemmBM * 8];
+  auto stage = [&](auto st) -> u32x4* {
+    if constexpr (st() == 0) return a_lds0;
+    else if constexpr (st() == 1) return a_lds1;
+    else if constexpr (st() == 2) return a_lds2;
+    else return a_lds3;
+  };
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int KS = Kd / kBK;
@@ -717,11 +735,9 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(const uint16_t* __rest
       const int strip = colw / 16 + (MODE == 0 ? 2 * half + t() : 2 * t() + half);
       wvo[t()] = (int)(strip * strip_stride) + (32 * hf + r) * 16;
     });
-    // activation loads: instruction d of this wave fills the 16-byte slots (4wv + d)*64 + lane
-    // of a stage; slot P holds row P/8, 16-byte piece (P%8) ^ ((P/8 >> 1) & 7) of the row.
-    // Buffer loads (byte offset per lane, k-step in a scalar register) like the weights:
-    // the compiler then keeps the prologue's loads in program order, so the steady-state
-    // wait counts hold from the first k-step on.
+    // activation copies: instruction d of this wave fills the 16-byte slots (4wv + d)*64 + lane
+    // of a stage; slot P holds row P/8, 16-byte piece (P%8) ^ ((P/8 >> 1) & 7) of the row
+    // (byte offset per lane, k-step in a scalar register).
     // (with a gather, A is the pool: the host checks that it spans under 2 GiB)
     const __amdgpu_buffer_rsrc_t ars =
         buffer_rsrc(A, gr.perm ? gr.P * gr.pitch * 2 : (int64_t)n_rows * Kd * 2);
@@ -736,60 +752,63 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(const uint16_t* __rest
     static_for<4>([&](auto i) { static_for<2>([&](auto jj) { acc[i()][jj()] = f32x16{}; }); });
 
     GemmW<WDT> wr[S];   // weight fragments of steps i .. i+S-1
-    u32x4 ar[S][4];     // this thread's activation pieces of steps i+1 .. i+S
     u32x4 af[4][4];     // activation fragments [k-slice s][mt] of the step being computed
-    auto issue_a = [&](auto aslot, int ks) {
+    // activations of step ks go straight from global memory into LDS stage slot (16 bytes
+    // per lane at the instruction's base + 16 lane, i.e. exactly the slot order above)
+    auto issue_a = [&](auto slot, int ks) {
       ks = min(ks, k1 - 1);
-      static_for<4>([&](auto d) { ar[aslot()][d()] = __builtin_amdgcn_raw_buffer_load_b128(ars, avo[d()], ks * kBK * 2, 0); });
+      static_for<4>([&](auto d) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ars, (__attribute__((address_space(3))) void*)(stage(slot) + (wv * 4 + d()) * 64), 16, avo[d()],
+            ks * kBK * 2, 0, 0);
+      });
     };
     auto issue_w = [&](auto slot, int ks) { wr[slot()].load(wrs, wvo, min(ks, k1 - 1) * 1024 * esz); };
-    // park this thread's pieces of a step in LDS; the compiler waits for their loads only
-    // (loads retire in order and the weights of the same step were issued after them)
-    auto park = [&](auto aslot, auto stg) {
-      static_for<4>([&](auto d) { a_lds[stg()][(wv * 4 + d()) * 64 + lane] = ar[aslot()][d()]; });
-    };
+    // Workgroup barrier for the copy pipeline.  Before it this wave's LDS reads are complete
+    // (so after it no wave still reads a stage a copy may refill) and the caller has waited
+    // for its own copies with an explicit vmcnt; a release fence here would also wait for
+    // every copy still in flight, draining the pipeline.  The acquire fence keeps the LDS
+    // reads after the barrier.
     auto barrier = [&]() {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     };
-    auto read = [&](auto stg, auto s_lo) {  // fragments of k-slices s_lo, s_lo + 1
-      const u32x4* tile = a_lds[stg()];
-      static_for<2>([&](auto ds) {
-        static_for<4>([&](auto mt) {
-          constexpr int ss = s_lo() + ds();
-          const int row = mt() * 32 + l32, kq = 4 * hf + ss;
-          af[ss][mt()] = tile[row * 8 + (kq ^ ((row >> 1) & 7))];
-        });
+    auto read1 = [&](auto stg, auto ss) {  // fragments of k-slice ss
+      const u32x4* tile = stage(stg);
+      static_for<4>([&](auto mt) {
+        const int row = mt() * 32 + l32, kq = 4 * hf + ss();
+        af[ss()][mt()] = tile[row * 8 + (kq ^ ((row >> 1) & 7))];
       });
     };
-    auto mfmas = [&](auto slot, auto s_lo) {  // MFMAs of k-slices s_lo, s_lo + 1
-      static_for<2>([&](auto ds) {
-        constexpr int ss = s_lo() + ds();
-        bf16x8 bw[2];
-        static_for<2>([&](auto t) { bw[t()] = wr[slot()].frag(t(), ss); });
-        static_for<4>([&](auto mt) {
-          bf16x8 a;
-          __builtin_memcpy(&a, &af[ss][mt()], 16);
-          static_for<2>([&](auto t) {
-            acc[mt()][t()] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bw[t()], acc[mt()][t()], 0, 0, 0);
-          });
+    auto mfma1 = [&](auto slot, auto ss) {  // MFMAs of k-slice ss
+      bf16x8 bw[2];
+      static_for<2>([&](auto t) { bw[t()] = wr[slot()].frag(t(), ss()); });
+      static_for<4>([&](auto mt) {
+        bf16x8 a;
+        __builtin_memcpy(&a, &af[ss()][mt()], 16);
+        static_for<2>([&](auto t) {
+          acc[mt()][t()] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bw[t()], acc[mt()][t()], 0, 0, 0);
         });
       });
     };
     using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
-    // Software pipeline over k-steps i = k0, k0+1, ... (weight and activation slot
-    // (i - k0) % S, LDS stage (i - k0) % 2).  Step i: MFMAs of slices 0-1 of step i; park the
-    // activation pieces of step i+1 in LDS and barrier; read slices 0-1 of step i+1 into the
-    // registers just freed; MFMAs of slices 2-3 of step i; read slices 2-3 of step i+1
-    // (their LDS latency hides behind the first MFMAs of step i+1); issue the loads of step
-    // i+S (activations, then weights) into the slots step i has freed.  Loads are issued in
-    // the order they are needed, so the in-order completion of loads never makes a wait
-    // drain a later step.  An item runs a whole number of S-step groups: steps past k1 read
-    // clamped (valid) data and zero their activation fragments, so every step has the same
-    // branch-free body.
-    static_assert(S % 2 == 0, "an even ring keeps the LDS stage parity of each slot fixed");
+    using I3 = std::integral_constant<int, 3>;
+    // Software pipeline over k-steps i = k0, k0+1, ... (weight slot and LDS stage (i - k0) % S).
+    // Step i: MFMAs of slice 0 of step i; wait until this wave's activation copy of step i+1
+    // has landed in LDS, barrier (then every wave's has, and every wave has finished
+    // reading the stage of step i); copy the activations of step i+S into that stage; then
+    // for s = 0..3 read slice s of step i+1 and run the MFMAs of slice s+1 of step i, so each
+    // LDS read has three slices of MFMAs to land in; finally load the weights of step i+S
+    // into the slot step i's MFMAs have released.  Loads are issued in the order they are
+    // needed.  The waits for the copies are explicit vmcnt counts (behind the copy of step
+    // i+1 are the weights of i+1 and the S-2 later batches).  An item runs a whole number of
+    // S-step groups: steps past k1 load clamped (valid) data and zero their activation
+    // fragments, so every step has the same branch-free body.
+    static_assert(S >= 2, "a ring of at least two stages");
+    constexpr int kA = 4, kW = GemmW<WDT>::kLoads;
     auto issue = [&](auto slot, int ks) {
       issue_a(slot, ks);
       issue_w(slot, ks);
@@ -799,10 +818,13 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(const uint16_t* __rest
       issue(v, k0 + v());
     });
     __builtin_amdgcn_sched_barrier(0);
-    park(I0{}, I0{});
+    wait_vmcnt<kW + (S - 1) * (kA + kW)>();  // the copy of step k0
     barrier();
-    read(I0{}, I0{});
-    read(I0{}, I2{});
+    __builtin_amdgcn_sched_barrier(0);
+    read1(I0{}, I0{});
+    read1(I0{}, I1{});
+    read1(I0{}, I2{});
+    read1(I0{}, I3{});
     const int n_steps = (k1 - k0 + S - 1) / S * S;
 #pragma clang loop unroll(disable)
     for (int it = 0; it < n_steps; it += S) {
@@ -810,21 +832,34 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(const uint16_t* __rest
         constexpr int slot = v();
         using SL = std::integral_constant<int, slot>;
         using NX = std::integral_constant<int, (slot + 1) % S>;
-        using P1 = std::integral_constant<int, (slot + 1) & 1>;
         const int i = k0 + it + v();
         if (i >= k1) static_for<4>([&](auto ss) { static_for<4>([&](auto mt) { af[ss()][mt()] = u32x4{}; }); });
-        mfmas(SL{}, I0{});
-        park(NX{}, P1{});
+        mfma1(SL{}, I0{});
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<kW + (S - 2) * (kA + kW)>();  // the copy of step i+1
         barrier();
-        read(P1{}, I0{});
-        mfmas(SL{}, I2{});
-        read(P1{}, I2{});
-        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch batch where it is issued
-        issue(SL{}, i + S);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_a(SL{}, i + S);  // the stage of step i is free now (no LDS reads pending)
+        __builtin_amdgcn_sched_barrier(0);
+        read1(NX{}, I0{});
+        mfma1(SL{}, I1{});
+        __builtin_amdgcn_sched_barrier(0);
+        read1(NX{}, I1{});
+        mfma1(SL{}, I2{});
+        __builtin_amdgcn_sched_barrier(0);
+        read1(NX{}, I2{});
+        mfma1(SL{}, I3{});
+        __builtin_amdgcn_sched_barrier(0);
+        read1(NX{}, I3{});
+        __builtin_amdgcn_sched_barrier(0);
+        issue_w(SL{}, i + S);  // weight slot of step i is free after its last MFMAs
         __builtin_amdgcn_sched_barrier(0);
       });
     }
-    barrier();  // the next item's first LDS writes wait for this item's last reads
+    // no copy may still be in flight into a stage the next item's prologue fills, and the
+    // next item's copies wait for this item's last LDS reads
+    wait_vmcnt<0>();
+    barrier();
     if (!wact) continue;
     if (piece)
       store_partial(acc, parts + (int64_t)b * kGemmPartFloats, tid);
