@@ -38,15 +38,32 @@ __global__ __launch_bounds__(kAsmThreads) void assemble_index_kernel(
   if (tid == 0) s_err = 0u;
   __syncthreads();
 
-  // pass 1: validate and count
+  // pass 1: validate and count.  key = local expert, or kMaxElocAsm for a rejected pair or
+  // past the end; the keys of the first kCached chunks stay in registers for pass 2 (one
+  // global round trip per chunk fewer)
+  constexpr int kCached = 8;
   unsigned myerr = 0u;
-  for (int i = tid; i < n; i += kAsmThreads) {
-    const int64_t s = slot[i];
-    const int e = expert[i] - base;
-    bool ok = true;
-    if (s < 0 || s >= P) { myerr |= MOE_ERR_SLOT_RANGE; ok = false; }
-    if (e < 0 || e >= E_loc) { myerr |= MOE_ERR_EXPERT_NONLOCAL; ok = false; }
-    if (ok) atomicAdd(&s_run[e], 1);
+  auto key_of = [&](int i) {
+    int key = kMaxElocAsm;
+    if (i < n) {
+      const int64_t s = slot[i];
+      const int e = expert[i] - base;
+      bool ok = true;
+      if (s < 0 || s >= P) { myerr |= MOE_ERR_SLOT_RANGE; ok = false; }
+      if (e < 0 || e >= E_loc) { myerr |= MOE_ERR_EXPERT_NONLOCAL; ok = false; }
+      if (ok) key = e;
+    }
+    return key;
+  };
+  int kc[kCached];
+#pragma unroll
+  for (int c = 0; c < kCached; ++c) {
+    kc[c] = key_of(c * kAsmThreads + tid);
+    if (kc[c] < kMaxElocAsm) atomicAdd(&s_run[kc[c]], 1);
+  }
+  for (int i = kCached * kAsmThreads + tid; i < n; i += kAsmThreads) {
+    const int key = key_of(i);
+    if (key < kMaxElocAsm) atomicAdd(&s_run[key], 1);
   }
   if (myerr) atomicOr(&s_err, myerr);
   __syncthreads();
@@ -85,14 +102,7 @@ __global__ __launch_bounds__(kAsmThreads) void assemble_index_kernel(
   __syncthreads();
 
   // pass 2: stable scatter, one chunk of kAsmThreads queue entries at a time
-  for (int c0 = 0; c0 < n; c0 += kAsmThreads) {
-    const int i = c0 + tid;
-    int key = kMaxElocAsm;  // "rejected / past the end" key
-    if (i < n) {
-      const int64_t s = slot[i];
-      const int e = expert[i] - base;
-      if (s >= 0 && s < P && e >= 0 && e < E_loc) key = e;
-    }
+  auto scatter = [&](int i, int key) {
     for (int x = tid; x < kAsmWaves * E_loc; x += kAsmThreads) s_wcnt[x / E_loc][x % E_loc] = 0;
     __syncthreads();
     uint64_t peers = ~0ull;
@@ -124,6 +134,19 @@ __global__ __launch_bounds__(kAsmThreads) void assemble_index_kernel(
       pos[i] = -1;
     }
     __syncthreads();
+  };
+#pragma unroll
+  for (int c = 0; c < kCached; ++c)
+    if (c * kAsmThreads < n) scatter(c * kAsmThreads + tid, kc[c]);
+  for (int c0 = kCached * kAsmThreads; c0 < n; c0 += kAsmThreads) {
+    const int i = c0 + tid;
+    int key = kMaxElocAsm;  // "rejected / past the end" key
+    if (i < n) {
+      const int64_t s = slot[i];
+      const int e = expert[i] - base;
+      if (s >= 0 && s < P && e >= 0 && e < E_loc) key = e;
+    }
+    scatter(i, key);
   }
   for (int r = s_total + tid; r < n; r += kAsmThreads) perm[r] = -1;
   if (tid == 0 && s_err) atomicOr(err, s_err);

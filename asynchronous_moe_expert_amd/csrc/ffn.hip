@@ -498,9 +498,9 @@ static void launch_mfma_t(const void* A, const int32_t* offsets, int E_loc, cons
 constexpr int kGemmBM = 128;
 constexpr int kGemmWaveN = 64;
 constexpr int kGemmBN = kGemmWaveN * kFfnWaves;
-// register-ring depth (k-steps of loads in flight + 1).  A 6-deep ring for fp8 weights
-// (500 VGPRs; 8 spills) measured no faster than 4: the CU's outstanding-request limit, not
-// the wave's prefetch distance, bounds the loads in flight
+// ring depth (k-steps of loads in flight + 1; LDS stages and weight register slots).  With
+// fp8 weights 6 and 8 stages fit (456 and 504 VGPRs, 96 and 128 KiB LDS) but measured
+// 2-7% slower than 4
 #ifndef MOE_FFN_GEMM_STAGES_FP8
 #define MOE_FFN_GEMM_STAGES_FP8 4
 #endif

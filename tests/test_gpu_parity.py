@@ -36,6 +36,7 @@ ASM_CASES = [
     (1025, 3, 0, 300, 64, "bf16", 0, 0.1),
     (3000, 256, 0, 5000, 64, "bf16", 0, 0.02),
     (5000, 32, 64, 9000, 2880, "bf16", 0, 0.0),
+    (9000, 16, 0, 12000, 64, "bf16", 0, 0.05),   # past the 8 chunks whose keys stay in registers
 ]
 
 
