@@ -186,12 +186,7 @@ def main() -> int:
         ev.record(e_end[s], stream)
 
     if args.calibration_copy:
-        src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calibration_copy(dev)
     for s in range(W_steps):
         step(s)
     torch.cuda.synchronize()
@@ -378,6 +373,19 @@ def cpu_baseline_prefill(setup, b, seconds: float) -> dict:
                       f"(assemble and combine are a small share of the oracle's time), {el:.1f} s"}
 
 
+def calibration_copy(dev) -> None:
+    """One device-to-device copy of CALIB_BYTES: the reference dispatch that scales the
+    rocprofv3 byte counters of the same run to bytes."""
+    import torch
+
+    src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def run_prefill(args) -> int:
     """Prefill-shaped rank share: each of the four waves is one step (assemble, FFN,
     combine of the local result into tokens whose 7 remote results were delivered first)."""
@@ -413,6 +421,8 @@ def run_prefill(args) -> int:
     names = ["assemble", "gate_up", "down", "combine"]
     times = {w: {k: [] for k in names} for w in range(nw)}
     evs = [ev.create() for _ in range(5)]
+    if args.calibration_copy:
+        calibration_copy(dev)
     for rep in range(W_reps + reps):
         for w, b in enumerate(waves):
             d = dw[w]
