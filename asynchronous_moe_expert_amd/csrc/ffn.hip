@@ -506,10 +506,6 @@ constexpr int kGemmBN = kGemmWaveN * kFfnWaves;
 #endif
 template <int WDT>
 constexpr int gemm_stages() { return WDT == MOE_FP8_E4M3 ? MOE_FFN_GEMM_STAGES_FP8 : 4; }
-#ifndef MOE_FFN_GEMM_CHUNK_MAJOR
-#define MOE_FFN_GEMM_CHUNK_MAJOR 1
-#endif
-constexpr bool kGemmChunkMajor = MOE_FFN_GEMM_CHUNK_MAJOR != 0;
 
 // s_waitcnt vmcnt(N) alone (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt
 // at their no-wait maxima)
@@ -589,15 +585,13 @@ struct GemmSplit {
   }
 };
 
-// chunk and column block of unit u (units are chunk-major or column-block-major)
-__device__ __forceinline__ void gemm_unit_coords(int u, int total, int n_blocks_N, int& c, int& nb) {
-  if (kGemmChunkMajor) {
-    c = u / n_blocks_N;
-    nb = u - c * n_blocks_N;
-  } else {
-    nb = u / total;
-    c = u - nb * total;
-  }
+// chunk and column block of unit u (chunk-major: the column blocks of a chunk are
+// neighbours, so an XCD's concurrent workgroups share the chunk's activation tile).  Tiles of
+// 4 chunks x 8 blocks per expert, which also share each weight tile among 4 chunks, measured
+// no faster.
+__device__ __forceinline__ void gemm_unit_coords(int u, int n_blocks_N, int& c, int& nb) {
+  c = u / n_blocks_N;
+  nb = u - c * n_blocks_N;
 }
 
 // Epilogue of a 128 x 256 unit; accumulator v of lane l holds column l%32 and row
@@ -718,7 +712,7 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(const uint16_t* __rest
       k1 = (pc + 1) * KS / sp.S;
     }
     int c, nb, e, m0, mend;
-    gemm_unit_coords(u, total, n_blocks_N, c, nb);
+    gemm_unit_coords(u, n_blocks_N, c, nb);
     tab.find(c, kGemmBM, e, m0, mend);
     if (e < 0) break;  // not reachable: every unit id below U names a chunk
     const int col0 = nb * kGemmBN + wv * kGemmWaveN;
@@ -891,7 +885,7 @@ __global__ __launch_bounds__(256) void ffn_gemm_finalize_kernel(const int32_t* _
   sp.init(tab.total * n_blocks_N, G, xcd, KS, true);
   if (sp.S < 2 || t >= sp.T) return;
   int c, nb, e, m0, mend;
-  gemm_unit_coords(sp.u0 + sp.R * sp.Gx + t, tab.total, n_blocks_N, c, nb);
+  gemm_unit_coords(sp.u0 + sp.R * sp.Gx + t, n_blocks_N, c, nb);
   tab.find(c, kGemmBM, e, m0, mend);
   const int col0 = nb * kGemmBN + wv * kGemmWaveN;
   if (e < 0 || col0 >= Nw || m0 + mt * 32 >= mend) return;  // (no barriers: waves leave independently)
