@@ -59,6 +59,13 @@ def test_workspace_size(lib):
     assert M.moe_ffn_workspace_size(64, 8, 64, 128, M.MOE_F32) == 64 * 128 * 4
     assert M.moe_ffn_workspace_size(3, 1, 64, 64, M.MOE_BF16) == 512  # rounded up to 256 B
     assert M.moe_ffn_workspace_size(1, 1, 64, 64, 7) == 0
+    # batches that can take the tiled GEMM path (>= 96 rows per local expert, bf16 activations)
+    # also hold 256 fp32 partial tiles of 128 KiB for the split tail units
+    parts = 256 * 128 * 1024
+    assert M.moe_ffn_workspace_size(6554, 32, 4096, 2048, M.MOE_BF16) == 6554 * 2048 * 2 + parts
+    assert M.moe_ffn_workspace_size(96 * 32, 32, 4096, 2048, M.MOE_BF16) == 96 * 32 * 2048 * 2 + parts
+    assert M.moe_ffn_workspace_size(96 * 32 - 1, 32, 4096, 2048, M.MOE_BF16) == (96 * 32 - 1) * 2048 * 2
+    assert M.moe_ffn_workspace_size(4096, 8, 64, 128, M.MOE_F32) == 4096 * 128 * 4  # fp32 path: no GEMM
     # plan path: a 16-byte header, a 16-byte record and an 8-byte list entry per arrival
     assert M.moe_combine_workspace_size(256) == 6160 and M.moe_combine_workspace_size(3) == 96
 
