@@ -29,7 +29,8 @@ _i64 = C.c_int64
 class AssembleArgs(C.Structure):
     _fields_ = [("n", _i32), ("slot", _p), ("expert", _p), ("expert_base", _i32), ("E_loc", _i32),
                 ("pool", _p), ("P", _i64), ("pool_pitch", _i64), ("H", _i32), ("act_dtype", _i32),
-                ("perm", _p), ("pos", _p), ("counts", _p), ("offsets", _p), ("xb", _p), ("err", _p)]
+                ("perm", _p), ("pos", _p), ("counts", _p), ("offsets", _p), ("xb", _p), ("err", _p),
+                ("row_slot", _p)]
 
 
 class PackArgs(C.Structure):
@@ -41,7 +42,7 @@ class FfnArgs(C.Structure):
     _fields_ = [("n", _i32), ("E_loc", _i32), ("H", _i32), ("I", _i32), ("act_dtype", _i32), ("w_dtype", _i32),
                 ("xb", _p), ("offsets", _p), ("w_gu", _p), ("w_d", _p), ("s_gate", _p), ("s_up", _p),
                 ("s_down", _p), ("y", _p), ("workspace", _p), ("workspace_bytes", C.c_size_t), ("ev_mid", _p),
-                ("perm", _p), ("slot", _p), ("pool", _p), ("P", _i64), ("pool_pitch", _i64)]
+                ("perm", _p), ("slot", _p), ("pool", _p), ("P", _i64), ("pool_pitch", _i64), ("row_slot", _p)]
 
 
 class StateC(C.Structure):
@@ -145,12 +146,13 @@ def moe_ffn_workspace_size(n_max: int, E_loc: int, H: int, I: int, act_dtype: in
 
 
 def moe_assemble(slot, expert, expert_base: int, E_loc: int, pool, perm, pos, counts, offsets, xb, err,
-                 n: int | None = None, stream=None) -> None:
-    """pool: [P][pitch] (f32 or bf16); xb: [>= n][H] of the same dtype."""
+                 n: int | None = None, stream=None, row_slot=None) -> None:
+    """pool: [P][pitch] (f32 or bf16); xb: [>= n][H] of the same dtype (or None);
+    row_slot: optional [>= n] int32 output, the pool slot of each batch row."""
     H = pool.shape[1] if xb is None else xb.shape[1]
     a = AssembleArgs(int(slot.numel() if n is None else n), _ptr(slot), _ptr(expert), expert_base, E_loc,
                      _ptr(pool), pool.shape[0], pool.stride(0), H, dtype_code(pool), _ptr(perm),
-                     _ptr(pos), _ptr(counts), _ptr(offsets), _ptr(xb), _ptr(err))
+                     _ptr(pos), _ptr(counts), _ptr(offsets), _ptr(xb), _ptr(err), _ptr(row_slot))
     _check(load().moe_assemble(C.byref(a), _stream(stream)), "moe_assemble")
 
 
@@ -163,15 +165,18 @@ def moe_pack_ffn_weights(wg, wu, wd, w_gu, w_d, w_dtype: int, stream=None) -> No
 def moe_expert_ffn_grouped(n: int, E_loc: int, H: int, I: int, act_dtype: int, w_dtype: int, xb, offsets, w_gu,
                            w_d, y, workspace, s_gate=None, s_up=None, s_down=None, ev_mid: int | None = None,
                            stream=None, gather=None) -> None:
-    """gather=(perm, slot, pool): read batch rows from the pool (gather-on-load); xb may be None."""
-    perm = slot = pool = None
+    """gather=(perm, slot, pool) or (perm, slot, pool, row_slot): read batch rows from the pool
+    (gather-on-load; with row_slot, pool row row_slot[r] and perm/slot unused); xb may be None."""
+    perm = slot = pool = row_slot = None
     P = pitch = 0
     if gather is not None:
-        perm, slot, pool = gather
+        perm, slot, pool = gather[:3]
+        row_slot = gather[3] if len(gather) > 3 else None
         P, pitch = pool.shape[0], pool.stride(0)
     a = FfnArgs(n, E_loc, H, I, act_dtype, w_dtype, _ptr(xb), _ptr(offsets), _ptr(w_gu), _ptr(w_d),
                 _ptr(s_gate), _ptr(s_up), _ptr(s_down), _ptr(y), _ptr(workspace),
-                workspace.numel() * workspace.element_size(), ev_mid, _ptr(perm), _ptr(slot), _ptr(pool), P, pitch)
+                workspace.numel() * workspace.element_size(), ev_mid, _ptr(perm), _ptr(slot), _ptr(pool), P, pitch,
+                _ptr(row_slot))
     _check(load().moe_expert_ffn_grouped(C.byref(a), _stream(stream)), "moe_expert_ffn_grouped")
 
 

@@ -25,8 +25,8 @@ constexpr int kMaxElocAsm = 256;
 template <int kAsmThreads>
 __global__ __launch_bounds__(kAsmThreads) void assemble_index_kernel(
     int n, const int32_t* __restrict__ slot, const int32_t* __restrict__ expert, int base, int E_loc, int64_t P,
-    int32_t* __restrict__ perm, int32_t* __restrict__ pos, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, uint32_t* __restrict__ err) {
+    int32_t* __restrict__ perm, int32_t* __restrict__ pos, int32_t* __restrict__ row_slot,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, uint32_t* __restrict__ err) {
   constexpr int kAsmWaves = kAsmThreads / kWave;
   __shared__ int s_run[kMaxElocAsm];
   __shared__ int s_wcnt[kAsmWaves][kMaxElocAsm + 1];
@@ -39,14 +39,16 @@ __global__ __launch_bounds__(kAsmThreads) void assemble_index_kernel(
   __syncthreads();
 
   // pass 1: validate and count.  key = local expert, or kMaxElocAsm for a rejected pair or
-  // past the end; the keys of the first kCached chunks stay in registers for pass 2 (one
-  // global round trip per chunk fewer)
+  // past the end; the keys (and slots) of the first kCached chunks stay in registers for
+  // pass 2 (one global round trip per chunk fewer)
   constexpr int kCached = 8;
   unsigned myerr = 0u;
-  auto key_of = [&](int i) {
+  auto key_of = [&](int i, int& sv) {
     int key = kMaxElocAsm;
+    sv = 0;
     if (i < n) {
       const int64_t s = slot[i];
+      sv = (int)s;
       const int e = expert[i] - base;
       bool ok = true;
       if (s < 0 || s >= P) { myerr |= MOE_ERR_SLOT_RANGE; ok = false; }
@@ -55,14 +57,15 @@ __global__ __launch_bounds__(kAsmThreads) void assemble_index_kernel(
     }
     return key;
   };
-  int kc[kCached];
+  int kc[kCached], ks[kCached];
 #pragma unroll
   for (int c = 0; c < kCached; ++c) {
-    kc[c] = key_of(c * kAsmThreads + tid);
+    kc[c] = key_of(c * kAsmThreads + tid, ks[c]);
     if (kc[c] < kMaxElocAsm) atomicAdd(&s_run[kc[c]], 1);
   }
   for (int i = kCached * kAsmThreads + tid; i < n; i += kAsmThreads) {
-    const int key = key_of(i);
+    int sv;
+    const int key = key_of(i, sv);
     if (key < kMaxElocAsm) atomicAdd(&s_run[key], 1);
   }
   if (myerr) atomicOr(&s_err, myerr);
@@ -102,7 +105,7 @@ __global__ __launch_bounds__(kAsmThreads) void assemble_index_kernel(
   __syncthreads();
 
   // pass 2: stable scatter, one chunk of kAsmThreads queue entries at a time
-  auto scatter = [&](int i, int key) {
+  auto scatter = [&](int i, int key, int sv) {
     for (int x = tid; x < kAsmWaves * E_loc; x += kAsmThreads) s_wcnt[x / E_loc][x % E_loc] = 0;
     __syncthreads();
     uint64_t peers = ~0ull;
@@ -130,6 +133,7 @@ __global__ __launch_bounds__(kAsmThreads) void assemble_index_kernel(
       const int r = s_wcnt[wv][key] + rank;
       perm[r] = i;
       if (pos) pos[i] = r;
+      if (row_slot) row_slot[r] = sv;
     } else if (i < n && pos) {
       pos[i] = -1;
     }
@@ -137,18 +141,23 @@ __global__ __launch_bounds__(kAsmThreads) void assemble_index_kernel(
   };
 #pragma unroll
   for (int c = 0; c < kCached; ++c)
-    if (c * kAsmThreads < n) scatter(c * kAsmThreads + tid, kc[c]);
+    if (c * kAsmThreads < n) scatter(c * kAsmThreads + tid, kc[c], ks[c]);
   for (int c0 = kCached * kAsmThreads; c0 < n; c0 += kAsmThreads) {
     const int i = c0 + tid;
     int key = kMaxElocAsm;  // "rejected / past the end" key
+    int sv = 0;
     if (i < n) {
       const int64_t s = slot[i];
       const int e = expert[i] - base;
+      sv = (int)s;
       if (s >= 0 && s < P && e >= 0 && e < E_loc) key = e;
     }
-    scatter(i, key);
+    scatter(i, key, sv);
   }
-  for (int r = s_total + tid; r < n; r += kAsmThreads) perm[r] = -1;
+  for (int r = s_total + tid; r < n; r += kAsmThreads) {
+    perm[r] = -1;
+    if (row_slot) row_slot[r] = -1;
+  }
   if (tid == 0 && s_err) atomicOr(err, s_err);
 }
 
@@ -188,10 +197,10 @@ extern "C" int moe_assemble(const moe_assemble_args* a, hipStream_t stream) {
   }
   if (a->n <= 256)
     hipLaunchKernelGGL(assemble_index_kernel<256>, dim3(1), dim3(256), 0, stream, a->n, a->slot, a->expert,
-                       a->expert_base, a->E_loc, a->P, a->perm, a->pos, a->counts, a->offsets, a->err);
+                       a->expert_base, a->E_loc, a->P, a->perm, a->pos, a->row_slot, a->counts, a->offsets, a->err);
   else
     hipLaunchKernelGGL(assemble_index_kernel<1024>, dim3(1), dim3(1024), 0, stream, a->n, a->slot, a->expert,
-                       a->expert_base, a->E_loc, a->P, a->perm, a->pos, a->counts, a->offsets, a->err);
+                       a->expert_base, a->E_loc, a->P, a->perm, a->pos, a->row_slot, a->counts, a->offsets, a->err);
   if (a->n == 0 || !a->xb) return launch_status();  // no xb: the FFN gathers on load
   const int cpr = row_bytes / 16;
   const int64_t work = (int64_t)a->n * cpr;

@@ -61,17 +61,24 @@ __global__ __launch_bounds__(256) void pack_kernel(const T* __restrict__ src, T*
 // ------------------------------------------------------------- gather-on-load rows
 // Where batch row r's activations live.  Without a gather (perm == nullptr) they are row r
 // of the batch matrix A ([n][Kd]).  With one, A is the token pool and row r is pool row
-// slot[perm[r]] (clamped into [0, P): a pair moe_assemble rejected has no batch row, so
-// the clamps only guard against inconsistent inputs), pitch `pitch` elements.
+// row_slot[r] when that index is given, else slot[perm[r]] (clamped into [0, P): a pair
+// moe_assemble rejected has no batch row, so the clamps only guard against inconsistent
+// inputs), pitch `pitch` elements.  perm marks the gather; with row_slot it is not read.
 struct GatherRows {
   const int32_t* perm;
   const int32_t* slot;
   int64_t pitch;
   int64_t P;
+  const int32_t* row_slot;
   __device__ __forceinline__ int64_t row_offset(int r, int Kd) const {
     if (perm == nullptr) return (int64_t)r * Kd;
-    const int q = perm[r];
-    int64_t s = slot[q < 0 ? 0 : q];
+    int64_t s;
+    if (row_slot != nullptr) {
+      s = row_slot[r];
+    } else {
+      const int q = perm[r];
+      s = slot[q < 0 ? 0 : q];
+    }
     s = s < 0 ? 0 : (s >= P ? P - 1 : s);
     return s * pitch;
   }
@@ -1048,21 +1055,22 @@ extern "C" int moe_expert_ffn_grouped(const moe_ffn_args* a, hipStream_t stream)
     return MOE_OK;
   }
   // the rows the gate/up projection reads: the batch xb, or pool rows through the queue
-  GatherRows gr{nullptr, nullptr, 0, 0};
+  GatherRows gr{nullptr, nullptr, 0, 0, nullptr};
   const void* x_src = a->xb;
-  if (a->perm) {
+  if (a->perm || a->row_slot) {
     const int esz = dtype_size(a->act_dtype);
-    if (!a->slot || !a->pool) return MOE_EINVAL_NULL;
+    if ((!a->row_slot && !a->slot) || !a->pool) return MOE_EINVAL_NULL;
     if (a->P < 1 || a->pool_pitch < a->H) return MOE_EINVAL_SIZE;
     if (!f32 && (double)a->P * (double)a->pool_pitch * esz >= 2147483648.0) return MOE_EINVAL_SIZE;
     if (!aligned16(a->pool) || (a->pool_pitch * esz) % 16) return MOE_EINVAL_ALIGN;
-    gr = GatherRows{a->perm, a->slot, a->pool_pitch, a->P};
+    // (perm only marks the gather when row_slot is given; it is then never read)
+    gr = GatherRows{a->perm ? a->perm : a->row_slot, a->slot, a->pool_pitch, a->P, a->row_slot};
     x_src = a->pool;
   }
   if (!x_src || !a->w_gu || !a->w_d || !a->y) return MOE_EINVAL_NULL;
   if (f8 && (!a->s_gate || !a->s_up || !a->s_down)) return MOE_EINVAL_NULL;
   if (!aligned16(x_src) || !aligned16(a->w_gu) || !aligned16(a->w_d) || !aligned16(a->y)) return MOE_EINVAL_ALIGN;
-  const GatherRows none{nullptr, nullptr, 0, 0};
+  const GatherRows none{nullptr, nullptr, 0, 0, nullptr};
   // h is required; the partial area after it is optional (see below)
   if (!a->workspace || a->workspace_bytes < h_bytes(a->n, a->I, dtype_size(a->act_dtype))) return MOE_EWORKSPACE;
   if (!aligned16(a->workspace)) return MOE_EINVAL_ALIGN;

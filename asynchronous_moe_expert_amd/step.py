@@ -35,6 +35,7 @@ class ExpertStep:
         nm = max(n_max, 1)
         self.perm = torch.empty(nm, dtype=torch.int32, device=dev)
         self.pos = torch.empty(nm, dtype=torch.int32, device=dev)
+        self.row_slot = torch.empty(nm, dtype=torch.int32, device=dev)  # pool slot of each batch row
         self.counts = torch.empty(E_loc, dtype=torch.int32, device=dev)
         self.offsets = torch.empty(E_loc + 1, dtype=torch.int32, device=dev)
         self.xb = torch.empty((nm, H), dtype=adt, device=dev)
@@ -50,7 +51,7 @@ class ExpertStep:
         self.out = torch.empty((T_cap, H), dtype=adt, device=dev)
         self.w_gu = self.w_d = None
         self.gather_on_load = gather_on_load
-        self._gather = None  # (perm, slot, pool) of the last assemble when gathering on load
+        self._gather = None  # (perm, slot, pool, row_slot) of the last assemble when gathering on load
         self.side = torch.cuda.Stream(device=dev) if overlap else None
         self._ev_asm = torch.cuda.Event() if overlap else None
         self._ev_plan = torch.cuda.Event() if overlap else None
@@ -67,9 +68,10 @@ class ExpertStep:
 
     def assemble(self, slot, expert, expert_base: int, pool, n: int | None = None, stream=None) -> None:
         xb = None if self.gather_on_load else self.xb
+        rs = self.row_slot if self.gather_on_load else None
         N.moe_assemble(slot, expert, expert_base, self.E_loc, pool, self.perm, self.pos, self.counts, self.offsets,
-                       xb, self.err, n=n, stream=stream)
-        self._gather = (self.perm, slot, pool) if self.gather_on_load else None
+                       xb, self.err, n=n, stream=stream, row_slot=rs)
+        self._gather = (self.perm, slot, pool, rs) if self.gather_on_load else None
 
     def ffn(self, n: int, ev_mid: int | None = None, stream=None) -> None:
         N.moe_expert_ffn_grouped(n, self.E_loc, self.H, self.I, self.act_dtype, self.w_dtype, self.xb, self.offsets,

@@ -111,6 +111,8 @@ typedef struct moe_assemble_args {
   int32_t* offsets;        /* out [E_loc + 1] */
   void* xb;                /* out [n][H], optional */
   uint32_t* err;           /* device error word (OR-ed) */
+  int32_t* row_slot;       /* out [n], optional: pool slot of batch row r (slot[perm[r]]), -1 past the
+                              accepted pairs; the FFN's gather-on-load reads it in one step */
 } moe_assemble_args;
 
 int moe_assemble(const moe_assemble_args* args, hipStream_t stream);
@@ -166,6 +168,8 @@ int moe_pack_ffn_weights(const moe_pack_args* args, hipStream_t stream);
  * elements), and xb is not read (it may be NULL).  perm and slot are those of the
  * moe_assemble call for the same queue (which may then skip its copy, xb = NULL); a slot
  * outside [0, P) is clamped into range (moe_assemble gives such pairs no batch row).
+ * With row_slot != NULL (moe_assemble's row_slot output) batch row r is pool row
+ * row_slot[r]: the same rows, one dependent load fewer; perm and slot are then not read.
  * The pool must be 16-byte aligned with pool_pitch * element size a multiple of 16, and
  * for bf16 activations P * pool_pitch * 2 < 2^31 (MOE_EINVAL_SIZE otherwise). */
 typedef struct moe_ffn_args {
@@ -187,6 +191,8 @@ typedef struct moe_ffn_args {
   const void* pool;        /* [P][pool_pitch] token pool (act_dtype) */
   int64_t P;               /* pool rows */
   int64_t pool_pitch;      /* elements between pool rows */
+  const int32_t* row_slot; /* optional gather-on-load index: pool row of batch row r (moe_assemble's
+                              row_slot); when set it replaces perm and slot (which may be NULL) */
 } moe_ffn_args;
 
 size_t moe_ffn_workspace_size(int32_t n_max, int32_t E_loc, int32_t H, int32_t I, int32_t act_dtype);

@@ -62,7 +62,9 @@ def test_assemble_matches_oracle(case):
     counts = torch.empty(E, dtype=torch.int32, device="cuda")
     offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
-    M.moe_assemble(dev(slot), dev(expert), base, E, pool, perm, pos, counts, offsets, st_xb, err, n=n)
+    row_slot = torch.full((max(n, 1),), -9, dtype=torch.int32, device="cuda")
+    M.moe_assemble(dev(slot), dev(expert), base, E, pool, perm, pos, counts, offsets, st_xb, err, n=n,
+                   row_slot=row_slot)
     e = sync_err(err)
     a = O.assemble(slot, expert, base, E, P)
     assert e == a["err"]
@@ -72,6 +74,9 @@ def test_assemble_matches_oracle(case):
         assert np.array_equal(perm.cpu().numpy()[:n], a["perm"])
         assert np.array_equal(pos.cpu().numpy()[:n], a["pos"])
         nv = int(a["offsets"][-1])
+        # row_slot: the pool slot of each batch row, -1 past the accepted pairs
+        rs = row_slot.cpu().numpy()[:n]
+        assert np.array_equal(rs[:nv], slot[a["perm"][:nv]]) and np.all(rs[nv:] == -1)
         ref = O.gather_rows(pool_np[:, :H], slot, a["perm"], nv)
         got = to_numpy_bits(st_xb[:nv])
         assert np.array_equal(got.view(np.uint8), np.ascontiguousarray(ref).view(np.uint8))
@@ -426,16 +431,20 @@ def test_gather_on_load_matches_explicit_gather(case):
     wt = weight_tensors(wts)
     pool = dev(pool_np, act)
     ys = []
-    for gol in (True, False):
-        st = M.ExpertStep(E, H, I, 2, codes[act], codes[wdt], n, 4, gather_on_load=gol)
+    # gather through row_slot (the default), through perm and slot, and the explicit copy
+    for mode in ("row_slot", "perm_slot", "explicit"):
+        st = M.ExpertStep(E, H, I, 2, codes[act], codes[wdt], n, 4, gather_on_load=mode != "explicit")
         st.load_weights(wt["wg"], wt["wu"], wt["wd"], wt.get("s_gate"), wt.get("s_up"), wt.get("s_down"))
         st.assemble(dev(slot), dev(expert), 0, pool)
+        if mode == "perm_slot":
+            st._gather = st._gather[:3]
         st.ffn(n)
         assert sync_err(st.err) == (M.ERR_SLOT_RANGE | M.ERR_EXPERT_NONLOCAL)
         ys.append(to_numpy_bits(st.y))
         offsets = st.offsets.cpu().numpy()
     nv = int(offsets[-1])
-    assert np.array_equal(ys[0][:nv], ys[1][:nv]), "gather-on-load differs from the explicit gather"
+    assert np.array_equal(ys[0][:nv], ys[2][:nv]), "gather through row_slot differs from the explicit gather"
+    assert np.array_equal(ys[1][:nv], ys[2][:nv]), "gather through perm/slot differs from the explicit gather"
     a = O.assemble(slot, expert, 0, E, P)
     assert np.array_equal(offsets, a["offsets"])
     y_ref = O.expert_ffn(O.decode(O.gather_rows(pool_np, slot, a["perm"], nv), act), a["offsets"], wts)
