@@ -511,8 +511,16 @@ constexpr int kGemmBN = kGemmWaveN * kFfnWaves;
 #ifndef MOE_FFN_GEMM_STAGES_FP8
 #define MOE_FFN_GEMM_STAGES_FP8 4
 #endif
+// Workgroups per CU the tiled kernel is built for.  Two (fp8 weights only: bf16 weight
+// fragments do not fit the 256-register budget) let one workgroup's MFMAs run while the other
+// waits, with a 2-stage ring and a 2-slice fragment ring per wave.
+#ifndef MOE_FFN_GEMM_OCC_FP8
+#define MOE_FFN_GEMM_OCC_FP8 2
+#endif
 template <int WDT>
-constexpr int gemm_stages() { return WDT == MOE_FP8_E4M3 ? MOE_FFN_GEMM_STAGES_FP8 : 4; }
+constexpr int gemm_occ() { return WDT == MOE_FP8_E4M3 ? MOE_FFN_GEMM_OCC_FP8 : 1; }
+template <int WDT>
+constexpr int gemm_stages() { return gemm_occ<WDT>() == 2 ? 2 : (WDT == MOE_FP8_E4M3 ? MOE_FFN_GEMM_STAGES_FP8 : 4); }
 
 // s_waitcnt vmcnt(N) alone (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt
 // at their no-wait maxima)
@@ -575,7 +583,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, int
 // epilogue.  With no partial area (or S < 2) the tail units run whole.
 constexpr int kGemmAccRegs = 4 * 2 * 16;                         // fp32 accumulators per thread
 constexpr int64_t kGemmPartFloats = (int64_t)kGemmAccRegs * 256;  // one partial tile
-constexpr int kGemmSplitSlots = 256;                              // partial tiles in the workspace
+constexpr int kGemmSplitSlots = 512;  // partial tiles in the workspace (2 workgroups x 256 CUs)
 constexpr int kGemmMaxSplit = 8;
 
 struct GemmSplit {
@@ -657,22 +665,24 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16 (&acc)[4][2], int e, 
 }
 
 // Partial tile layout: accumulator group q = 4 (2 mt + t) + v/4 of thread tid at
-// part[1024 q + 4 tid .. + 3] (each wave stores and loads 1 KiB runs).
+// part[1024 q + 4 tid .. + 3] (each wave stores and loads 1 KiB runs).  Buffer stores with the
+// group offset in a scalar register, so no per-group 64-bit address stays live.
 __device__ __forceinline__ void store_partial(const f32x16 (&acc)[4][2], float* __restrict__ part, int tid) {
+  const __amdgpu_buffer_rsrc_t r = buffer_rsrc(part, kGemmPartFloats * 4);
   static_for<4>([&](auto mt) {
     static_for<2>([&](auto t) {
       static_for<4>([&](auto g) {
         constexpr int q = 4 * (2 * mt() + t()) + g();
-        const float4 v = make_float4(acc[mt()][t()][4 * g()], acc[mt()][t()][4 * g() + 1], acc[mt()][t()][4 * g() + 2],
-                                     acc[mt()][t()][4 * g() + 3]);
-        *reinterpret_cast<float4*>(part + 1024 * q + 4 * tid) = v;
+        u32x4 v;
+        static_for<4>([&](auto k) { v[k()] = __float_as_uint(acc[mt()][t()][4 * g() + k()]); });
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, 16 * tid, 4096 * q, 0);
       });
     });
   });
 }
 
 template <int MODE, int WDT>
-__global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets,
+__global__ __launch_bounds__(256, gemm_occ<WDT>()) void ffn_gemm_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets,
                                                        int E_loc, const char* __restrict__ W,
                                                        const float* __restrict__ s0, const float* __restrict__ s1,
                                                        uint16_t* __restrict__ out, int Kd, int Nw, int out_ld,
@@ -753,7 +763,6 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(const uint16_t* __rest
     static_for<4>([&](auto i) { static_for<2>([&](auto jj) { acc[i()][jj()] = f32x16{}; }); });
 
     GemmW<WDT> wr[S];   // weight fragments of steps i .. i+S-1
-    u32x4 af[4][4];     // activation fragments [k-slice s][mt] of the step being computed
     // activations of step ks go straight from global memory into LDS stage slot (16 bytes
     // per lane at the instruction's base + 16 lane, i.e. exactly the slot order above)
     auto issue_a = [&](auto slot, int ks) {
@@ -775,24 +784,6 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(const uint16_t* __rest
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     };
-    auto read1 = [&](auto stg, auto ss) {  // fragments of k-slice ss
-      const u32x4* tile = stage(stg);
-      static_for<4>([&](auto mt) {
-        const int row = mt() * 32 + l32, kq = 4 * hf + ss();
-        af[ss()][mt()] = tile[row * 8 + (kq ^ ((row >> 1) & 7))];
-      });
-    };
-    auto mfma1 = [&](auto slot, auto ss) {  // MFMAs of k-slice ss
-      bf16x8 bw[2];
-      static_for<2>([&](auto t) { bw[t()] = wr[slot()].frag(t(), ss()); });
-      static_for<4>([&](auto mt) {
-        bf16x8 a;
-        __builtin_memcpy(&a, &af[ss()][mt()], 16);
-        static_for<2>([&](auto t) {
-          acc[mt()][t()] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bw[t()], acc[mt()][t()], 0, 0, 0);
-        });
-      });
-    };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
@@ -813,6 +804,91 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(const uint16_t* __rest
     auto issue = [&](auto slot, int ks) {
       issue_a(slot, ks);
       issue_w(slot, ks);
+    };
+    if constexpr (gemm_occ<WDT>() == 2) {
+      // Two workgroups per CU: 2-stage ring, fragments of two k-slices at a time.  Step i:
+      // slices 1-3 of step i are read from its stage one slice ahead of their MFMAs; after the
+      // barrier (copy of step i+1 landed everywhere, stage of step i read by everyone) the
+      // copy of step i+2 goes into that stage and slice 0 of step i+1 is read; the weights of
+      // step i+2 load into the slot step i has released.  Behind the copy of step i+1 there
+      // are only the weights of step i+1.  Steps past k1 zero their weight fragments.
+      static_assert(S == 2, "two-workgroup variant: 2-stage ring");
+      u32x4 fr[2][4];
+      auto read2 = [&](auto stg, auto ss, auto dst) {
+        const u32x4* tile = stage(stg);
+        static_for<4>([&](auto mt) {
+          const int row = mt() * 32 + l32, kq = 4 * hf + ss();
+          fr[dst()][mt()] = tile[row * 8 + (kq ^ ((row >> 1) & 7))];
+        });
+      };
+      auto mfma2 = [&](auto slot, auto ss, auto src, bool dead) {
+        bf16x8 bw[2];
+        static_for<2>([&](auto t) { bw[t()] = dead ? bf16x8{} : wr[slot()].frag(t(), ss()); });
+        static_for<4>([&](auto mt) {
+          bf16x8 a;
+          __builtin_memcpy(&a, &fr[src()][mt()], 16);
+          static_for<2>([&](auto t) {
+            acc[mt()][t()] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bw[t()], acc[mt()][t()], 0, 0, 0);
+          });
+        });
+      };
+      __builtin_amdgcn_sched_barrier(0);
+      issue(I0{}, k0);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(I1{}, k0 + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<kW + kA + kW>();  // the copy of step k0
+      barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      read2(I0{}, I0{}, I0{});
+      const int n_steps = (k1 - k0 + 1) / 2 * 2;
+#pragma clang loop unroll(disable)
+      for (int it = 0; it < n_steps; it += 2) {
+        static_for<2>([&](auto v) {
+          using SL = std::integral_constant<int, v()>;
+          using NX = std::integral_constant<int, 1 - v()>;
+          const int i = k0 + it + v();
+          const bool dead = i >= k1;
+          read2(SL{}, I1{}, I1{});
+          mfma2(SL{}, I0{}, I0{}, dead);
+          __builtin_amdgcn_sched_barrier(0);
+          read2(SL{}, I2{}, I0{});
+          mfma2(SL{}, I1{}, I1{}, dead);
+          __builtin_amdgcn_sched_barrier(0);
+          read2(SL{}, I3{}, I1{});
+          mfma2(SL{}, I2{}, I0{}, dead);
+          __builtin_amdgcn_sched_barrier(0);
+          wait_vmcnt<kW>();  // the copy of step i+1
+          barrier();
+          __builtin_amdgcn_sched_barrier(0);
+          issue_a(SL{}, i + 2);  // the stage of step i is free now
+          __builtin_amdgcn_sched_barrier(0);
+          read2(NX{}, I0{}, I0{});
+          mfma2(SL{}, I3{}, I1{}, dead);
+          __builtin_amdgcn_sched_barrier(0);
+          issue_w(SL{}, i + 2);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      }
+    } else {
+    u32x4 af[4][4];     // activation fragments [k-slice s][mt] of the step being computed
+    auto read1 = [&](auto stg, auto ss) {  // fragments of k-slice ss
+      const u32x4* tile = stage(stg);
+      static_for<4>([&](auto mt) {
+        const int row = mt() * 32 + l32, kq = 4 * hf + ss();
+        af[ss()][mt()] = tile[row * 8 + (kq ^ ((row >> 1) & 7))];
+      });
+    };
+    auto mfma1 = [&](auto slot, auto ss) {  // MFMAs of k-slice ss
+      bf16x8 bw[2];
+      static_for<2>([&](auto t) { bw[t()] = wr[slot()].frag(t(), ss()); });
+      static_for<4>([&](auto mt) {
+        bf16x8 a;
+        __builtin_memcpy(&a, &af[ss()][mt()], 16);
+        static_for<2>([&](auto t) {
+          acc[mt()][t()] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bw[t()], acc[mt()][t()], 0, 0, 0);
+        });
+      });
     };
     static_for<S>([&](auto v) {  // same batch order as the loop, so every wait matches the steady state
       __builtin_amdgcn_sched_barrier(0);
@@ -856,6 +932,7 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(const uint16_t* __rest
         issue_w(SL{}, i + S);  // weight slot of step i is free after its last MFMAs
         __builtin_amdgcn_sched_barrier(0);
       });
+    }
     }
     // no copy may still be in flight into a stage the next item's prologue fills, and the
     // next item's copies wait for this item's last LDS reads

@@ -155,7 +155,7 @@ int moe_pack_ffn_weights(const moe_pack_args* args, hipStream_t stream);
  * Limits: 1 <= E_loc <= 256, H % 64 == 0, I % 64 == 0, 0 <= n <= 2^24; 16-byte aligned
  * buffers.  The workspace must hold moe_ffn_workspace_size(...) bytes: h ([n][I] in
  * act_dtype, rounded up to 256 bytes) and, for batches that can take the tiled path for
- * many rows per expert (bf16 activations, n_max >= 96 E_loc), 32 MiB of fp32 partial tiles
+ * many rows per expert (bf16 activations, n_max >= 96 E_loc), 64 MiB of fp32 partial tiles
  * for the k-split of each XCD's last partial round of work units.  With a workspace sized
  * for h alone the call still runs, with those units computed whole (same values up to
  * rounding order).  Results are deterministic for a given device and workspace size.

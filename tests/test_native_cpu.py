@@ -60,8 +60,9 @@ def test_workspace_size(lib):
     assert M.moe_ffn_workspace_size(3, 1, 64, 64, M.MOE_BF16) == 512  # rounded up to 256 B
     assert M.moe_ffn_workspace_size(1, 1, 64, 64, 7) == 0
     # batches that can take the tiled GEMM path (>= 96 rows per local expert, bf16 activations)
-    # also hold 256 fp32 partial tiles of 128 KiB for the split tail units
-    parts = 256 * 128 * 1024
+    # also hold 512 fp32 partial tiles of 128 KiB for the split tail units (one per workgroup
+    # of a grid of up to 2 workgroups x 256 CUs)
+    parts = 512 * 128 * 1024
     assert M.moe_ffn_workspace_size(6554, 32, 4096, 2048, M.MOE_BF16) == 6554 * 2048 * 2 + parts
     assert M.moe_ffn_workspace_size(96 * 32, 32, 4096, 2048, M.MOE_BF16) == 96 * 32 * 2048 * 2 + parts
     assert M.moe_ffn_workspace_size(96 * 32 - 1, 32, 4096, 2048, M.MOE_BF16) == (96 * 32 - 1) * 2048 * 2
