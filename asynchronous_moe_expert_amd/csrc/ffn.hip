@@ -6,8 +6,10 @@
 //
 // Design (gfx950):
 //   * Two launches: gate/up GEMM with the SwiGLU epilogue (writes h), then the down GEMM.
-//   * Work unit = (row chunk of <= 48 rows of one expert, 4 waves x NS weight strips of 16
-//     output columns).  The chunk list is derived on the device from `offsets`, so ragged
+//   * Decode-sized batches (streaming kernel below): work unit = (row chunk of <= 48 rows of
+//     one expert, WV waves x NS weight strips of 16 output columns).  Prefill-sized batches
+//     (>= 96 rows per expert on average) take the tiled GEMM kernel further down (128-row
+//     chunks x 256 columns).  The chunk list is derived on the device from `offsets`, so ragged
 //     and empty experts need no host round trip.  The grid is what the device holds at
 //     once (CUs x occupancy) and strides over the active units only: a decode batch's
 //     units all start in the first round and no workgroup slot is spent on an idle unit.
@@ -483,18 +485,18 @@ static void launch_mfma_t(const void* A, const int32_t* offsets, int E_loc, cons
 // on gfx950) with every operand byte feeding as many MFMAs as registers allow:
 //   * unit = (128-row chunk of one expert, 256 weight columns); each of the 4 waves owns
 //     64 columns for all 128 rows (4 x 2 tiles of 32 x 32, 128 fp32 accumulators);
-//   * the activation k-tile (128 rows x 64 k, bf16) is shared by the 4 waves through a
-//     double-buffered LDS tile: each thread loads its quarter four k-steps ahead into a
-//     register ring and parks it in LDS one step ahead; the 16-byte slots of a tile row
-//     are XOR-swizzled so that the loads stay coalesced (8 rows x 128 B per instruction)
-//     and the operand reads are free of bank conflicts;
-//   * each wave loads its weight fragments four k-steps ahead straight from the packed
+//   * the activation k-tile (128 rows x 64 k, bf16) is shared by the 4 waves through an
+//     LDS ring: each wave copies its quarter straight from global memory into the stage
+//     (buffer_load ... lds, 16 bytes per lane), several k-steps ahead; the 16-byte slots of
+//     a tile row are XOR-swizzled so that the copies stay coalesced (8 rows x 128 B per
+//     instruction) and the operand reads are free of bank conflicts;
+//   * each wave loads its weight fragments several k-steps ahead straight from the packed
 //     layout into a register ring (buffer loads: a per-lane offset fixed for the unit, the
 //     k-step in a scalar register) and widens fp8 to bf16 in registers;
-//   * one wave per SIMD with a software pipeline: the activation fragments of the next
-//     k-step are read from LDS in two halves, each into the registers the current step has
-//     just consumed, between MFMA halves, so LDS latency and the per-step barrier overlap
-//     the math;
+//   * software pipeline: the activation fragments are read from LDS one k-slice at a time
+//     between the MFMAs of the previous slices, so LDS latency overlaps the math; one
+//     workgroup per CU with a 4-stage ring for bf16 weights, two per CU with a 2-stage ring
+//     and a 2-slice fragment ring for fp8 weights (one computes while the other waits);
 //   * gate/up: a wave's 64 packed rows are 2 gate and 2 up strips; its column tile 0 takes
 //     the gate strips and tile 1 the matching up strips, so the SwiGLU epilogue pairs values
 //     within a lane (no cross-lane exchange);
