@@ -823,15 +823,21 @@ __global__ __launch_bounds__(256, gemm_occ<WDT>()) void ffn_gemm_kernel(const ui
           fr[dst()][mt()] = tile[row * 8 + (kq ^ ((row >> 1) & 7))];
         });
       };
+      // 32-row tiles that hold rows of the unit: the MFMAs of the rest (padding of an
+      // expert's last chunk) are skipped; their accumulators stay zero and are never stored.
+      // (With two workgroups per CU the freed matrix-core cycles go to the other one.)
+      const int mt_act = __builtin_amdgcn_readfirstlane((mend - m0 + 31) / 32);
       auto mfma2 = [&](auto slot, auto ss, auto src, bool dead) {
         bf16x8 bw[2];
         static_for<2>([&](auto t) { bw[t()] = dead ? bf16x8{} : wr[slot()].frag(t(), ss()); });
         static_for<4>([&](auto mt) {
-          bf16x8 a;
-          __builtin_memcpy(&a, &fr[src()][mt()], 16);
-          static_for<2>([&](auto t) {
-            acc[mt()][t()] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bw[t()], acc[mt()][t()], 0, 0, 0);
-          });
+          if (mt() == 0 || mt() < mt_act) {
+            bf16x8 a;
+            __builtin_memcpy(&a, &fr[src()][mt()], 16);
+            static_for<2>([&](auto t) {
+              acc[mt()][t()] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bw[t()], acc[mt()][t()], 0, 0, 0);
+            });
+          }
         });
       };
       __builtin_amdgcn_sched_barrier(0);
