@@ -97,6 +97,8 @@ FFN_CASES = [
     ("fp8", 3, 640, 192, [257, 1, 130]),
     ("bf16", 2, 2880, 2880, [200, 190]),
     ("fp8", 2, 4096, 2048, [300, 60]),
+    # last chunks of 70, 96 and 97 rows: 3, 3 and 4 executed 32-row tiles (the fp8 kernel skips the rest)
+    ("fp8", 3, 512, 256, [198, 96, 353]),
 ]
 
 
