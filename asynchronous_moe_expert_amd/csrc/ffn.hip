@@ -147,17 +147,30 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// 16-byte weight load; NT marks it non-temporal (for weights read once per launch, so that
+// they neither displace reused lines nor wait for allocation in the caches)
+template <bool NT>
+__device__ __forceinline__ uint4 wload(const uint4* p) {
+  if constexpr (NT) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+  } else {
+    return *p;
+  }
+}
+
 template <int WDT, int NS>
 struct WTile;  // one k-step of NS weight strips, as loaded (16 bytes per lane per run)
 
 template <int NS>
 struct WTile<MOE_BF16, NS> {
   uint4 raw[NS][2];
+  template <bool NT>
   __device__ __forceinline__ void load(const char* __restrict__ p, int64_t strip_stride) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      raw[s][0] = *reinterpret_cast<const uint4*>(p + s * strip_stride);
-      raw[s][1] = *reinterpret_cast<const uint4*>(p + s * strip_stride + 1024);
+      raw[s][0] = wload<NT>(reinterpret_cast<const uint4*>(p + s * strip_stride));
+      raw[s][1] = wload<NT>(reinterpret_cast<const uint4*>(p + s * strip_stride + 1024));
     }
   }
   __device__ __forceinline__ bf16x8 frag(int s, int h) const {
@@ -170,9 +183,10 @@ struct WTile<MOE_BF16, NS> {
 template <int NS>
 struct WTile<MOE_FP8_E4M3, NS> {
   uint4 raw[NS];
+  template <bool NT>
   __device__ __forceinline__ void load(const char* __restrict__ p, int64_t strip_stride) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s) raw[s] = *reinterpret_cast<const uint4*>(p + s * strip_stride);
+    for (int s = 0; s < NS; ++s) raw[s] = wload<NT>(reinterpret_cast<const uint4*>(p + s * strip_stride));
   }
   __device__ __forceinline__ bf16x8 frag(int s, int h) const {
     return h == 0 ? e4m3x8_to_bf16(raw[s].x, raw[s].y) : e4m3x8_to_bf16(raw[s].z, raw[s].w);
@@ -243,10 +257,11 @@ struct ChunkTable {
     total = __builtin_amdgcn_readfirstlane(base);
   }
 
-  // expert, first row and end row of chunk c (0 <= c < total; e = -1 otherwise)
-  __device__ __forceinline__ void find(int c, int BM, int& e, int& m0, int& mend) const {
+  // expert, first row and end row of chunk c (0 <= c < total; e = -1 otherwise), and the
+  // number of chunks of that expert
+  __device__ __forceinline__ void find(int c, int BM, int& e, int& m0, int& mend, int& nce) const {
     e = -1;
-    m0 = mend = 0;
+    m0 = mend = nce = 0;
     static_for<4>([&](auto jc) {
       constexpr int j = jc();
       const uint64_t hit = __ballot(c >= start[j] && c < start[j] + nc[j]);
@@ -255,8 +270,13 @@ struct ChunkTable {
         e = l + 64 * j;
         m0 = __shfl(a0[j], l, 64) + (c - __shfl(start[j], l, 64)) * BM;
         mend = min(__shfl(a1[j], l, 64), m0 + BM);
+        nce = __shfl(nc[j], l, 64);
       }
     });
+  }
+  __device__ __forceinline__ void find(int c, int BM, int& e, int& m0, int& mend) const {
+    int nce;
+    find(c, BM, e, m0, mend, nce);
   }
 };
 
@@ -272,13 +292,13 @@ constexpr int kFfnWaves = 4;
 // expert (or -1), column block and rows of unit u of the batch, when u < u_end.  Units are
 // numbered column-block-major (u = nb * total + chunk).
 __device__ __forceinline__ int next_unit(const int32_t* __restrict__ offsets, int E_loc, int n_rows, int BM, int lane,
-                                         int u, int u_end, int total, int& nb, int& m0, int& mend) {
+                                         int u, int u_end, int total, int& nb, int& m0, int& mend, int& nce) {
   int e = -1;
   if (u < u_end) {
     ChunkTable tab;
     tab.build(offsets, E_loc, n_rows, BM, lane);
     nb = u / total;
-    tab.find(u - nb * total, BM, e, m0, mend);
+    tab.find(u - nb * total, BM, e, m0, mend, nce);
   }
   return e;
 }
@@ -316,7 +336,7 @@ __global__ __launch_bounds__(64 * WV) void ffn_mfma_kernel(const uint16_t* __res
   // for the first unit and again for each later one, so that it holds no registers across
   // the contraction.
   const int G = gridDim.x, b = blockIdx.x, xcd = b & 7;
-  int total, u, u_end, nb = 0, e = -1, m0 = 0, mend = 0;
+  int total, u, u_end, nb = 0, e = -1, m0 = 0, mend = 0, nce = 0;
   {
     ChunkTable tab;
     tab.build(offsets, E_loc, n_rows, BM, lane);
@@ -326,10 +346,11 @@ __global__ __launch_bounds__(64 * WV) void ffn_mfma_kernel(const uint16_t* __res
     u_end = (int)((int64_t)U * (xcd + 1) / 8);
     if (u < u_end) {
       nb = u / total;
-      tab.find(u - nb * total, BM, e, m0, mend);
+      tab.find(u - nb * total, BM, e, m0, mend, nce);
     }
   }
-  for (; u < u_end; u += G >> 3, e = next_unit(offsets, E_loc, n_rows, BM, lane, u, u_end, total, nb, m0, mend)) {
+  for (; u < u_end;
+       u += G >> 3, e = next_unit(offsets, E_loc, n_rows, BM, lane, u, u_end, total, nb, m0, mend, nce)) {
     if (e < 0) break;  // not reachable: the table is the same on every build
     const int strip0 = (nb * WV + wv) * NS;  // this wave's first strip
     const bool wact = strip0 < n_strips;            // (the last block may be partial)
@@ -371,37 +392,46 @@ __global__ __launch_bounds__(64 * WV) void ffn_mfma_kernel(const uint16_t* __res
 
     // k-step i: issue the loads of step i+R-1 (clamped to the last step: valid memory,
     // result unused), park this thread's activation piece of step i in LDS, barrier, MFMAs.
-    // Ring slots are compile-time indices so that every slot lives in registers.
-    WTile<WDT, NS> wr[R];
-    AP ar[R];
-    // Every load is unconditional (an idle wave streams valid strip-0 weights and its
-    // results are never stored): a load under a branch makes the compiler's wait counts
-    // assume the branch was not taken, which drains the ring at every k-step.
-    auto issue = [&](auto slot, int ks) {
-      ks = min(ks, KS - 1);
-      wr[slot()].load(wlane + ks * blk_bytes, strip_stride);
-      ar[slot()].load(ap, ks * kBK);
-    };
-    auto step = [&](auto slot, int i) {
-      ar[slot()].store(a_lds[i & 1], tid);
-      wg_barrier();
-      compute(wr[slot()], a_lds[i & 1]);
-    };
-    static_for<R - 1>([&](auto v) { issue(v, v()); });
-    int it = 0;
+    // Ring slots are compile-time indices so that every slot lives in registers.  The whole
+    // pipeline is instantiated for both weight-load policies: non-temporal when the unit's
+    // expert is a single row chunk (its weight strips are read once in this launch), cached
+    // otherwise (the expert's other chunks re-read them through L2).
+    auto pipeline = [&](auto nt) {
+      WTile<WDT, NS> wr[R];
+      AP ar[R];
+      // Every load is unconditional (an idle wave streams valid strip-0 weights and its
+      // results are never stored): a load under a branch makes the compiler's wait counts
+      // assume the branch was not taken, which drains the ring at every k-step.
+      auto issue = [&](auto slot, int ks) {
+        ks = min(ks, KS - 1);
+        wr[slot()].template load<nt()>(wlane + ks * blk_bytes, strip_stride);
+        ar[slot()].load(ap, ks * kBK);
+      };
+      auto step = [&](auto slot, int i) {
+        ar[slot()].store(a_lds[i & 1], tid);
+        wg_barrier();
+        compute(wr[slot()], a_lds[i & 1]);
+      };
+      static_for<R - 1>([&](auto v) { issue(v, v()); });
+      int it = 0;
 #pragma clang loop unroll(disable)
-    for (; it + R <= KS; it += R) {
-      static_for<R>([&](auto v) {
-        issue(std::integral_constant<int, (v() + R - 1) % R>{}, it + v() + R - 1);
-        __builtin_amdgcn_sched_barrier(0);
-        step(v, it + v());
-        __builtin_amdgcn_sched_barrier(0);
+      for (; it + R <= KS; it += R) {
+        static_for<R>([&](auto v) {
+          issue(std::integral_constant<int, (v() + R - 1) % R>{}, it + v() + R - 1);
+          __builtin_amdgcn_sched_barrier(0);
+          step(v, it + v());
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      }
+      // the remaining KS - it < R steps sit in slots 0, 1, ...
+      static_for<R - 1>([&](auto v) {
+        if (it + v() < KS) step(v, it + v());
       });
-    }
-    // the remaining KS - it < R steps sit in slots 0, 1, ...
-    static_for<R - 1>([&](auto v) {
-      if (it + v() < KS) step(v, it + v());
-    });
+    };
+    if (nce == 1)
+      pipeline(std::true_type{});
+    else
+      pipeline(std::false_type{});
     wg_barrier();  // the next unit's first LDS writes wait for this unit's last reads
     if (!wact) continue;
 
