@@ -366,12 +366,20 @@ def test_c2_skewed_batches():
             _check_step(st, e, b, wts, a, y, TOL["bf16"])
 
 
-def test_c4_prefill_wave0_sampled():
-    """Full-size prefill wave (6554 pairs, 32 experts, fp8 weights): integer parts
-    bit-exact; FFN and combined rows on a seeded sample of 96 rows / tokens."""
-    _say("C4 prefill fp8 wave 0")
-    s = W.c4_prefill_setup()
-    b = W.c4_wave(s, 0)
+@pytest.fixture(scope="module")
+def c4_setup():
+    return W.c4_prefill_setup()
+
+
+@pytest.mark.parametrize("wave", [0, 1, 2, 3])
+def test_c4_prefill_wave_sampled(c4_setup, wave):
+    """Full-size prefill waves (6554 / 4915 / 3277 / 1638 pairs, 32 experts, fp8 weights):
+    integer parts bit-exact; FFN and combined rows on a seeded sample of about 96 rows /
+    tokens.  Waves 0-2 run the 128-row tiled GEMM, wave 3 the weight-streaming kernel with
+    experts of one row chunk and of several (Zipf-skewed counts)."""
+    _say(f"C4 prefill fp8 wave {wave}")
+    s = c4_setup
+    b = W.c4_wave(s, wave)
     st, e = _run_config_step(b, s.weights, M.MOE_BF16, M.MOE_FP8_E4M3, T_cap=b.T)
     a = O.assemble(b.slot, b.expert, 0, b.E_loc, b.P)
     assert e == 0 == a["err"]
