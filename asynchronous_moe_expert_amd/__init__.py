@@ -18,6 +18,8 @@ from ._native import (  # noqa: F401
     MOE_FP8_E4M3,
     CombineState,
     MoeError,
+    combine_args,
+    combine_call,
     load,
     moe_assemble,
     moe_combine_release,

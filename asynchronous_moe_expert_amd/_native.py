@@ -42,7 +42,8 @@ class FfnArgs(C.Structure):
     _fields_ = [("n", _i32), ("E_loc", _i32), ("H", _i32), ("I", _i32), ("act_dtype", _i32), ("w_dtype", _i32),
                 ("xb", _p), ("offsets", _p), ("w_gu", _p), ("w_d", _p), ("s_gate", _p), ("s_up", _p),
                 ("s_down", _p), ("y", _p), ("workspace", _p), ("workspace_bytes", C.c_size_t), ("ev_mid", _p),
-                ("perm", _p), ("slot", _p), ("pool", _p), ("P", _i64), ("pool_pitch", _i64), ("row_slot", _p)]
+                ("perm", _p), ("slot", _p), ("pool", _p), ("P", _i64), ("pool_pitch", _i64), ("row_slot", _p),
+                ("plan", _p)]
 
 
 class StateC(C.Structure):
@@ -164,9 +165,11 @@ def moe_pack_ffn_weights(wg, wu, wd, w_gu, w_d, w_dtype: int, stream=None) -> No
 
 def moe_expert_ffn_grouped(n: int, E_loc: int, H: int, I: int, act_dtype: int, w_dtype: int, xb, offsets, w_gu,
                            w_d, y, workspace, s_gate=None, s_up=None, s_down=None, ev_mid: int | None = None,
-                           stream=None, gather=None) -> None:
+                           stream=None, gather=None, plan: "CombineArgs | None" = None) -> None:
     """gather=(perm, slot, pool) or (perm, slot, pool, row_slot): read batch rows from the pool
-    (gather-on-load; with row_slot, pool row row_slot[r] and perm/slot unused); xb may be None."""
+    (gather-on-load; with row_slot, pool row row_slot[r] and perm/slot unused); xb may be None.
+    plan: the arguments (combine_args) of a moe_combine_plan call that this call enqueues as
+    well, inside the gate/up launch where it fits."""
     perm = slot = pool = row_slot = None
     P = pitch = 0
     if gather is not None:
@@ -176,7 +179,7 @@ def moe_expert_ffn_grouped(n: int, E_loc: int, H: int, I: int, act_dtype: int, w
     a = FfnArgs(n, E_loc, H, I, act_dtype, w_dtype, _ptr(xb), _ptr(offsets), _ptr(w_gu), _ptr(w_d),
                 _ptr(s_gate), _ptr(s_up), _ptr(s_down), _ptr(y), _ptr(workspace),
                 workspace.numel() * workspace.element_size(), ev_mid, _ptr(perm), _ptr(slot), _ptr(pool), P, pitch,
-                _ptr(row_slot))
+                _ptr(row_slot), None if plan is None else C.addressof(plan))
     _check(load().moe_expert_ffn_grouped(C.byref(a), _stream(stream)), "moe_expert_ffn_grouped")
 
 
@@ -212,6 +215,13 @@ def _combine_args(rows, row_idx, tok, kslot, w, gen, K, state, out, rel_list, re
                        _ptr(rel_count), _ptr(err), _ptr(workspace), workspace.numel() * workspace.element_size())
 
 
+def combine_args(rows, row_idx, tok, kslot, w, gen, K: int, state: CombineState, out, rel_list, rel_count, err,
+                 workspace, m: int | None = None, n_rows: int | None = None) -> CombineArgs:
+    """The argument struct of a combine call (for moe_expert_ffn_grouped's plan)."""
+    return _combine_args(rows, row_idx, tok, kslot, w, gen, K, state, out, rel_list, rel_count, err, workspace, m,
+                         n_rows)
+
+
 def moe_combine_release(rows, row_idx, tok, kslot, w, gen, K: int, state: CombineState, out, rel_list, rel_count,
                         err, workspace, m: int | None = None, n_rows: int | None = None, stream=None,
                         part: str = "release") -> None:
@@ -219,5 +229,10 @@ def moe_combine_release(rows, row_idx, tok, kslot, w, gen, K: int, state: Combin
     part = "plan" / "apply" calls moe_combine_plan / moe_combine_apply instead."""
     a = _combine_args(rows, row_idx, tok, kslot, w, gen, K, state, out, rel_list, rel_count, err, workspace, m,
                       n_rows)
+    combine_call(a, part, stream)
+
+
+def combine_call(a: CombineArgs, part: str = "release", stream=None) -> None:
+    """moe_combine_release / _plan / _apply on an argument struct from combine_args."""
     fn = {"release": "moe_combine_release", "plan": "moe_combine_plan", "apply": "moe_combine_apply"}[part]
     _check(getattr(load(), fn)(C.byref(a), _stream(stream)), fn)

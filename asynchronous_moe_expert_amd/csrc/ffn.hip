@@ -33,6 +33,7 @@
 #include <type_traits>
 #include <utility>
 
+#include "combine_plan.hpp"
 #include "common.hpp"
 
 namespace moe {
@@ -317,7 +318,7 @@ __global__ __launch_bounds__(64 * WV) void ffn_mfma_kernel(const uint16_t* __res
                                                     int E_loc, const char* __restrict__ W,
                                                     const float* __restrict__ s0, const float* __restrict__ s1,
                                                     uint16_t* __restrict__ out, int Kd, int Nw, int out_ld,
-                                                    int n_blocks_N, int n_rows, GatherRows gr) {
+                                                    int n_blocks_N, int n_rows, GatherRows gr, PlanJob plan) {
   constexpr int BM = MT * 16;
   static_assert(MODE == 1 || NS % 2 == 0, "gate/up waves own (gate, up) strip pairs");
   using AP = APart<MT, 64 * WV>;
@@ -330,12 +331,22 @@ __global__ __launch_bounds__(64 * WV) void ffn_mfma_kernel(const uint16_t* __res
   const int64_t blk_bytes = 1024 * esz;
   const int64_t strip_stride = (int64_t)KS * blk_bytes;
 
+  // With a combine plan (gate/up only, m <= 256) the grid has one workgroup more than the
+  // FFN needs; that last workgroup runs the plan on a compute unit the units leave idle.
+  const bool with_plan = MODE == 0 && plan.m > 0;
+  if constexpr (MODE == 0) {
+    if (with_plan && (int)blockIdx.x == (int)gridDim.x - 1) {
+      combine_plan_body<64 * WV>(plan);
+      return;
+    }
+  }
+
   // XCD-aware order: physical workgroup b runs on XCD b % 8.  Each XCD gets an equal,
   // contiguous range of unit ids (so the chunks that share a weight tile run on one XCD's
   // L2), and its G/8 workgroups stride through that range.  The chunk table is built once
   // for the first unit and again for each later one, so that it holds no registers across
   // the contraction.
-  const int G = gridDim.x, b = blockIdx.x, xcd = b & 7;
+  const int G = (int)gridDim.x - (with_plan ? 1 : 0), b = blockIdx.x, xcd = b & 7;
   int total, u, u_end, nb = 0, e = -1, m0 = 0, mend = 0, nce = 0;
   {
     ChunkTable tab;
@@ -498,15 +509,17 @@ static int resident_workgroups(int threads) {
 template <int MODE, int WDT, int NS, int MT, int R, int WV>
 static void launch_mfma_t(const void* A, const int32_t* offsets, int E_loc, const void* W, const float* s0,
                           const float* s1, void* out, int Kd, int Nw, int out_ld, int n, GatherRows gr,
-                          hipStream_t stream) {
+                          const PlanJob& plan, hipStream_t stream) {
   constexpr int BM = MT * 16;
   constexpr auto kernel = ffn_mfma_kernel<MODE, WDT, NS, MT, R, WV>;
+  static_assert(MODE == 1 || kPlanFusedMax <= 64 * WV, "a fused plan takes m <= the workgroup's threads");
   const int n_blocks_N = (Nw / 16 + WV * NS - 1) / (WV * NS);
   const int64_t chunks_max = (n + (int64_t)(BM - 1) * E_loc) / BM;  // ragged worst case
   int64_t grid = std::min<int64_t>(chunks_max * n_blocks_N, resident_workgroups<kernel>(64 * WV));
   grid = (grid + 7) / 8 * 8;  // the XCD-aware order needs a multiple of 8
+  if (MODE == 0 && plan.m > 0) grid += 1;  // the plan's workgroup
   hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(64 * WV), 0, stream, (const uint16_t*)A, offsets, E_loc,
-                     (const char*)W, s0, s1, (uint16_t*)out, Kd, Nw, out_ld, n_blocks_N, n, gr);
+                     (const char*)W, s0, s1, (uint16_t*)out, Kd, Nw, out_ld, n_blocks_N, n, gr, plan);
 }
 
 // ------------------------------------------------------------ prefill GEMM path
@@ -1092,22 +1105,33 @@ static int pick_mt(int n, int E_loc) {
 #define MOE_FFN_GEMM_ROWS 96  // mean rows per expert from which the GEMM kernel is used
 #endif
 
+// whether a projection over n rows takes the tiled GEMM kernel (the GEMM kernel addresses its
+// activation operand with 32-bit byte offsets)
+static bool takes_gemm(int n, int E_loc, int Kd, const GatherRows& gr) {
+  const int64_t a_bytes = gr.perm ? gr.P * gr.pitch * 2 : (int64_t)n * Kd * 2;
+  return MOE_FFN_MT == 0 && n >= MOE_FFN_GEMM_ROWS * E_loc && a_bytes < ((int64_t)1 << 31);
+}
+
+// plan: a combine plan for the streaming gate/up launch's spare workgroup (m = 0: none;
+// the caller passes one only when takes_gemm is false)
 template <int MODE, int WDT>
 static void launch_mfma(const void* A, const int32_t* offsets, int E_loc, const void* W, const float* s0,
                         const float* s1, void* out, int Kd, int Nw, int out_ld, int n, GatherRows gr, float* parts,
-                        hipStream_t stream) {
+                        const PlanJob& plan, hipStream_t stream) {
   constexpr int NS = MODE == 0 ? MOE_FFN_NS_GU : MOE_FFN_NS_D;
   constexpr int R = MODE == 0 ? MOE_FFN_R_GU : MOE_FFN_R_D;
   constexpr int WV = MODE == 0 ? MOE_FFN_WV_GU : MOE_FFN_WV_D;
-  // (the GEMM kernel addresses its activation operand with 32-bit byte offsets)
-  const int64_t a_bytes = gr.perm ? gr.P * gr.pitch * 2 : (int64_t)n * Kd * 2;
-  if (MOE_FFN_MT == 0 && n >= MOE_FFN_GEMM_ROWS * E_loc && a_bytes < ((int64_t)1 << 31)) {
+  if (takes_gemm(n, E_loc, Kd, gr)) {
     launch_gemm<MODE, WDT>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, gr, parts, stream);
     return;
   }
   switch (pick_mt(n, E_loc)) {
-    case 2: launch_mfma_t<MODE, WDT, NS, 2, R, WV>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, gr, stream); break;
-    default: launch_mfma_t<MODE, WDT, NS, 3, R, WV>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, gr, stream); break;
+    case 2:
+      launch_mfma_t<MODE, WDT, NS, 2, R, WV>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, gr, plan, stream);
+      break;
+    default:
+      launch_mfma_t<MODE, WDT, NS, 3, R, WV>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, gr, plan, stream);
+      break;
   }
 }
 
@@ -1165,7 +1189,18 @@ extern "C" int moe_expert_ffn_grouped(const moe_ffn_args* a, hipStream_t stream)
   const bool f8 = a->act_dtype == MOE_BF16 && a->w_dtype == MOE_FP8_E4M3;
   if (!f32 && !bf && !f8) return MOE_EINVAL_DTYPE;
   if (!a->offsets) return MOE_EINVAL_NULL;
+  // the combine plan to enqueue with the FFN: validated here, so that an invalid one
+  // enqueues nothing; job.m > 0 when it may run inside the gate/up launch
+  PlanJob job{};
+  if (a->plan) {
+    const int rc = combine_plan_job(a->plan, &job);
+    if (rc != MOE_OK) return rc;
+  }
   if (a->n == 0) {
+    if (a->plan) {
+      const int rc = moe_combine_plan(a->plan, stream);
+      if (rc != MOE_OK) return rc;
+    }
     if (a->ev_mid) (void)hipEventRecord(a->ev_mid, stream);
     return MOE_OK;
   }
@@ -1197,6 +1232,13 @@ extern "C" int moe_expert_ffn_grouped(const moe_ffn_args* a, hipStream_t stream)
     const size_t off = h_bytes(n, I, dtype_size(a->act_dtype));
     if (a->workspace_bytes >= off + kPartAreaBytes) parts = (float*)((char*)a->workspace + off);
   }
+  // the plan joins the gate/up launch of the streaming kernel, else it runs before the FFN
+  if (f32 || takes_gemm(n, E, H, gr)) job.m = 0;
+  if (a->plan && job.m == 0) {
+    const int rc = moe_combine_plan(a->plan, stream);
+    if (rc != MOE_OK) return rc;
+  }
+  const PlanJob no_plan{};
   if (f32) {
     const int64_t t1 = (int64_t)n * I, t2 = (int64_t)n * H;
     hipLaunchKernelGGL(gateup_f32_kernel, dim3((unsigned)((t1 + 255) / 256)), dim3(256), 0, stream,
@@ -1208,16 +1250,16 @@ extern "C" int moe_expert_ffn_grouped(const moe_ffn_args* a, hipStream_t stream)
   }
   if (bf) {
     launch_mfma<0, MOE_BF16>(x_src, a->offsets, E, a->w_gu, nullptr, nullptr, a->workspace, H, 2 * I, I, n, gr, parts,
-                             stream);
+                             job, stream);
     if (a->ev_mid) (void)hipEventRecord(a->ev_mid, stream);
     launch_mfma<1, MOE_BF16>(a->workspace, a->offsets, E, a->w_d, nullptr, nullptr, a->y, I, H, H, n, none, parts,
-                             stream);
+                             no_plan, stream);
   } else {
     launch_mfma<0, MOE_FP8_E4M3>(x_src, a->offsets, E, a->w_gu, a->s_gate, a->s_up, a->workspace, H, 2 * I, I, n, gr,
-                                 parts, stream);
+                                 parts, job, stream);
     if (a->ev_mid) (void)hipEventRecord(a->ev_mid, stream);
     launch_mfma<1, MOE_FP8_E4M3>(a->workspace, a->offsets, E, a->w_d, a->s_down, nullptr, a->y, I, H, H, n, none,
-                                 parts, stream);
+                                 parts, no_plan, stream);
   }
   return launch_status();
 }

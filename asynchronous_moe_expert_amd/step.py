@@ -9,6 +9,11 @@ With gather_on_load (the default) moe_assemble only builds the index (perm, pos,
 offsets) and the FFN reads each batch row straight from the token pool through
 slot[perm[r]]; the contiguous batch is never written out.
 
+With fuse_plan (the default) run() hands the first half of the combine (moe_combine_plan)
+to moe_expert_ffn_grouped, which runs it in a spare workgroup of the gate/up launch when the
+batch takes the weight-streaming kernels (every decode step) and launches it before the FFN
+otherwise; moe_combine_apply follows the FFN.
+
 With overlap, run() puts the first half of the combine (moe_combine_plan: it reads only
 the arrival metadata and the token state) on a side stream, where it runs while the FFN
 streams the expert weights; moe_combine_apply then waits for it on the main stream.  The
@@ -27,7 +32,7 @@ _TORCH = {N.MOE_F32: torch.float32, N.MOE_BF16: torch.bfloat16, N.MOE_FP8_E4M3: 
 
 class ExpertStep:
     def __init__(self, E_loc: int, H: int, I: int, K: int, act_dtype: int, w_dtype: int, n_max: int, T_cap: int,
-                 device="cuda", gather_on_load: bool = True, overlap: bool = False):
+                 device="cuda", gather_on_load: bool = True, overlap: bool = False, fuse_plan: bool = True):
         self.E_loc, self.H, self.I, self.K = E_loc, H, I, K
         self.act_dtype, self.w_dtype, self.n_max, self.T_cap = act_dtype, w_dtype, n_max, T_cap
         dev = torch.device(device)
@@ -52,6 +57,7 @@ class ExpertStep:
         self.w_gu = self.w_d = None
         self.gather_on_load = gather_on_load
         self._gather = None  # (perm, slot, pool, row_slot) of the last assemble when gathering on load
+        self.fuse_plan = fuse_plan
         self.side = torch.cuda.Stream(device=dev) if overlap else None
         self._ev_asm = torch.cuda.Event() if overlap else None
         self._ev_plan = torch.cuda.Event() if overlap else None
@@ -73,19 +79,28 @@ class ExpertStep:
                        xb, self.err, n=n, stream=stream, row_slot=rs)
         self._gather = (self.perm, slot, pool, rs) if self.gather_on_load else None
 
-    def ffn(self, n: int, ev_mid: int | None = None, stream=None) -> None:
+    def ffn(self, n: int, ev_mid: int | None = None, stream=None, plan=None) -> None:
         N.moe_expert_ffn_grouped(n, self.E_loc, self.H, self.I, self.act_dtype, self.w_dtype, self.xb, self.offsets,
                                  self.w_gu, self.w_d, self.y, self.workspace, self.s_gate, self.s_up, self.s_down,
-                                 ev_mid=ev_mid, stream=stream, gather=self._gather)
+                                 ev_mid=ev_mid, stream=stream, gather=self._gather, plan=plan)
 
-    def combine(self, rows, row_idx, tok, kslot, w, gen, m: int | None = None, n_rows: int | None = None,
-                stream=None, part: str = "release") -> None:
-        m = int(tok.numel() if m is None else m)
+    def _combine_room(self, m: int) -> None:
         if m > self.cmb_ws_m:  # plumbing: grow the caller-owned scratch (outside any timed loop)
             self.cmb_ws_m = m
             self.cmb_ws = torch.empty(N.moe_combine_workspace_size(m), dtype=torch.uint8, device=self.cmb_ws.device)
         if m > self.rel_list.numel():
             self.rel_list = torch.empty(m, dtype=torch.int32, device=self.rel_list.device)
+
+    def local_combine_args(self, tok, kslot, w, gen, n: int):
+        """Arguments of the combine of this step's local results (rows y[pos[i]])."""
+        self._combine_room(n)
+        return N.combine_args(self.y, self.pos, tok, kslot, w, gen, self.K, self.state, self.out, self.rel_list,
+                              self.rel_count, self.err, self.cmb_ws, m=n, n_rows=n)
+
+    def combine(self, rows, row_idx, tok, kslot, w, gen, m: int | None = None, n_rows: int | None = None,
+                stream=None, part: str = "release") -> None:
+        m = int(tok.numel() if m is None else m)
+        self._combine_room(m)
         N.moe_combine_release(rows, row_idx, tok, kslot, w, gen, self.K, self.state, self.out, self.rel_list,
                               self.rel_count, self.err, self.cmb_ws, m=m, n_rows=n_rows, stream=stream, part=part)
 
@@ -94,6 +109,13 @@ class ExpertStep:
         """The whole step on one batch: assemble, FFN, combine of the local results."""
         n = int(slot.numel() if n is None else n)
         self.assemble(slot, expert, expert_base, pool, n=n, stream=stream)
+        if self.side is None and self.fuse_plan:
+            # the combine plan rides in the FFN call (inside the gate/up launch where it fits);
+            # the same argument struct then drives the apply
+            plan = self.local_combine_args(tok, kslot, w, gen, n)
+            self.ffn(n, ev_mid=ev_mid, stream=stream, plan=plan)
+            N.combine_call(plan, "apply", stream)
+            return
         if self.side is None:
             self.ffn(n, ev_mid=ev_mid, stream=stream)
             self.combine(self.y, self.pos, tok, kslot, w, gen, m=n, n_rows=n, stream=stream)

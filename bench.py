@@ -177,12 +177,14 @@ def main() -> int:
         st.run(d["slot"], d["expert"], b.expert_base, d["pool"], tok_steps[s], d["kslot"], d["w"], d["gen"], n=b.n)
 
     def step_timed(s: int) -> None:
-        # the same three calls with HIP events between them on the launch stream
+        # the same calls as ExpertStep.run (the combine plan inside the FFN call, then the
+        # apply) with HIP events between them on the launch stream
         st.assemble(d["slot"], d["expert"], b.expert_base, d["pool"])
         ev.record(e_asm[s], stream)
-        st.ffn(b.n, ev_mid=e_mid[s])
+        plan = st.local_combine_args(tok_steps[s], d["kslot"], d["w"], d["gen"], b.n)
+        st.ffn(b.n, ev_mid=e_mid[s], plan=plan)
         ev.record(e_ffn[s], stream)
-        st.combine(st.y, st.pos, tok_steps[s], d["kslot"], d["w"], d["gen"], m=b.n, n_rows=b.n)
+        M.combine_call(plan, "apply")
         ev.record(e_end[s], stream)
 
     if args.calibration_copy:

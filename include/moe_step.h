@@ -171,7 +171,19 @@ int moe_pack_ffn_weights(const moe_pack_args* args, hipStream_t stream);
  * With row_slot != NULL (moe_assemble's row_slot output) batch row r is pool row
  * row_slot[r]: the same rows, one dependent load fewer; perm and slot are then not read.
  * The pool must be 16-byte aligned with pool_pitch * element size a multiple of 16, and
- * for bf16 activations P * pool_pitch * 2 < 2^31 (MOE_EINVAL_SIZE otherwise). */
+ * for bf16 activations P * pool_pitch * 2 < 2^31 (MOE_EINVAL_SIZE otherwise).
+ *
+ * plan: optional (NULL: none).  The arguments of a moe_combine_plan call to enqueue with
+ * this FFN; the call then does the work of moe_combine_plan(plan, stream) as well, with the
+ * same results and validation (an invalid plan returns its error and enqueues nothing).
+ * For an arrival list of at most 256 entries taking the plan path, on batches that take
+ * the weight-streaming kernels (bf16 activations, fewer than 96 E_loc rows), the plan runs
+ * in one extra workgroup of the gate/up launch, on a compute unit the FFN leaves idle;
+ * otherwise it is launched on the stream before the FFN.  Either way it reads only the
+ * arrival metadata (including row_idx, so moe_assemble's pos must already be enqueued) and
+ * the token state, and it is complete when the down projection starts; follow it with
+ * moe_combine_apply(plan, ...) ordered after this call. */
+struct moe_combine_args;
 typedef struct moe_ffn_args {
   int32_t n, E_loc, H, I;
   int32_t act_dtype, w_dtype;
@@ -193,6 +205,7 @@ typedef struct moe_ffn_args {
   int64_t pool_pitch;      /* elements between pool rows */
   const int32_t* row_slot; /* optional gather-on-load index: pool row of batch row r (moe_assemble's
                               row_slot); when set it replaces perm and slot (which may be NULL) */
+  const struct moe_combine_args* plan; /* optional combine plan to run with the FFN (above) */
 } moe_ffn_args;
 
 size_t moe_ffn_workspace_size(int32_t n_max, int32_t E_loc, int32_t H, int32_t I, int32_t act_dtype);

@@ -366,6 +366,58 @@ def test_c2_skewed_batches():
             _check_step(st, e, b, wts, a, y, TOL["bf16"])
 
 
+def test_fused_plan_matches_separate_plan():
+    """The combine plan run by moe_expert_ffn_grouped (in a spare workgroup of the gate/up
+    launch for up to 256 arrivals, else launched before the FFN) gives the same bits as
+    moe_combine_plan launched on its own: combined rows, release list and count, error
+    word, masks, generations and held partial sums, with stale and duplicate arrivals."""
+    wts = W.c2_weights()
+    pool = W.c2_pool()
+    wt = weight_tensors(wts)
+    steps = []
+    for fuse in (True, False):
+        st = M.ExpertStep(8, 2880, 2880, 4, M.MOE_BF16, M.MOE_BF16, 512, 512, fuse_plan=fuse)
+        st.load_weights(wt["wg"], wt["wu"], wt["wd"])
+        steps.append(st)
+    pool_t = dev(pool, "bf16")
+    batches = [W.c2_skewed_batch(i, pool) for i in range(60)]
+    ns = np.array([bb.n for bb in batches])
+    pick = [int(np.argmin(ns)), int(np.flatnonzero((ns > 100) & (ns <= 256))[0]),
+            int(np.argmax(np.where(ns <= 256, ns, 0))), int(np.flatnonzero(ns > 256)[0])]
+    rng = np.random.default_rng(7)
+    for i in pick:
+        b = batches[i]
+        _say(f"fused plan: batch {i} n={b.n}")
+        d = batch_tensors(b)
+        d["pool"] = pool_t
+        gen, ks = b.gen.copy(), b.kslot.copy()
+        bad = rng.choice(b.n, min(4, b.n), replace=False)
+        gen[bad[:2]] += 1                              # stale generation
+        ks[bad[2:]] = (ks[bad[2:]] + 1) % b.K          # a position the token already holds
+        d["gen"], d["kslot"] = dev(gen.astype(np.uint32)), dev(ks.astype(np.int32))
+        res = []
+        for st in steps:
+            M.moe_state_reset(st.state, 0)
+            st.err.zero_()
+            st.out.zero_()
+            st.combine(d["r_rows"], d["r_idx"], d["r_tok"], d["r_kslot"], d["r_w"], d["r_gen"])
+            st.run(d["slot"], d["expert"], 0, d["pool"], d["tok"], d["kslot"], d["w"], d["gen"])
+            torch.cuda.synchronize()
+            cnt = int(st.rel_count.item())
+            mask = st.state.mask.cpu().numpy()
+            held = np.flatnonzero(mask)
+            res.append(dict(err=int(st.err.item()), cnt=cnt, rel=st.rel_list[:cnt].cpu().numpy(), mask=mask,
+                            tgen=st.state.tgen.cpu().numpy(), out=to_numpy_bits(st.out), held=held,
+                            acc=st.state.acc[torch.as_tensor(held, device="cuda").long()].cpu().numpy()))
+        f, u = res
+        assert f["err"] == u["err"] != 0
+        assert f["cnt"] == u["cnt"] and np.array_equal(f["rel"], u["rel"])
+        assert np.array_equal(f["mask"], u["mask"]) and np.array_equal(f["tgen"], u["tgen"])
+        assert np.array_equal(f["out"], u["out"])
+        assert np.array_equal(f["held"], u["held"]) and len(f["held"]) > 0
+        assert np.array_equal(f["acc"].view(np.uint32), u["acc"].view(np.uint32))
+
+
 @pytest.fixture(scope="module")
 def c4_setup():
     return W.c4_prefill_setup()
