@@ -1,6 +1,6 @@
 // Planning half of the combine for calls of up to kPlanMax arrivals, shared by the planning
-// kernel (combine.hip) and the decode gate/up kernel (ffn.hip), which runs it in one spare
-// workgroup so that the plan costs no launch and no time of its own.
+// kernel (combine.hip) and the weight-streaming gate/up kernel (ffn.hip), which runs it in
+// one extra workgroup beside its work units, so that the plan costs no launch of its own.
 //
 // [SEP] (marsggbo, "SOSP'26 | StreamEP") section 3: the first K-1 results of a token are
 // held and the K-th releases it; [NOTES] (Steven He, inferred obligations): each top-k

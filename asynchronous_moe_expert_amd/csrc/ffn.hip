@@ -332,7 +332,8 @@ __global__ __launch_bounds__(64 * WV) void ffn_mfma_kernel(const uint16_t* __res
   const int64_t strip_stride = (int64_t)KS * blk_bytes;
 
   // With a combine plan (gate/up only, m <= 256) the grid has one workgroup more than the
-  // FFN needs; that last workgroup runs the plan on a compute unit the units leave idle.
+  // FFN needs; that last workgroup runs the plan beside the units (a decode-sized batch has
+  // fewer units than compute units).
   const bool with_plan = MODE == 0 && plan.m > 0;
   if constexpr (MODE == 0) {
     if (with_plan && (int)blockIdx.x == (int)gridDim.x - 1) {

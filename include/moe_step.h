@@ -178,7 +178,8 @@ int moe_pack_ffn_weights(const moe_pack_args* args, hipStream_t stream);
  * same results and validation (an invalid plan returns its error and enqueues nothing).
  * For an arrival list of at most 256 entries taking the plan path, on batches that take
  * the weight-streaming kernels (bf16 activations, fewer than 96 E_loc rows), the plan runs
- * in one extra workgroup of the gate/up launch, on a compute unit the FFN leaves idle;
+ * in one extra workgroup of the gate/up launch, beside the FFN's work units (a decode-sized
+ * batch leaves compute units free), so it costs no launch and no time of its own;
  * otherwise it is launched on the stream before the FFN.  Either way it reads only the
  * arrival metadata (including row_idx, so moe_assemble's pos must already be enqueued) and
  * the token state, and it is complete when the down projection starts; follow it with
