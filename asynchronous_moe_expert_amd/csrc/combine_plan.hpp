@@ -67,8 +67,9 @@ struct PlanJob {
 
 // T threads: kPlanThreads, or 256 for calls of at most 256 arrivals (every decode step), where a
 // quarter of the waves makes each workgroup barrier cheaper; or the 384 threads of the decode
-// gate/up launch, which runs the plan in a spare workgroup.  Takes m <= T arrivals; every
-// thread of the workgroup calls it (it has workgroup barriers).
+// gate/up launch, which runs the plan in a spare workgroup.  Takes m arrivals whose next
+// power of two is at most T (m <= 256 for the 384-thread case); every thread of the
+// workgroup calls it (it has workgroup barriers).
 template <int T>
 __device__ __forceinline__ void combine_plan_body(const PlanJob& job) {
   const int m = job.m, K = job.K, T_cap = job.T_cap;

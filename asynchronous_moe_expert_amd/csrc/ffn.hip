@@ -513,7 +513,8 @@ static void launch_mfma_t(const void* A, const int32_t* offsets, int E_loc, cons
                           const PlanJob& plan, hipStream_t stream) {
   constexpr int BM = MT * 16;
   constexpr auto kernel = ffn_mfma_kernel<MODE, WDT, NS, MT, R, WV>;
-  static_assert(MODE == 1 || kPlanFusedMax <= 64 * WV, "a fused plan takes m <= the workgroup's threads");
+  static_assert(MODE == 1 || kPlanFusedMax <= 64 * WV, "a fused plan rounds m up to a power of two <= the threads");
+  static_assert((kPlanFusedMax & (kPlanFusedMax - 1)) == 0, "kPlanFusedMax is a power of two");
   const int n_blocks_N = (Nw / 16 + WV * NS - 1) / (WV * NS);
   const int64_t chunks_max = (n + (int64_t)(BM - 1) * E_loc) / BM;  // ragged worst case
   int64_t grid = std::min<int64_t>(chunks_max * n_blocks_N, resident_workgroups<kernel>(64 * WV));
