@@ -43,7 +43,7 @@ class FfnArgs(C.Structure):
                 ("xb", _p), ("offsets", _p), ("w_gu", _p), ("w_d", _p), ("s_gate", _p), ("s_up", _p),
                 ("s_down", _p), ("y", _p), ("workspace", _p), ("workspace_bytes", C.c_size_t), ("ev_mid", _p),
                 ("perm", _p), ("slot", _p), ("pool", _p), ("P", _i64), ("pool_pitch", _i64), ("row_slot", _p),
-                ("plan", _p)]
+                ("plan", _p), ("ev_gu_start", _p), ("ev_gu_stop", _p)]
 
 
 class StateC(C.Structure):
@@ -165,11 +165,13 @@ def moe_pack_ffn_weights(wg, wu, wd, w_gu, w_d, w_dtype: int, stream=None) -> No
 
 def moe_expert_ffn_grouped(n: int, E_loc: int, H: int, I: int, act_dtype: int, w_dtype: int, xb, offsets, w_gu,
                            w_d, y, workspace, s_gate=None, s_up=None, s_down=None, ev_mid: int | None = None,
-                           stream=None, gather=None, plan: "CombineArgs | None" = None) -> None:
+                           stream=None, gather=None, plan: "CombineArgs | None" = None,
+                           ev_gu: tuple[int, int] | None = None) -> None:
     """gather=(perm, slot, pool) or (perm, slot, pool, row_slot): read batch rows from the pool
     (gather-on-load; with row_slot, pool row row_slot[r] and perm/slot unused); xb may be None.
     plan: the arguments (combine_args) of a moe_combine_plan call that this call enqueues as
-    well, inside the gate/up launch where it fits."""
+    well, inside the gate/up launch where it fits.  ev_gu: (start, stop) hipEvent_t handles
+    that the weight-streaming gate/up kernel records around itself."""
     perm = slot = pool = row_slot = None
     P = pitch = 0
     if gather is not None:
@@ -179,7 +181,7 @@ def moe_expert_ffn_grouped(n: int, E_loc: int, H: int, I: int, act_dtype: int, w
     a = FfnArgs(n, E_loc, H, I, act_dtype, w_dtype, _ptr(xb), _ptr(offsets), _ptr(w_gu), _ptr(w_d),
                 _ptr(s_gate), _ptr(s_up), _ptr(s_down), _ptr(y), _ptr(workspace),
                 workspace.numel() * workspace.element_size(), ev_mid, _ptr(perm), _ptr(slot), _ptr(pool), P, pitch,
-                _ptr(row_slot), None if plan is None else C.addressof(plan))
+                _ptr(row_slot), None if plan is None else C.addressof(plan), *(ev_gu or (None, None)))
     _check(load().moe_expert_ffn_grouped(C.byref(a), _stream(stream)), "moe_expert_ffn_grouped")
 
 

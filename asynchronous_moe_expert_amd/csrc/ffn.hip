@@ -29,6 +29,8 @@
 //     bf16 value) and the per-row scale is applied to the fp32 result in the epilogue.
 //   * Units are spread XCD-aware: each XCD gets an equal contiguous range of unit ids, so
 //     the chunks that share a weight tile run on one XCD's L2 (reuse for big experts).
+#include <hip/hip_ext.h>
+
 #include <algorithm>
 #include <type_traits>
 #include <utility>
@@ -510,7 +512,7 @@ static int resident_workgroups(int threads) {
 template <int MODE, int WDT, int NS, int MT, int R, int WV>
 static void launch_mfma_t(const void* A, const int32_t* offsets, int E_loc, const void* W, const float* s0,
                           const float* s1, void* out, int Kd, int Nw, int out_ld, int n, GatherRows gr,
-                          const PlanJob& plan, hipStream_t stream) {
+                          const PlanJob& plan, hipEvent_t ev0, hipEvent_t ev1, hipStream_t stream) {
   constexpr int BM = MT * 16;
   constexpr auto kernel = ffn_mfma_kernel<MODE, WDT, NS, MT, R, WV>;
   static_assert(MODE == 1 || kPlanFusedMax <= 64 * WV, "a fused plan rounds m up to a power of two <= the threads");
@@ -520,8 +522,10 @@ static void launch_mfma_t(const void* A, const int32_t* offsets, int E_loc, cons
   int64_t grid = std::min<int64_t>(chunks_max * n_blocks_N, resident_workgroups<kernel>(64 * WV));
   grid = (grid + 7) / 8 * 8;  // the XCD-aware order needs a multiple of 8
   if (MODE == 0 && plan.m > 0) grid += 1;  // the plan's workgroup
-  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(64 * WV), 0, stream, (const uint16_t*)A, offsets, E_loc,
-                     (const char*)W, s0, s1, (uint16_t*)out, Kd, Nw, out_ld, n_blocks_N, n, gr, plan);
+  // (ev0, ev1: timestamps taken by the dispatch itself, or none)
+  hipExtLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(64 * WV), 0, stream, ev0, ev1, 0, (const uint16_t*)A,
+                        offsets, E_loc, (const char*)W, s0, s1, (uint16_t*)out, Kd, Nw, out_ld, n_blocks_N, n, gr,
+                        plan);
 }
 
 // ------------------------------------------------------------ prefill GEMM path
@@ -1119,7 +1123,7 @@ static bool takes_gemm(int n, int E_loc, int Kd, const GatherRows& gr) {
 template <int MODE, int WDT>
 static void launch_mfma(const void* A, const int32_t* offsets, int E_loc, const void* W, const float* s0,
                         const float* s1, void* out, int Kd, int Nw, int out_ld, int n, GatherRows gr, float* parts,
-                        const PlanJob& plan, hipStream_t stream) {
+                        const PlanJob& plan, hipEvent_t ev0, hipEvent_t ev1, hipStream_t stream) {
   constexpr int NS = MODE == 0 ? MOE_FFN_NS_GU : MOE_FFN_NS_D;
   constexpr int R = MODE == 0 ? MOE_FFN_R_GU : MOE_FFN_R_D;
   constexpr int WV = MODE == 0 ? MOE_FFN_WV_GU : MOE_FFN_WV_D;
@@ -1129,10 +1133,12 @@ static void launch_mfma(const void* A, const int32_t* offsets, int E_loc, const 
   }
   switch (pick_mt(n, E_loc)) {
     case 2:
-      launch_mfma_t<MODE, WDT, NS, 2, R, WV>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, gr, plan, stream);
+      launch_mfma_t<MODE, WDT, NS, 2, R, WV>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, gr, plan, ev0, ev1,
+                                             stream);
       break;
     default:
-      launch_mfma_t<MODE, WDT, NS, 3, R, WV>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, gr, plan, stream);
+      launch_mfma_t<MODE, WDT, NS, 3, R, WV>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, gr, plan, ev0, ev1,
+                                             stream);
       break;
   }
 }
@@ -1241,6 +1247,9 @@ extern "C" int moe_expert_ffn_grouped(const moe_ffn_args* a, hipStream_t stream)
     if (rc != MOE_OK) return rc;
   }
   const PlanJob no_plan{};
+  // the gate/up kernel's own start/stop timestamps, when asked for as a pair
+  const bool ev_pair = a->ev_gu_start && a->ev_gu_stop;
+  const hipEvent_t ev0 = ev_pair ? a->ev_gu_start : nullptr, ev1 = ev_pair ? a->ev_gu_stop : nullptr;
   if (f32) {
     const int64_t t1 = (int64_t)n * I, t2 = (int64_t)n * H;
     hipLaunchKernelGGL(gateup_f32_kernel, dim3((unsigned)((t1 + 255) / 256)), dim3(256), 0, stream,
@@ -1252,16 +1261,16 @@ extern "C" int moe_expert_ffn_grouped(const moe_ffn_args* a, hipStream_t stream)
   }
   if (bf) {
     launch_mfma<0, MOE_BF16>(x_src, a->offsets, E, a->w_gu, nullptr, nullptr, a->workspace, H, 2 * I, I, n, gr, parts,
-                             job, stream);
+                             job, ev0, ev1, stream);
     if (a->ev_mid) (void)hipEventRecord(a->ev_mid, stream);
     launch_mfma<1, MOE_BF16>(a->workspace, a->offsets, E, a->w_d, nullptr, nullptr, a->y, I, H, H, n, none, parts,
-                             no_plan, stream);
+                             no_plan, nullptr, nullptr, stream);
   } else {
     launch_mfma<0, MOE_FP8_E4M3>(x_src, a->offsets, E, a->w_gu, a->s_gate, a->s_up, a->workspace, H, 2 * I, I, n, gr,
-                                 parts, job, stream);
+                                 parts, job, ev0, ev1, stream);
     if (a->ev_mid) (void)hipEventRecord(a->ev_mid, stream);
     launch_mfma<1, MOE_FP8_E4M3>(a->workspace, a->offsets, E, a->w_d, a->s_down, nullptr, a->y, I, H, H, n, none,
-                                 parts, no_plan, stream);
+                                 parts, no_plan, nullptr, nullptr, stream);
   }
   return launch_status();
 }

@@ -79,10 +79,10 @@ class ExpertStep:
                        xb, self.err, n=n, stream=stream, row_slot=rs)
         self._gather = (self.perm, slot, pool, rs) if self.gather_on_load else None
 
-    def ffn(self, n: int, ev_mid: int | None = None, stream=None, plan=None) -> None:
+    def ffn(self, n: int, ev_mid: int | None = None, stream=None, plan=None, ev_gu=None) -> None:
         N.moe_expert_ffn_grouped(n, self.E_loc, self.H, self.I, self.act_dtype, self.w_dtype, self.xb, self.offsets,
                                  self.w_gu, self.w_d, self.y, self.workspace, self.s_gate, self.s_up, self.s_down,
-                                 ev_mid=ev_mid, stream=stream, gather=self._gather, plan=plan)
+                                 ev_mid=ev_mid, stream=stream, gather=self._gather, plan=plan, ev_gu=ev_gu)
 
     def _combine_room(self, m: int) -> None:
         if m > self.cmb_ws_m:  # plumbing: grow the caller-owned scratch (outside any timed loop)

@@ -161,6 +161,10 @@ int moe_pack_ffn_weights(const moe_pack_args* args, hipStream_t stream);
  * rounding order).  Results are deterministic for a given device and workspace size.
  * ev_mid: optional hipEvent_t recorded on the stream between the gate/up kernel and
  * the down kernel (for timing); pass NULL otherwise.
+ * ev_gu_start, ev_gu_stop: optional hipEvent_t pair (both or neither) that the
+ * weight-streaming gate/up kernel records in its own dispatch, at its start and at its end,
+ * so that hipEventElapsedTime gives that kernel's duration alone (for roofline figures);
+ * not recorded when the batch takes the tiled GEMM path or the fp32 kernels.
  *
  * Gather-on-load ([SEP] section 6 fuses the gather of scattered token vectors into the
  * computation that consumes them): when perm != NULL the gate/up projection reads batch
@@ -207,6 +211,8 @@ typedef struct moe_ffn_args {
   const int32_t* row_slot; /* optional gather-on-load index: pool row of batch row r (moe_assemble's
                               row_slot); when set it replaces perm and slot (which may be NULL) */
   const struct moe_combine_args* plan; /* optional combine plan to run with the FFN (above) */
+  hipEvent_t ev_gu_start;  /* optional, with ev_gu_stop: gate/up kernel duration (above) */
+  hipEvent_t ev_gu_stop;
 } moe_ffn_args;
 
 size_t moe_ffn_workspace_size(int32_t n_max, int32_t E_loc, int32_t H, int32_t I, int32_t act_dtype);
