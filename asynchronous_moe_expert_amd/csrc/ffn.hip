@@ -1052,23 +1052,26 @@ __global__ __launch_bounds__(256) void ffn_gemm_finalize_kernel(const int32_t* _
   gemm_store_group<MODE>(a, bb, mt, g, m0, mend, col0, hf, l32, sc0, sc1, out, out_ld);
 }
 
-// parts: kGemmSplitSlots partial tiles of workspace, or nullptr (tail units run whole)
+// parts: kGemmSplitSlots partial tiles of workspace, or nullptr (tail units run whole).
+// ev0, ev1: optional timestamps taken by the dispatches themselves, at the start of the GEMM
+// and at the end of the last launch of the projection (the finalize, if any).
 template <int MODE, int WDT>
 static void launch_gemm(const void* A, const int32_t* offsets, int E_loc, const void* W, const float* s0,
                         const float* s1, void* out, int Kd, int Nw, int out_ld, int n, GatherRows gr, float* parts,
-                        hipStream_t stream) {
+                        hipEvent_t ev0, hipEvent_t ev1, hipStream_t stream) {
   constexpr auto kernel = ffn_gemm_kernel<MODE, WDT>;
   const int n_blocks_N = (Nw + kGemmBN - 1) / kGemmBN;
   const int64_t chunks_max = (n + (int64_t)(kGemmBM - 1) * E_loc) / kGemmBM;
   int64_t grid = std::min<int64_t>(chunks_max * n_blocks_N, resident_workgroups<kernel>(256));
   grid = (grid + 7) / 8 * 8;
   if (grid > kGemmSplitSlots) parts = nullptr;
-  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), 0, stream, (const uint16_t*)A, offsets, E_loc,
-                     (const char*)W, s0, s1, (uint16_t*)out, Kd, Nw, out_ld, n_blocks_N, n, gr, parts);
+  hipExtLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), 0, stream, ev0, parts ? nullptr : ev1, 0,
+                        (const uint16_t*)A, offsets, E_loc, (const char*)W, s0, s1, (uint16_t*)out, Kd, Nw, out_ld,
+                        n_blocks_N, n, gr, parts);
   if (parts)
-    hipLaunchKernelGGL((ffn_gemm_finalize_kernel<MODE, WDT>), dim3((unsigned)(8 * grid)), dim3(256), 0, stream, offsets,
-                       E_loc, n, n_blocks_N, Kd / kBK, (int)grid, (const float*)parts, s0, s1, (uint16_t*)out, Nw,
-                       out_ld);
+    hipExtLaunchKernelGGL((ffn_gemm_finalize_kernel<MODE, WDT>), dim3((unsigned)(8 * grid)), dim3(256), 0, stream,
+                          nullptr, ev1, 0, offsets, E_loc, n, n_blocks_N, Kd / kBK, (int)grid, (const float*)parts, s0,
+                          s1, (uint16_t*)out, Nw, out_ld);
 }
 
 // Row-chunk height: tall enough that an average expert group fits one chunk with room for
@@ -1128,7 +1131,7 @@ static void launch_mfma(const void* A, const int32_t* offsets, int E_loc, const 
   constexpr int R = MODE == 0 ? MOE_FFN_R_GU : MOE_FFN_R_D;
   constexpr int WV = MODE == 0 ? MOE_FFN_WV_GU : MOE_FFN_WV_D;
   if (takes_gemm(n, E_loc, Kd, gr)) {
-    launch_gemm<MODE, WDT>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, gr, parts, stream);
+    launch_gemm<MODE, WDT>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, gr, parts, ev0, ev1, stream);
     return;
   }
   switch (pick_mt(n, E_loc)) {

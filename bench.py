@@ -448,6 +448,20 @@ def run_prefill(args) -> int:
             if rep >= W_reps:
                 for k, nm in enumerate(names):
                     times[w][nm].append(ev.ms(evs[k], evs[k + 1]))
+    # the gate/up projection's kernel time alone (start/stop events taken by its own
+    # dispatches), in a pass of its own so that these events stay out of the intervals above
+    gs, ge = ev.create(), ev.create()
+    gu_kernel = {w: [] for w in range(nw)}
+    for rep in range(reps):
+        for w, b in enumerate(waves):
+            d = dw[w]
+            M.moe_state_reset(st.state, 0)
+            st.combine(d["r_rows"], d["r_idx"], d["r_tok"], d["r_kslot"], d["r_w"], d["r_gen"])
+            st.assemble(d["slot"], d["expert"], b.expert_base, pool, n=b.n)
+            st.ffn(b.n, ev_gu=(gs, ge))
+            st.combine(st.y, st.pos, d["tok"], d["kslot"], d["w"], d["gen"], m=b.n, n_rows=b.n)
+            torch.cuda.synchronize()
+            gu_kernel[w].append(ev.ms(gs, ge))
     med = {w: {nm: float(np.median(times[w][nm])) for nm in names} for w in range(nw)}
     step_ms = sum(sum(med[w].values()) for w in range(nw))
     n_tot = sum(b.n for b in waves)
@@ -461,11 +475,13 @@ def run_prefill(args) -> int:
         # the row gather is fused into the gate/up GEMM's activation loads (the assemble
         # stage builds the index only), so it has no time of its own to price
         per_wave.append({"pairs": n, "us": {k: round(v * 1e3, 2) for k, v in m.items()},
+                         "gate_up_kernel_us": round(float(np.median(gu_kernel[w])) * 1e3, 2),
                          "ffn_mfma_frac": round((fl_gu + fl_dn) / ((m["gate_up"] + m["down"]) * 1e-3) / 1e12
                                                 / BF16_PEAK_TFLOPS, 4),
                          "combine_hbm_frac": round(c_bytes / (m["combine"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
     b0, m0 = waves[0], med[0]
-    gu_tf = 4.0 * b0.n * H * I / (m0["gate_up"] * 1e-3) / 1e12
+    gu0_ms = float(np.median(gu_kernel[0]))
+    gu_tf = 4.0 * b0.n * H * I / (gu0_ms * 1e-3) / 1e12
     out = {
         "metric": "expert tokens/sec per GPU (assemble+FFN+combine)",
         "value": round(value, 1), "unit": "expert tokens/s", "n_gpus": 1, "steps": reps * nw, "warmup": W_reps * nw,
@@ -476,10 +492,11 @@ def run_prefill(args) -> int:
                    "E_loc": E, "K": K, "H": H, "I": I, "pairs": n_tot, "pool_slots": P, "waves_per_step": g},
         "roofline": {"bound": "mfma", "kernel": f"ffn gate/up GEMM, first step ({b0.n} pairs)", "achieved": round(gu_tf, 1),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(gu_tf / BF16_PEAK_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": None, "kernel_us": round(gu0_ms * 1e3, 2)},
         "waves": per_wave,
         "note": "per-stage medians of HIP-event intervals on the launch stream; each step is timed alone "
-                "(state reset and remote delivery untimed before it)",
+                "(state reset and remote delivery untimed before it); gate_up_kernel_us and roofline.kernel_us: "
+                "the gate/up GEMM and its finalize alone, from events its dispatches record, in a separate pass",
     }
     out["cpu_baseline"] = cpu_baseline_prefill(setup, W.c4_wave(setup, 0, with_remote=False), args.cpu_seconds) \
         if args.cpu_seconds > 0 else None

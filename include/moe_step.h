@@ -161,10 +161,11 @@ int moe_pack_ffn_weights(const moe_pack_args* args, hipStream_t stream);
  * rounding order).  Results are deterministic for a given device and workspace size.
  * ev_mid: optional hipEvent_t recorded on the stream between the gate/up kernel and
  * the down kernel (for timing); pass NULL otherwise.
- * ev_gu_start, ev_gu_stop: optional hipEvent_t pair (both or neither) that the
- * weight-streaming gate/up kernel records in its own dispatch, at its start and at its end,
- * so that hipEventElapsedTime gives that kernel's duration alone (for roofline figures);
- * not recorded when the batch takes the tiled GEMM path or the fp32 kernels.
+ * ev_gu_start, ev_gu_stop: optional hipEvent_t pair (both or neither) that the gate/up
+ * projection's own dispatches record: at the start of its kernel and at the end of its last
+ * launch (the tiled GEMM path's finalize, when it runs one), so that hipEventElapsedTime
+ * gives the projection's kernel time alone (for roofline figures); not recorded by the fp32
+ * kernels.
  *
  * Gather-on-load ([SEP] section 6 fuses the gather of scattered token vectors into the
  * computation that consumes them): when perm != NULL the gate/up projection reads batch

@@ -40,3 +40,34 @@ def dev(a, dtype=None):
 def sync_err(t: torch.Tensor) -> int:
     torch.cuda.synchronize()
     return int(t.item()) & 0xFFFFFFFF
+
+
+class HipEvents:
+    """Raw hipEvent_t handles through the HIP runtime (for the library's event arguments)."""
+
+    def __init__(self):
+        import ctypes as C
+        self.C = C
+        self.hip = C.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.hip.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [C.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [C.c_void_p]
+
+    def create(self) -> int:
+        e = self.C.c_void_p()
+        assert self.hip.hipEventCreate(self.C.byref(e)) == 0
+        return e.value
+
+    def record(self, ev: int, stream: int) -> None:
+        assert self.hip.hipEventRecord(self.C.c_void_p(ev), self.C.c_void_p(stream)) == 0
+
+    def ms(self, a: int, b: int) -> float:
+        assert self.hip.hipEventSynchronize(self.C.c_void_p(b)) == 0
+        out = self.C.c_float()
+        assert self.hip.hipEventElapsedTime(self.C.byref(out), self.C.c_void_p(a), self.C.c_void_p(b)) == 0
+        return float(out.value)
+
+    def destroy(self, ev: int) -> None:
+        self.hip.hipEventDestroy(self.C.c_void_p(ev))

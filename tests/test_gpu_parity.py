@@ -8,7 +8,7 @@ import torch
 import asynchronous_moe_expert_amd as M
 import oracle as O
 import workloads as W
-from gpu_helpers import TOL, decode_tensor, dev, row_rel_err, sync_err
+from gpu_helpers import TOL, HipEvents, decode_tensor, dev, row_rel_err, sync_err
 from workloads.device import batch_tensors, to_numpy_bits, weight_tensors
 
 pytestmark = pytest.mark.gpu
@@ -323,6 +323,35 @@ def test_c1_decode_overlapped_step():
     st, e = _run_config_step(b, wts, M.MOE_BF16, M.MOE_BF16, overlap=True)
     a, y = _oracle_step(b, wts)
     _check_step(st, e, b, wts, a, y, TOL["bf16"])
+
+
+def test_gate_up_dispatch_events():
+    """The gate/up kernel's own start/stop events (moe_ffn_args.ev_gu_start / ev_gu_stop):
+    the FFN gives the same bits with and without them, and the duration they record is
+    positive and inside the interval of events recorded around the whole call."""
+    _say("C1 decode FFN with the gate/up dispatch events")
+    b, wts = W.c1_decode()
+    d = batch_tensors(b)
+    wt = weight_tensors(wts)
+    st = M.ExpertStep(b.E_loc, b.H, wts.I, b.K, M.MOE_BF16, M.MOE_BF16, b.n, b.T)
+    st.load_weights(wt["wg"], wt["wu"], wt["wd"])
+    st.assemble(d["slot"], d["expert"], b.expert_base, d["pool"])
+    st.ffn(b.n)
+    torch.cuda.synchronize()
+    y0 = to_numpy_bits(st.y[: b.n])
+    hip = HipEvents()
+    ev = [hip.create() for _ in range(4)]
+    stream = torch.cuda.current_stream().cuda_stream
+    hip.record(ev[0], stream)
+    st.ffn(b.n, ev_gu=(ev[1], ev[2]))
+    hip.record(ev[3], stream)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_numpy_bits(st.y[: b.n]), y0)
+    kernel, whole = hip.ms(ev[1], ev[2]), hip.ms(ev[0], ev[3])
+    _say(f"  gate/up kernel {kernel * 1e3:.1f} us of {whole * 1e3:.1f} us")
+    assert 0.0 < kernel < whole
+    for e in ev:
+        hip.destroy(e)
 
 
 def test_c1_decode_other_rank():
