@@ -126,6 +126,9 @@ def main() -> int:
     ap.add_argument("--batches", type=int, default=1000, help="expert batches of the stream workload")
     ap.add_argument("--merge", type=int, choices=[1, 2, 4], default=1,
                     help="prefill: consecutive waves merged into one ready batch (1 = each wave alone)")
+    ap.add_argument("--weight-copies", type=int, default=4,
+                    help="decode: packed copies of the layer's weights the steps cycle through (so that no step "
+                         "finds weights left in the caches by the one before, as in a model of many layers)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="copy 256 MiB device to device once before the warm-up (reference dispatch for "
                          "rocprofv3 byte counters)")
@@ -156,6 +159,11 @@ def main() -> int:
     st = M.ExpertStep(b.E_loc, b.H, wts.I, b.K, M.MOE_BF16, M.MOE_BF16, b.n, S * b.T)
     st.load_weights(wt["wg"], wt["wu"], wt["wd"])
     del wt
+    # copies of the packed weights at distinct addresses; step s uses copy s % L, so the
+    # weights a step streams (398 MB) were last read L steps earlier, with L x 398 MB of
+    # other weights in between: more than the 256 MB last-level cache holds
+    L = max(1, args.weight_copies)
+    w_copies = [(st.w_gu, st.w_d)] + [(st.w_gu.clone(), st.w_d.clone()) for _ in range(L - 1)]
     # per-step token indices (each step completes tokens of its own) and the remote
     # results of every step's tokens, delivered before timing
     tok_steps = [d["tok"] + s * b.T for s in range(S)]
@@ -176,11 +184,13 @@ def main() -> int:
     e_start = ev.create()
 
     def step(s: int) -> None:
+        st.w_gu, st.w_d = w_copies[s % L]
         st.run(d["slot"], d["expert"], b.expert_base, d["pool"], tok_steps[s], d["kslot"], d["w"], d["gen"], n=b.n)
 
     def step_timed(s: int) -> None:
         # the same calls as ExpertStep.run (the combine plan inside the FFN call, then the
         # apply) with HIP events between them on the launch stream
+        st.w_gu, st.w_d = w_copies[s % L]
         st.assemble(d["slot"], d["expert"], b.expert_base, d["pool"])
         ev.record(e_asm[s], stream)
         plan = st.local_combine_args(tok_steps[s], d["kslot"], d["w"], d["gen"], b.n)
@@ -241,7 +251,8 @@ def main() -> int:
         "data": "synthetic (seeded; random-init expert weights)",
         "config": {"workload": "decode-shaped EP rank share: 8 of 128 experts, top-4, hidden 2880, SwiGLU "
                                "intermediate 2880, 256 token-expert pairs from a 4096-slot token pool",
-                   "E_loc": b.E_loc, "K": b.K, "H": H, "I": I, "pairs": n, "tokens": b.T, "pool_slots": b.P},
+                   "E_loc": b.E_loc, "K": b.K, "H": H, "I": I, "pairs": n, "tokens": b.T, "pool_slots": b.P,
+                   "weight_copies": L},
         "roofline": {"bound": "hbm", "kernel": "ffn_mfma_kernel<gate/up, bf16>", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": stored_traffic(), "algorithmic_bytes": gu_bytes,
