@@ -138,6 +138,25 @@ def test_ffn_empty_batch_is_a_no_op():
     assert torch.all(st.y == 3.0)
 
 
+@pytest.mark.parametrize("fuse_plan", [True, False])
+def test_empty_step_releases_nothing(fuse_plan):
+    """A whole step on an empty queue (n = 0): the FFN call still enqueues the (empty)
+    combine plan; nothing is accepted or released and the token state is unchanged."""
+    st = M.ExpertStep(2, 64, 64, 2, M.MOE_BF16, M.MOE_BF16, 4, 8, fuse_plan=fuse_plan)
+    z = torch.zeros((2, 64, 64), dtype=torch.bfloat16, device="cuda")
+    st.load_weights(z, z, z)
+    M.moe_state_reset(st.state, 5)
+    st.err.zero_()
+    st.rel_count.fill_(-1)
+    mask0, tgen0 = st.state.mask.clone(), st.state.tgen.clone()
+    pool = torch.zeros((4, 64), dtype=torch.bfloat16, device="cuda")
+    i32 = lambda: torch.zeros(0, dtype=torch.int32, device="cuda")  # noqa: E731
+    st.run(i32(), i32(), 0, pool, i32(), i32(), torch.zeros(0, dtype=torch.float32, device="cuda"), i32())
+    torch.cuda.synchronize()
+    assert int(st.err.item()) == 0 and int(st.rel_count.item()) == 0
+    assert torch.equal(st.state.mask, mask0) and torch.equal(st.state.tgen, tgen0)
+
+
 # --------------------------------------------------------------------------- combine
 def _combine_call(st, rows_t, rows64, arr, ocs, K):
     """Run one combine call on GPU and oracle; compare err, rel list and state."""
