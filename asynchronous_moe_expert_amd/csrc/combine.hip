@@ -76,7 +76,9 @@ struct RowIO<uint16_t> {
   }
 };
 
-constexpr int kCmbThreads = 256;
+// apply workgroup: 384 threads cover a 2880-wide bf16 row (360 vectors of 8) in one pass
+// (256 threads took two for 104 of them: decode combine 7.5 -> 6.7 us)
+constexpr int kCmbThreads = 384;
 #ifndef MOE_MERGE_THREADS
 #define MOE_MERGE_THREADS 256
 #endif
