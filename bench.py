@@ -134,8 +134,8 @@ def main() -> int:
                          "rocprofv3 byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs one expert-parallel rank's share on a single GPU; multi-GPU runs are not part "
-              "of this build (use --gpus 1)", file=sys.stderr)
+        print("bench.py runs one expert-parallel rank's share on a single GPU; it has no multi-GPU mode "
+              "(use --gpus 1)", file=sys.stderr)
         return 2
 
     if args.workload == "prefill":

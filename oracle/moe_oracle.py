@@ -7,7 +7,7 @@ constants); the error-flag values below are the documented contract, restated he
 
 What it computes, and where the pages define it
 -----------------------------------------------
-Sources (the web pages this build follows):
+Sources (web pages, cited by title and section):
   [SEP]  marsggbo, "SOSP'26 | StreamEP" blog post (sections numbered as on the page)
   [NOTES] Steven He, "asynchronous MoE serving: StreamEP, buffering, and progress"
           (section "inferred obligations for a concrete protocol")
