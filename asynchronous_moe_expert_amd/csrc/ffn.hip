@@ -1065,6 +1065,10 @@ static void launch_gemm(const void* A, const int32_t* offsets, int E_loc, const 
   int64_t grid = std::min<int64_t>(chunks_max * n_blocks_N, resident_workgroups<kernel>(256));
   grid = (grid + 7) / 8 * 8;
   if (grid > kGemmSplitSlots) parts = nullptr;
+  // The down projection's units are half as long (K = I), so a split tail saves less than the
+  // finalize launch and the partial tiles cost; it runs whole tail units (prefill waves of
+  // 6554 / 4915 / 3277 pairs: down 4-7, 6-8 and 16-20 us faster than with the split).
+  if (MODE == 1) parts = nullptr;
   hipExtLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), 0, stream, ev0, parts ? nullptr : ev1, 0,
                         (const uint16_t*)A, offsets, E_loc, (const char*)W, s0, s1, (uint16_t*)out, Kd, Nw, out_ld,
                         n_blocks_N, n, gr, parts);
