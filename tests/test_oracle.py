@@ -106,6 +106,25 @@ def test_gather_is_byte_exact_and_page_payload_size(golden):
     assert np.array_equal(xb, pool[slot])
 
 
+def test_gather_follows_perm_for_a_scrambled_multi_expert_queue():
+    """[SEP] section 3: the scattered token vectors of a queue become one contiguous batch,
+    here grouped by expert.  With several experts in a shuffled queue the batch order is far
+    from the queue order, so a gather that ignored perm (rows in queue order) fails."""
+    rng = np.random.default_rng(11)
+    P, H, E_loc, n = 96, 6, 5, 40
+    pool = rng.integers(0, 65536, size=(P, H)).astype(np.uint16)
+    slot = rng.permutation(P)[:n]
+    expert = rng.integers(0, E_loc, size=n)
+    a = O.assemble(slot, expert, 0, E_loc, P)
+    _, perm = _brute_assemble(list(slot), list(expert), 0, E_loc, P)
+    expected = np.stack([pool[slot[i]] for i in perm])  # expert ascending, queue order inside
+    assert not np.array_equal(pool[slot], expected)
+    assert np.array_equal(O.gather_rows(pool, slot, a["perm"], int(a["offsets"][-1])), expected)
+    # the row index is slot[perm[r]] for any perm (here a reversal of the queue)
+    rev = np.arange(n)[::-1]
+    assert np.array_equal(O.gather_rows(pool, slot, rev, n), pool[slot[::-1]])
+
+
 def test_request37_queue_assembles_in_queue_order(golden):
     g = golden("streamep_request37_queue.json")
     rng = np.random.default_rng(37)
