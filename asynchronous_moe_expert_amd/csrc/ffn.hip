@@ -32,6 +32,7 @@
 #include <hip/hip_ext.h>
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 #include <utility>
 
@@ -493,19 +494,24 @@ __global__ __launch_bounds__(64 * WV) void ffn_mfma_kernel(const uint16_t* __res
 }
 
 // Workgroups of one kernel that the device holds at once (its CU count times the kernel's
-// occupancy), cached per device for each kernel (the template argument is the kernel).
+// occupancy), cached per device for each kernel (the template argument is the kernel).  The
+// cache holds read-only device properties: concurrent first calls compute the same value and
+// store it with an atomic.
 template <auto Kernel>
 static int resident_workgroups(int threads) {
   constexpr int kMaxDev = 64;
-  static int cache[kMaxDev];  // 0 = not yet known; racing writers store the same value
+  static std::atomic<int> cache[kMaxDev];  // 0 = not yet known
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) dev = -1;
-  if (dev >= 0 && cache[dev] > 0) return cache[dev];
+  if (dev >= 0) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) != hipSuccess) cus = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, Kernel, threads, 0) != hipSuccess) per_cu = 0;
   const int r = cus > 0 && per_cu > 0 ? cus * per_cu : 1024;
-  if (dev >= 0) cache[dev] = r;
+  if (dev >= 0) cache[dev].store(r, std::memory_order_relaxed);
   return r;
 }
 

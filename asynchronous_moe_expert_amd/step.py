@@ -149,7 +149,9 @@ class SharedExpert:
         dev = torch.device(device)
         self._zero = torch.zeros(max(n_max, 1), dtype=torch.int32, device=dev)
         self._one = torch.ones(max(n_max, 1), dtype=torch.float32, device=dev)
-        self._kslot = torch.empty(max(n_max, 1), dtype=torch.int32, device=dev)
+        self._kslots: dict[int, torch.Tensor] = {}  # kslot -> constant [n_max] tensor, never written again
+        self._dev = dev
+        torch.cuda.synchronize(dev)  # the constants above are complete before any stream reads them
 
     def load_weights(self, wg, wu, wd, s_gate=None, s_up=None, s_down=None, stream=None) -> None:
         """wg, wu: [1][I][H], wd: [1][H][I] (one expert)."""
@@ -162,5 +164,11 @@ class SharedExpert:
         s = self.step
         s.assemble(slot, self._zero[:n], 0, pool, n=n, stream=stream)
         s.ffn(n, stream=stream)
-        self._kslot[:n].fill_(kslot)
-        owner.combine(s.y, s.pos, tok, self._kslot[:n], self._one[:n], gen, m=n, n_rows=n, stream=stream)
+        ks = self._kslots.get(kslot)
+        if ks is None:
+            # one-time setup per position: filled and synchronised before any combine reads it,
+            # and never written again, so calls on any stream may share it
+            ks = torch.full((max(self.n_max, 1),), kslot, dtype=torch.int32, device=self._dev)
+            torch.cuda.synchronize(self._dev)
+            self._kslots[kslot] = ks
+        owner.combine(s.y, s.pos, tok, ks[:n], self._one[:n], gen, m=n, n_rows=n, stream=stream)

@@ -1,28 +1,32 @@
 """Benchmark: one expert-parallel rank's expert step on one MI355X.
 
-Workload (decode-shaped rank share): 128 experts, top-4, 16 ranks -> 8 local experts,
-hidden 2880, SwiGLU intermediate 2880, bf16; 256 token-expert pairs gathered from random
-slots of a 4096-slot token pool, uniform routing, weights ~ N(0, 0.02).
+Default workload (the largest single-GPU configuration): the prefill-shaped rank share.
+256 experts, top-8, 32 local experts, hidden 4096, SwiGLU intermediate 2048, fp8 e4m3
+weights (fp32 row scales) with bf16 activations and fp32 accumulation; 16384 token-expert
+pairs with Zipf(1.0) routing arrive in four waves of 6554 / 4915 / 3277 / 1638 pairs, and
+each wave is one step (CascadeEP's and ASAP's prefill setting: expert work starts on each
+wave of ready tokens as attention replicas finish).
 
-A step = moe_assemble + moe_expert_ffn_grouped + moe_combine_release on one batch, all
-inputs resident in HBM.  Each step combines its local results into tokens of its own
-(distinct state indices per step), whose results from the other 15 ranks were delivered
-before the timed region; every step therefore releases all of its tokens.
+A step = moe_assemble + moe_expert_ffn_grouped + moe_combine_release on one ready batch,
+all inputs resident in HBM.  Every step combines its local results into a combine-state
+range of its own, whose results from the other ranks were delivered before the timed
+region, so each step releases all of its tokens.  W warm-up steps, then exactly K steps are
+timed back to back (synchronised on both sides); step s runs wave s mod 4.
 
-Prints one JSON line with the step throughput (expert tokens/s), the roofline of the
-dominant kernel (the gate/up GEMM, timed with HIP events on the launch stream) and the
-CPU oracle timed on a bounded sample on the host.
+The JSON line also carries: the roofline of the dominant kernel (the wave-0 gate/up GEMM,
+timed by start/stop events its own dispatch records, in a separate pass), per-stage times
+of each wave with the combine also measured after a 512 MiB cache-evicting write, the CPU
+oracle on a bounded sample of whole experts, and the decode-shaped workload's own figures
+(sub-object "decode").
 
---workload stream runs the multi-layer asynchronous stream (36 layers, 72 micro-queues, 16
-simulated sources with lognormal delays) for --batches expert batches under the queue pick
---policy (most tokens first, first layer first, or the defragmenting score) and reports the
-batch-size distribution, steps, per-layer token latency and the GPU time of the calls.
-
---workload prefill times the prefill-shaped rank share instead (256 experts, top-8, 32
-local experts, hidden 4096, intermediate 2048, fp8 e4m3 weights with bf16 activations,
-16384 pairs with Zipf(1.0) routing arriving in four waves of 6554/4915/3277/1638, each
-its own step).  Its line reports the FFN against the bf16 MFMA peak and the combine
-against the HBM peak (the row gather is fused into the FFN's activation loads).
+Other workloads (--workload):
+  decode   128 experts, top-4, 8 local, hidden 2880, intermediate 2880, bf16; 256 pairs
+           from a 4096-slot pool (steps cycle through four copies of the weights)
+  skewed   the decode layer shape with Zipf(1.2) routing over the 8 local experts: all 200
+           batches of U{8..512} pairs, value = sum of pairs / sum of step times
+  tiny     8 experts, top-2, hidden 64, intermediate 128, fp32 (launch-latency bound)
+  stream   36 layers, 72 micro-queues, 16 simulated sources with lognormal delays, under a
+           queue pick --policy (most tokens first, first layer first, defragmenting score)
 """
 from __future__ import annotations
 
@@ -40,15 +44,19 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+METRIC = "expert tokens/sec per GPU (assemble+FFN+combine); % MFMA peak, % HBM BW"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn_gateup_decode_traffic.md")
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILES = {"decode": os.path.join(PROFILES, "ffn_gateup_decode_traffic.md"),
+                 "prefill": os.path.join(PROFILES, "ffn_gateup_prefill_traffic.md")}
 CALIB_BYTES = 256 << 20
+FLUSH_BYTES = 512 << 20
 FFN_SRC = os.path.join(ROOT, "asynchronous_moe_expert_amd", "csrc", "ffn.hip")
 
 
 class HipEvents:
-    """Raw hipEvent_t handles (the library records one between its two FFN kernels)."""
+    """Raw hipEvent_t handles (the library records some of them inside its own calls)."""
 
     def __init__(self):
         self.hip = C.CDLL("libamdhip64.so")
@@ -56,7 +64,6 @@ class HipEvents:
         self.hip.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
         self.hip.hipEventSynchronize.argtypes = [C.c_void_p]
         self.hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
-        self.hip.hipEventDestroy.argtypes = [C.c_void_p]
 
     def create(self) -> int:
         e = C.c_void_p()
@@ -73,27 +80,206 @@ class HipEvents:
         return float(out.value)
 
 
-def stored_traffic():
+def stored_traffic(which: str):
     """HBM bytes per launch of the gate/up kernel from the committed rocprofv3 counter
     summary, if its counters were taken on the kernel source as it is now (else None)."""
     try:
-        text = open(TRAFFIC_FILE).read()
+        text = open(TRAFFIC_FILES[which]).read()
         sha = re.search(r"ffn\.hip sha256: ([0-9a-f]{64})", text).group(1)
         val = re.search(r"traffic bytes per launch: ([0-9]+)", text).group(1)
         src = hashlib.sha256(open(FFN_SRC, "rb").read()).hexdigest()
         return float(val) if sha == src else None
-    except (OSError, AttributeError, ValueError):
+    except (OSError, AttributeError, ValueError, KeyError):
         return None
 
 
-def cpu_baseline(b, wts, seconds: float) -> dict:
-    """The oracle (fp64 numpy) on the host: whole decode steps, repeated until `seconds`."""
+def cpu_info() -> dict:
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"cpu_model": model, "nproc": os.cpu_count(), "usable_cpus": usable}
+
+
+def blas_threads() -> int:
     import threadpoolctl
 
+    info = threadpoolctl.threadpool_info()
+    return int(max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1]))
+
+
+def calibration_copy(dev) -> None:
+    """One device-to-device copy of CALIB_BYTES: the reference dispatch that scales the
+    rocprofv3 byte counters of the same run to bytes."""
+    import torch
+
+    src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+# --------------------------------------------------------------------------- step runner
+def _compact(b):
+    """Token indices of a batch renumbered 0..T-1 (first appearance in the queue), and the
+    remote arrivals' tokens through the same map: each step then needs a state range of T."""
+    uniq, first = np.unique(b.tok, return_index=True)
+    order = uniq[np.argsort(first, kind="stable")]
+    lut = {int(t): i for i, t in enumerate(order)}
+    tok = np.array([lut[int(t)] for t in b.tok], np.int32)
+    r_tok = None if b.remote is None else np.array([lut[int(t)] for t in b.remote.tok], np.int32)
+    return tok, r_tok, len(order)
+
+
+class StepRunner:
+    """Expert steps over a cycle of ready batches: step s runs batch s mod len(batches) on
+    combine-state range s (its own tokens), whose remote results deliver() puts in first."""
+
+    def __init__(self, batches, wts, act_code, w_code, n_steps: int, weight_copies: int = 1):
+        import torch
+
+        import asynchronous_moe_expert_amd as M
+        from workloads.device import tensor, weight_tensors
+
+        self.M, self.torch = M, torch
+        self.batches = batches
+        b0 = batches[0]
+        self.E, self.H, self.I, self.K = b0.E_loc, b0.H, wts.I, b0.K
+        self.base = b0.expert_base
+        comp = [_compact(b) for b in batches]
+        self.T_step = max(c[2] for c in comp)
+        self.n_steps = n_steps
+        n_max = max(b.n for b in batches)
+        self.st = M.ExpertStep(self.E, self.H, self.I, self.K, act_code, w_code, n_max, n_steps * self.T_step)
+        wt = weight_tensors(wts)
+        self.st.load_weights(wt["wg"], wt["wu"], wt["wd"], wt.get("s_gate"), wt.get("s_up"), wt.get("s_down"))
+        del wt
+        # copies of the packed weights at distinct addresses; step s uses copy s % L, so no step
+        # finds the weights the one before it streamed still in a cache
+        L = max(1, weight_copies)
+        self.w_copies = [(self.st.w_gu, self.st.w_d)] + [(self.st.w_gu.clone(), self.st.w_d.clone())
+                                                         for _ in range(L - 1)]
+        self.pool = tensor(b0.pool, b0.act)
+        self.d = []
+        for b, (tok, r_tok, _) in zip(batches, comp):
+            x = dict(slot=tensor(b.slot), expert=tensor(b.expert), tok=tok, kslot=tensor(b.kslot), w=tensor(b.w),
+                     gen=tensor(b.gen))
+            if b.remote is not None and b.remote.m > 0:
+                r = b.remote
+                x.update(r_rows=tensor(r.rows, r.dtype), r_idx=tensor(r.row_idx), r_tok=r_tok,
+                         r_kslot=tensor(r.kslot), r_w=tensor(r.w), r_gen=tensor(r.gen))
+            self.d.append(x)
+        # per-step token tensors (state range s), made before any timing
+        self.tok = [tensor(self.d[s % len(batches)]["tok"] + s * self.T_step) for s in range(n_steps)]
+        self.stream = torch.cuda.current_stream().cuda_stream
+
+    def batch(self, s: int):
+        return self.batches[s % len(self.batches)]
+
+    def deliver(self, s: int) -> None:
+        """The remote results of step s's tokens (untimed; the tokens' other K-1 positions)."""
+        d = self.d[s % len(self.batches)]
+        if "r_rows" in d:
+            from workloads.device import tensor
+
+            self.st.combine(d["r_rows"], d["r_idx"], tensor(d["r_tok"] + s * self.T_step), d["r_kslot"], d["r_w"],
+                            d["r_gen"])
+
+    def step(self, s: int) -> None:
+        b, d = self.batch(s), self.d[s % len(self.batches)]
+        self.st.w_gu, self.st.w_d = self.w_copies[s % len(self.w_copies)]
+        self.st.run(d["slot"], d["expert"], self.base, self.pool, self.tok[s], d["kslot"], d["w"], d["gen"], n=b.n)
+
+    def check(self, s: int) -> None:
+        assert int(self.st.err.item()) == 0, "device error flags raised"
+        assert int(self.st.rel_count.item()) == _compact(self.batch(s))[2], "a step did not release its tokens"
+
+    def timed(self, W: int, K: int):
+        """W warm-up steps, then K timed steps back to back; returns (ms, sum of pairs)."""
+        torch = self.torch
+        for s in range(W + K):
+            self.deliver(s)
+        torch.cuda.synchronize()
+        assert int(self.st.rel_count.item()) == 0
+        for s in range(W):
+            self.step(s)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for s in range(W, W + K):
+            self.step(s)
+        t1.record()
+        torch.cuda.synchronize()
+        self.check(W + K - 1)
+        return t0.elapsed_time(t1), sum(self.batch(s).n for s in range(W, W + K))
+
+    def stages(self, ev: HipEvents, reps: int, flush: bool = False):
+        """Per-stage HIP-event intervals of each batch of the cycle (state reset and delivery
+        untimed before each step), plus the gate/up projection's own kernel time from the
+        events its dispatch records, in a pass of its own so that they stay out of the stage
+        intervals; with flush, the combine is also timed after a 512 MiB write that evicts
+        the last-level cache (cold)."""
+        torch, M, st = self.torch, self.M, self.st
+        nb = len(self.batches)
+        names = ["assemble", "gate_up", "down", "combine"]
+        evs = [ev.create() for _ in range(5)]
+        gs, ge, c0, c1 = ev.create(), ev.create(), ev.create(), ev.create()
+        scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda") if flush else None
+        times = {w: {k: [] for k in names + ["gate_up_kernel", "combine_cold"]} for w in range(nb)}
+        for _ in range(reps):
+            for w in range(nb):
+                b, d = self.batches[w], self.d[w]
+                self.st.w_gu, self.st.w_d = self.w_copies[w % len(self.w_copies)]
+                for p in range(2):
+                    M.moe_state_reset(st.state, 0)
+                    self.deliver(w)
+                    tok = self.tok[w]
+                    if p == 0:
+                        ev.record(evs[0], self.stream)
+                        st.assemble(d["slot"], d["expert"], self.base, self.pool, n=b.n)
+                        ev.record(evs[1], self.stream)
+                        plan = st.local_combine_args(tok, d["kslot"], d["w"], d["gen"], b.n)
+                        st.ffn(b.n, ev_mid=evs[2], plan=plan)
+                        ev.record(evs[3], self.stream)
+                        M.combine_call(plan, "apply")
+                        ev.record(evs[4], self.stream)
+                    else:
+                        st.assemble(d["slot"], d["expert"], self.base, self.pool, n=b.n)
+                        plan = st.local_combine_args(tok, d["kslot"], d["w"], d["gen"], b.n)
+                        st.ffn(b.n, plan=plan, ev_gu=(gs, ge))
+                        if scratch is not None:
+                            scratch.fill_(1.0)
+                        ev.record(c0, self.stream)
+                        M.combine_call(plan, "apply")
+                        ev.record(c1, self.stream)
+                    torch.cuda.synchronize()
+                    self.check(w)
+                    if p == 0:
+                        for k, nm in enumerate(names):
+                            times[w][nm].append(ev.ms(evs[k], evs[k + 1]))
+                    else:
+                        times[w]["gate_up_kernel"].append(ev.ms(gs, ge))
+                        if scratch is not None:
+                            times[w]["combine_cold"].append(ev.ms(c0, c1))
+        return {w: {k: float(np.median(v)) for k, v in t.items() if v} for w, t in times.items()}
+
+
+# ------------------------------------------------------------------------- CPU baselines
+def cpu_baseline_decode(b, wts, seconds: float) -> dict:
+    """The oracle (fp64 numpy) on the host: whole decode steps, repeated until `seconds`."""
     import oracle as O
 
-    info = threadpoolctl.threadpool_info()
-    cores = max([i.get("num_threads", 1) for i in info] or [1])
     r = b.remote
     rows_remote = O.decode(r.rows, r.dtype)
     t0 = time.perf_counter()
@@ -109,171 +295,215 @@ def cpu_baseline(b, wts, seconds: float) -> dict:
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    return {"value": b.n * reps / el, "unit": "expert tokens/s", "cores": int(cores), "kind": "oracle",
+    return {"value": b.n * reps / el, "unit": "expert tokens/s", "cores": blas_threads(), "kind": "oracle",
+            **cpu_info(),
             "sample": f"{reps} whole decode steps of {b.n} token-expert pairs (assemble, fp64 SwiGLU FFN over "
                       f"8 experts, combine incl. the delivery of the remote results), {el:.1f} s"}
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle CPU-baseline budget (0 = skip)")
-    ap.add_argument("--workload", choices=["decode", "prefill", "stream"], default="decode")
-    ap.add_argument("--policy", choices=["mtfs", "flfs", "defrag"], default="mtfs",
-                    help="queue pick of the stream workload")
-    ap.add_argument("--batches", type=int, default=1000, help="expert batches of the stream workload")
-    ap.add_argument("--merge", type=int, choices=[1, 2, 4], default=1,
-                    help="prefill: consecutive waves merged into one ready batch (1 = each wave alone)")
-    ap.add_argument("--weight-copies", type=int, default=4,
-                    help="decode: packed copies of the layer's weights the steps cycle through (so that no step "
-                         "finds weights left in the caches by the one before, as in a model of many layers)")
-    ap.add_argument("--calibration-copy", action="store_true",
-                    help="copy 256 MiB device to device once before the warm-up (reference dispatch for "
-                         "rocprofv3 byte counters)")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs one expert-parallel rank's share on a single GPU; it has no multi-GPU mode "
-              "(use --gpus 1)", file=sys.stderr)
-        return 2
+def _oracle_subqueue(b, wts, experts):
+    """One oracle pass over the pairs of `experts` in batch b: assemble, gather, FFN (each
+    expert's weights decoded once), combine of the local and remote results; returns pairs."""
+    import oracle as O
 
-    if args.workload == "prefill":
-        return run_prefill(args)
-    if args.workload == "stream":
-        return run_stream_bench(args)
+    sel = np.isin(b.expert - b.expert_base, experts)
+    slot, expert, tok = b.slot[sel], b.expert[sel], b.tok[sel]
+    a = O.assemble(slot, expert, b.expert_base, b.E_loc, b.P)
+    xb = O.decode(O.gather_rows(b.pool, slot, a["perm"], int(a["offsets"][-1])), b.act)
+    y = O.expert_ffn(xb, a["offsets"], wts)
+    r = b.remote
+    rsel = np.isin(r.tok, tok)
+    ridx = r.row_idx[rsel]
+    uniq, inv = np.unique(ridx, return_inverse=True)
+    cs = O.CombineState(b.T, b.K)
+    O.combine_release(cs, O.decode(r.rows[uniq], r.dtype), inv.astype(np.int32), r.tok[rsel], r.kslot[rsel],
+                      r.w[rsel], r.gen[rsel])
+    _, rel, _ = O.combine_release(cs, y, a["pos"], tok, b.kslot[sel], b.w[sel], b.gen[sel])
+    assert len(rel) == int(sel.sum())
+    return int(sel.sum())
+
+
+def cpu_baseline_prefill(b, wts, seconds: float, seconds_1core: float) -> dict:
+    """The oracle on whole experts of the first prefill wave, in a seeded random order of
+    experts, until `seconds` (all BLAS threads) and `seconds_1core` (one thread)."""
+    import threadpoolctl
+
+    order = list(np.random.default_rng(7).permutation(b.E_loc))
+
+    def run(budget):
+        pairs, done, t0 = 0, [], time.perf_counter()
+        for e in order:
+            pairs += _oracle_subqueue(b, wts, [e])
+            done.append(int(e))
+            if time.perf_counter() - t0 >= budget:
+                break
+        return pairs, done, time.perf_counter() - t0
+
+    pairs, done, el = run(seconds)
+    out = {"value": pairs / el, "unit": "expert tokens/s", "cores": blas_threads(), "kind": "oracle", **cpu_info(),
+           "sample": f"whole local experts {done} of the first prefill wave ({pairs} of its {b.n} pairs): for "
+                     f"each, assemble of its sub-queue, gather, fp64 SwiGLU FFN with the expert's fp8 weights "
+                     f"decoded once, combine with the tokens' 7 remote results; {el:.1f} s"}
+    if seconds_1core > 0:
+        with threadpoolctl.threadpool_limits(1):
+            p1, d1, e1 = run(seconds_1core)
+        out["value_1core"] = p1 / e1
+        out["sample_1core"] = f"whole local experts {d1} ({p1} pairs) with one BLAS thread, {e1:.1f} s"
+    return out
+
+
+# ------------------------------------------------------------------------------ workloads
+def run_decode(args, W_steps: int, K_steps: int, cpu_seconds: float) -> dict:
     import torch
 
-    import asynchronous_moe_expert_amd as M
     import workloads as W
-    from workloads.device import batch_tensors, weight_tensors
 
-    M.load()
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     b, wts = W.c1_decode()
-    K_steps, W_steps = args.steps, args.warmup
-    S = W_steps + 2 * K_steps  # warmup, the timed loop, then the loop timed per stage
-    d = batch_tensors(b)
-    wt = weight_tensors(wts)
-    st = M.ExpertStep(b.E_loc, b.H, wts.I, b.K, M.MOE_BF16, M.MOE_BF16, b.n, S * b.T)
-    st.load_weights(wt["wg"], wt["wu"], wt["wd"])
-    del wt
-    # copies of the packed weights at distinct addresses; step s uses copy s % L, so the
-    # weights a step streams (398 MB) were last read L steps earlier, with L x 398 MB of
-    # other weights in between: more than the 256 MB last-level cache holds
-    L = max(1, args.weight_copies)
-    w_copies = [(st.w_gu, st.w_d)] + [(st.w_gu.clone(), st.w_d.clone()) for _ in range(L - 1)]
-    # per-step token indices (each step completes tokens of its own) and the remote
-    # results of every step's tokens, delivered before timing
-    tok_steps = [d["tok"] + s * b.T for s in range(S)]
-    r_tok = torch.cat([d["r_tok"] + s * b.T for s in range(S)])
-    rep = lambda x: torch.cat([x] * S)  # noqa: E731
-    st.combine(d["r_rows"], rep(d["r_idx"]), r_tok, rep(d["r_kslot"]), rep(d["r_w"]), rep(d["r_gen"]))
-    torch.cuda.synchronize()
-    assert int(st.rel_count.item()) == 0
-
+    run = StepRunner([b], wts, 1, 1, W_steps + K_steps, args.weight_copies)
+    if args.calibration_copy and args.workload == "decode":
+        calibration_copy(torch.device("cuda:0"))
+    total_ms, pairs = run.timed(W_steps, K_steps)
     ev = HipEvents()
-    stream = torch.cuda.current_stream().cuda_stream
-    e_asm = [ev.create() for _ in range(S)]
-    e_mid = [ev.create() for _ in range(S)]
-    e_gs = [ev.create() for _ in range(S)]  # taken by the gate/up kernel's own dispatch
-    e_ge = [ev.create() for _ in range(S)]
-    e_ffn = [ev.create() for _ in range(S)]
-    e_end = [ev.create() for _ in range(S)]
-    e_start = ev.create()
+    stg = run.stages(ev, max(1, min(K_steps, 20)))[0]
+    counts = run.st.counts.cpu().numpy()
+    active = int((counts > 0).sum())
+    H, I, n = b.H, wts.I, b.n
+    gu_bytes = active * 2 * H * I * 2 + n * H * 2 + n * I * 2
+    gu_ms = stg["gate_up_kernel"]
+    achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
+    out = {
+        "value": round(pairs / (total_ms * 1e-3), 1), "unit": "expert tokens/s", "steps": K_steps,
+        "warmup": W_steps, "ms_per_step": round(total_ms / K_steps, 5), "dtype": "bf16",
+        "config": {"workload": "decode-shaped EP rank share: 8 of 128 experts, top-4, hidden 2880, SwiGLU "
+                               "intermediate 2880, 256 token-expert pairs from a 4096-slot token pool",
+                   "E_loc": b.E_loc, "K": b.K, "H": H, "I": I, "pairs": n, "tokens": b.T, "pool_slots": b.P,
+                   "weight_copies": len(run.w_copies)},
+        "roofline": {"bound": "hbm", "kernel": "ffn_mfma_kernel<gate/up, bf16>", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": stored_traffic("decode"), "algorithmic_bytes": gu_bytes,
+                     "kernel_us": round(gu_ms * 1e3, 2)},
+        "stages_us": {k: round(v * 1e3, 2) for k, v in stg.items()},
+    }
+    out["cpu_baseline"] = cpu_baseline_decode(b, wts, cpu_seconds) if cpu_seconds > 0 else None
+    return out
 
-    def step(s: int) -> None:
-        st.w_gu, st.w_d = w_copies[s % L]
-        st.run(d["slot"], d["expert"], b.expert_base, d["pool"], tok_steps[s], d["kslot"], d["w"], d["gen"], n=b.n)
 
-    def step_timed(s: int) -> None:
-        # the same calls as ExpertStep.run (the combine plan inside the FFN call, then the
-        # apply) with HIP events between them on the launch stream
-        st.w_gu, st.w_d = w_copies[s % L]
-        st.assemble(d["slot"], d["expert"], b.expert_base, d["pool"])
-        ev.record(e_asm[s], stream)
-        plan = st.local_combine_args(tok_steps[s], d["kslot"], d["w"], d["gen"], b.n)
-        st.ffn(b.n, ev_mid=e_mid[s], plan=plan, ev_gu=(e_gs[s], e_ge[s]))
-        ev.record(e_ffn[s], stream)
-        M.combine_call(plan, "apply")
-        ev.record(e_end[s], stream)
+def run_prefill(args) -> dict:
+    import torch
 
+    import workloads as W
+
+    setup = W.c4_prefill_setup()
+    g = args.merge
+    waves = [W.merge_batches([W.c4_wave(setup, w) for w in range(i, i + g)]) for i in range(0, 4, g)]
+    nw = len(waves)
+    K_steps, W_steps = args.steps, args.warmup
+    run = StepRunner(waves, setup.weights, 1, 2, W_steps + K_steps)
+    E, H, I, K = run.E, run.H, run.I, run.K
     if args.calibration_copy:
-        calibration_copy(dev)
+        calibration_copy(torch.device("cuda:0"))
+    total_ms, pairs = run.timed(W_steps, K_steps)
+    ev = HipEvents()
+    stg = run.stages(ev, max(1, min(K_steps // nw, 5)), flush=True)
+    per_wave = []
+    for w, b in enumerate(waves):
+        m, n = stg[w], b.n
+        fl = 6.0 * n * H * I
+        c_bytes = n * H * 2 + n * H * (4 + 2) + 24 * n  # combine: result rows, held sums, released rows
+        per_wave.append({"pairs": n, "us": {k: round(v * 1e3, 2) for k, v in m.items()},
+                         "ffn_mfma_frac": round(fl / ((m["gate_up"] + m["down"]) * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                         "gate_up_mfma_frac": round(4.0 * n * H * I / (m["gate_up_kernel"] * 1e-3) / 1e12
+                                                    / BF16_PEAK_TFLOPS, 4),
+                         "combine_hbm_frac": round(c_bytes / (m["combine"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "combine_cold_hbm_frac": round(c_bytes / (m["combine_cold"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+    b0 = waves[0]
+    gu0_ms = stg[0]["gate_up_kernel"]
+    gu_tf = 4.0 * b0.n * H * I / (gu0_ms * 1e-3) / 1e12
+    counts = np.bincount(b0.expert - b0.expert_base, minlength=E)
+    gu_alg = int((counts > 0).sum()) * 2 * I * H + b0.n * H * 2 + b0.n * I * 2
+    out = {
+        "metric": METRIC, "value": round(pairs / (total_ms * 1e-3), 1), "unit": "expert tokens/s", "n_gpus": 1,
+        "steps": K_steps, "warmup": W_steps, "ms_per_step": round(total_ms / K_steps, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 activations, fp8 e4m3 weights, fp32 accumulate",
+        "data": "synthetic (seeded; random-init expert weights)",
+        "config": {"workload": "prefill-shaped EP rank share: 32 of 256 experts, top-8, hidden 4096, SwiGLU "
+                               "intermediate 2048, 16384 pairs (Zipf 1.0) in waves of 6554/4915/3277/1638, "
+                               "each wave one step",
+                   "E_loc": E, "K": K, "H": H, "I": I, "pairs_per_cycle": sum(b.n for b in waves),
+                   "pool_slots": b0.P, "waves_per_step": g},
+        "roofline": {"bound": "mfma", "kernel": f"ffn gate/up GEMM, first wave ({b0.n} pairs)",
+                     "achieved": round(gu_tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gu_tf / BF16_PEAK_TFLOPS, 4), "traffic": stored_traffic("prefill"),
+                     "algorithmic_bytes": gu_alg, "kernel_us": round(gu0_ms * 1e3, 2)},
+        "waves": per_wave,
+        "note": "value: K steps timed back to back (step s = wave s mod 4, its remote results delivered before "
+                "the timed region); waves[].us: per-stage medians of HIP-event intervals, each step alone; "
+                "gate_up_kernel and roofline.kernel_us: the gate/up projection alone, from events its dispatch "
+                "records; combine_cold: the combine after a 512 MiB cache-evicting write",
+    }
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline_prefill(W.c4_wave(setup, 0), setup.weights, args.cpu_seconds,
+                                                   args.cpu_seconds / 2)
+    else:
+        out["cpu_baseline"] = None
+    return out
+
+
+def run_skewed(args) -> dict:
+    import workloads as W
+
+    pool = W.c2_pool()
+    batches = [W.c2_skewed_batch(i, pool) for i in range(W.C2["batches"])]
+    wts = W.c2_weights()
+    nb = len(batches)
+    run = StepRunner(batches, wts, 1, 1, nb + args.warmup, args.weight_copies)
+    # warm-up on the first batches, then all 200 batches back to back: sum n / sum time
+    W_steps = args.warmup
+    for s in range(W_steps + nb):
+        run.deliver(s)
+    import torch
+
+    torch.cuda.synchronize()
     for s in range(W_steps):
-        step(s)
+        run.step(s)
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
-    for s in range(W_steps, W_steps + K_steps):
-        step(s)
+    for s in range(W_steps, W_steps + nb):
+        run.step(s)
     t1.record()
     torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
-    assert int(st.err.item()) == 0, "device error flags raised"
-    assert int(st.rel_count.item()) == b.T
-
-    timed = range(W_steps + K_steps, S)
-    ev.record(e_start, stream)
-    for s in timed:
-        step_timed(s)
-    torch.cuda.synchronize()
-    assert int(st.err.item()) == 0 and int(st.rel_count.item()) == b.T
-    prev = [e_start] + [e_end[s] for s in timed][:-1]
-    asm_ms = np.mean([ev.ms(p, e_asm[s]) for p, s in zip(prev, timed)])
-    gu_ms = np.mean([ev.ms(e_asm[s], e_mid[s]) for s in timed])
-    gu_kernel_ms = np.mean([ev.ms(e_gs[s], e_ge[s]) for s in timed])  # the kernel alone
-    dn_ms = np.mean([ev.ms(e_mid[s], e_ffn[s]) for s in timed])
-    cb_ms = np.mean([ev.ms(e_ffn[s], e_end[s]) for s in timed])
-
-    counts = st.counts.cpu().numpy()
-    active = int((counts > 0).sum())
-    H, I, n = b.H, wts.I, b.n
-    gu_bytes = active * 2 * H * I * 2 + n * H * 2 + n * I * 2
-    gu_flops = 4.0 * n * H * I
-    achieved = gu_bytes / (gu_kernel_ms * 1e-3) / 1e9
-    ms_step = total_ms / K_steps
-    value = n * K_steps / (total_ms * 1e-3)
-    out = {
-        "metric": "expert tokens/sec per GPU (assemble+FFN+combine)",
-        "value": round(value, 1),
-        "unit": "expert tokens/s",
-        "n_gpus": 1,
-        "steps": K_steps,
-        "warmup": W_steps,
-        "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded; random-init expert weights)",
-        "config": {"workload": "decode-shaped EP rank share: 8 of 128 experts, top-4, hidden 2880, SwiGLU "
-                               "intermediate 2880, 256 token-expert pairs from a 4096-slot token pool",
-                   "E_loc": b.E_loc, "K": b.K, "H": H, "I": I, "pairs": n, "tokens": b.T, "pool_slots": b.P,
-                   "weight_copies": L},
-        "roofline": {"bound": "hbm", "kernel": "ffn_mfma_kernel<gate/up, bf16>", "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": stored_traffic(), "algorithmic_bytes": gu_bytes,
-                     "kernel_us": round(gu_kernel_ms * 1e3, 2),
-                     "mfma_frac": round(gu_flops / (gu_kernel_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 5)},
-        "stages_us": {"assemble": round(asm_ms * 1e3, 2), "ffn_gate_up": round(gu_ms * 1e3, 2),
-                      "ffn_down": round(dn_ms * 1e3, 2), "combine": round(cb_ms * 1e3, 2),
-                      "note": "second K-step loop with HIP events between the calls (events add a "
-                              "few us of launch latency to each interval, the gate/up one also its kernel's "
-                              "own start/stop events); value is from the loop without; roofline.kernel_us is "
-                              "the gate/up kernel alone"},
-    }
-    if args.cpu_seconds > 0:
-        out["cpu_baseline"] = cpu_baseline(b, wts, args.cpu_seconds)
-    else:
-        out["cpu_baseline"] = None
-    print(json.dumps(out), flush=True)
-    return 0
+    assert int(run.st.err.item()) == 0
+    ms = t0.elapsed_time(t1)
+    # (step s runs batch s mod 200, so the timed steps cover every batch once)
+    pairs = sum(run.batch(s).n for s in range(W_steps, W_steps + nb))
+    sizes = np.array([b.n for b in batches])
+    return {"metric": METRIC, "value": round(pairs / (ms * 1e-3), 1), "unit": "expert tokens/s", "n_gpus": 1,
+            "steps": nb, "warmup": W_steps, "ms_per_step": round(ms / nb, 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded)",
+            "config": {"workload": "skewed ragged routing: decode layer shape, Zipf(1.2) over 8 local experts, "
+                                   "200 batches of U{8..512} pairs", "pairs": int(sizes.sum()),
+                       "batch_pairs_mean": float(sizes.mean()), "weight_copies": len(run.w_copies)},
+            "roofline": None, "cpu_baseline": None}
 
 
-def run_stream_bench(args) -> int:
+def run_tiny(args) -> dict:
+    import workloads as W
+
+    b, wts = W.c0_tiny()
+    run = StepRunner([b], wts, 0, 0, args.warmup + args.steps)
+    ms, pairs = run.timed(args.warmup, args.steps)
+    return {"metric": METRIC, "value": round(pairs / (ms * 1e-3), 1), "unit": "expert tokens/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms / args.steps, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic (seeded)",
+            "config": {"workload": "tiny single MoE layer: 8 experts, top-2, hidden 64, intermediate 128, fp32, "
+                                   "64 pairs", "pairs": b.n},
+            "roofline": None, "cpu_baseline": None}
+
+
+def run_stream_bench(args) -> dict:
     """The multi-layer stream on the HIP path under one queue-pick policy.  Every expert
     batch and message delivery is one combine call whose release list feeds the queues
     back, so the host waits for each call; GPU time is summed from HIP events around the
@@ -285,8 +515,6 @@ def run_stream_bench(args) -> int:
     from workloads.device import device_layer_weights
     from workloads.stream import StreamConfig, StreamSim, run_stream
 
-    M.load()
-    torch.cuda.set_device(0)
     cfg = StreamConfig(policy=args.policy, batches=args.batches)
     sim = StreamSim(cfg)
     rows_f, xs_f = sim.banks()
@@ -342,10 +570,9 @@ def run_stream_bench(args) -> int:
     sizes = np.array([x[2] for x in sim.log if x[0] == "X"])
     lat = np.array(sim.latency)
     pct = lambda a, q: float(np.percentile(a, q)) if len(a) else None  # noqa: E731
-    out = {
-        "metric": "expert tokens/sec per GPU (assemble+FFN+combine)",
-        "value": round(acc["pairs"] / (acc["gpu_ms"] * 1e-3), 1), "unit": "expert tokens/s", "n_gpus": 1,
-        "steps": int(sim.batches_done), "warmup": 0, "higher_is_better": True, "scaling": "weak",
+    return {
+        "metric": METRIC, "value": round(acc["pairs"] / (acc["gpu_ms"] * 1e-3), 1), "unit": "expert tokens/s",
+        "n_gpus": 1, "steps": int(sim.batches_done), "warmup": 0, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded stream; random-init expert weights)",
         "config": {"workload": "multi-layer asynchronous stream: 36 layers (72 micro-queues), 8 of 128 experts, "
                                "top-4, hidden 2880, 4096 home tokens, 16 sources with lognormal(0,1) delays",
@@ -363,154 +590,55 @@ def run_stream_bench(args) -> int:
         "note": "value = expert pairs / GPU time of the expert-step and delivery calls (HIP events); the host "
                 "waits for each call's release list, so wall time includes the scheduler in Python",
     }
-    print(json.dumps(out), flush=True)
-    return 0
 
 
-def cpu_baseline_prefill(setup, b, seconds: float) -> dict:
-    """The oracle's FFN (fp64) on a seeded sample of the first wave's rows, for `seconds`."""
-    import threadpoolctl
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle CPU-baseline budget (0 = skip)")
+    ap.add_argument("--workload", choices=["prefill", "decode", "skewed", "tiny", "stream"], default="prefill")
+    ap.add_argument("--policy", choices=["mtfs", "flfs", "defrag"], default="mtfs",
+                    help="queue pick of the stream workload")
+    ap.add_argument("--batches", type=int, default=1000, help="expert batches of the stream workload")
+    ap.add_argument("--merge", type=int, choices=[1, 2, 4], default=1,
+                    help="prefill: consecutive waves merged into one ready batch (1 = each wave alone)")
+    ap.add_argument("--weight-copies", type=int, default=4,
+                    help="decode/skewed: packed copies of the layer's weights the steps cycle through (so that no "
+                         "step finds weights left in the caches by the one before, as in a model of many layers)")
+    ap.add_argument("--no-decode", action="store_true", help="prefill: skip the decode sub-object")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="copy 256 MiB device to device once before the warm-up (reference dispatch for "
+                         "rocprofv3 byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one expert-parallel rank's share on one GPU; there is no multi-GPU mode "
+              "(run it with --gpus 1)", file=sys.stderr)
+        return 2
 
-    import oracle as O
-
-    info = threadpoolctl.threadpool_info()
-    cores = max([i.get("num_threads", 1) for i in info] or [1])
-    rng = np.random.default_rng(7)
-    rows, reps = 0, 0
-    t0 = time.perf_counter()
-    while True:
-        pick = rng.choice(b.n, 16, replace=False)
-        x = O.decode(b.pool[b.slot[pick]], "bf16")
-        O.ffn_rows(x, b.expert[pick] - b.expert_base, setup.weights)
-        rows += len(pick)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": rows / el, "unit": "expert tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{rows} seeded rows of prefill wave 0 ({reps} draws of 16), fp64 SwiGLU FFN only "
-                      f"(assemble and combine are a small share of the oracle's time), {el:.1f} s"}
-
-
-def calibration_copy(dev) -> None:
-    """One device-to-device copy of CALIB_BYTES: the reference dispatch that scales the
-    rocprofv3 byte counters of the same run to bytes."""
-    import torch
-
-    src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
-    dst = torch.empty_like(src)
-    torch.cuda.synchronize()
-    dst.copy_(src)
-    torch.cuda.synchronize()
-    del src, dst
-
-
-def run_prefill(args) -> int:
-    """Prefill-shaped rank share: each of the four waves is one step (assemble, FFN,
-    combine of the local result into tokens whose 7 remote results were delivered first)."""
     import torch
 
     import asynchronous_moe_expert_amd as M
-    import workloads as W
-    from workloads.device import batch_tensors, weight_tensors
 
     M.load()
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    setup = W.c4_prefill_setup()
-    g = args.merge
-    waves = [W.merge_batches([W.c4_wave(setup, w) for w in range(i, i + g)]) for i in range(0, 4, g)]
-    nw = len(waves)
-    E, H, I, K, P = setup.weights.E, setup.weights.H, setup.weights.I, waves[0].K, waves[0].P
-    n_max = max(b.n for b in waves)
-    wt = weight_tensors(setup.weights)
-    st = M.ExpertStep(E, H, I, K, M.MOE_BF16, M.MOE_FP8_E4M3, n_max, P)
-    st.load_weights(wt["wg"], wt["wu"], wt["wd"], wt["s_gate"], wt["s_up"], wt["s_down"])
-    del wt
-    pool = batch_tensors(waves[0])["pool"]
-    dw = []
-    for b in waves:
-        d = batch_tensors(b)
-        d.pop("pool")
-        dw.append(d)
-    ev = HipEvents()
-    stream = torch.cuda.current_stream().cuda_stream
-    reps = max(1, args.steps // nw)
-    W_reps = max(1, args.warmup // nw)
-    names = ["assemble", "gate_up", "down", "combine"]
-    times = {w: {k: [] for k in names} for w in range(nw)}
-    evs = [ev.create() for _ in range(5)]
-    if args.calibration_copy:
-        calibration_copy(dev)
-    for rep in range(W_reps + reps):
-        for w, b in enumerate(waves):
-            d = dw[w]
-            M.moe_state_reset(st.state, 0)
-            st.combine(d["r_rows"], d["r_idx"], d["r_tok"], d["r_kslot"], d["r_w"], d["r_gen"])
-            ev.record(evs[0], stream)
-            st.assemble(d["slot"], d["expert"], b.expert_base, pool, n=b.n)
-            ev.record(evs[1], stream)
-            st.ffn(b.n, ev_mid=evs[2])
-            ev.record(evs[3], stream)
-            st.combine(st.y, st.pos, d["tok"], d["kslot"], d["w"], d["gen"], m=b.n, n_rows=b.n)
-            ev.record(evs[4], stream)
-            torch.cuda.synchronize()
-            assert int(st.err.item()) == 0 and int(st.rel_count.item()) == b.n, "prefill step did not release"
-            if rep >= W_reps:
-                for k, nm in enumerate(names):
-                    times[w][nm].append(ev.ms(evs[k], evs[k + 1]))
-    # the gate/up projection's kernel time alone (start/stop events taken by its own
-    # dispatches), in a pass of its own so that these events stay out of the intervals above
-    gs, ge = ev.create(), ev.create()
-    gu_kernel = {w: [] for w in range(nw)}
-    for rep in range(reps):
-        for w, b in enumerate(waves):
-            d = dw[w]
-            M.moe_state_reset(st.state, 0)
-            st.combine(d["r_rows"], d["r_idx"], d["r_tok"], d["r_kslot"], d["r_w"], d["r_gen"])
-            st.assemble(d["slot"], d["expert"], b.expert_base, pool, n=b.n)
-            st.ffn(b.n, ev_gu=(gs, ge))
-            st.combine(st.y, st.pos, d["tok"], d["kslot"], d["w"], d["gen"], m=b.n, n_rows=b.n)
-            torch.cuda.synchronize()
-            gu_kernel[w].append(ev.ms(gs, ge))
-    med = {w: {nm: float(np.median(times[w][nm])) for nm in names} for w in range(nw)}
-    step_ms = sum(sum(med[w].values()) for w in range(nw))
-    n_tot = sum(b.n for b in waves)
-    value = n_tot / (step_ms * 1e-3)
-    per_wave = []
-    for w, b in enumerate(waves):
-        m = med[w]
-        n = b.n
-        fl_gu, fl_dn = 4.0 * n * H * I, 2.0 * n * H * I
-        c_bytes = n * H * 2 + n * H * (4 + 2) + 24 * n   # combine: result rows, held sums, released rows
-        # the row gather is fused into the gate/up GEMM's activation loads (the assemble
-        # stage builds the index only), so it has no time of its own to price
-        per_wave.append({"pairs": n, "us": {k: round(v * 1e3, 2) for k, v in m.items()},
-                         "gate_up_kernel_us": round(float(np.median(gu_kernel[w])) * 1e3, 2),
-                         "ffn_mfma_frac": round((fl_gu + fl_dn) / ((m["gate_up"] + m["down"]) * 1e-3) / 1e12
-                                                / BF16_PEAK_TFLOPS, 4),
-                         "combine_hbm_frac": round(c_bytes / (m["combine"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
-    b0, m0 = waves[0], med[0]
-    gu0_ms = float(np.median(gu_kernel[0]))
-    gu_tf = 4.0 * b0.n * H * I / (gu0_ms * 1e-3) / 1e12
-    out = {
-        "metric": "expert tokens/sec per GPU (assemble+FFN+combine)",
-        "value": round(value, 1), "unit": "expert tokens/s", "n_gpus": 1, "steps": reps * nw, "warmup": W_reps * nw,
-        "ms_per_step": round(step_ms / nw, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16 activations, fp8 e4m3 weights, fp32 accumulate", "data": "synthetic (seeded; random-init expert weights)",
-        "config": {"workload": "prefill-shaped EP rank share: 32 of 256 experts, top-8, hidden 4096, SwiGLU "
-                               "intermediate 2048, 16384 pairs (Zipf 1.0) in waves of 6554/4915/3277/1638",
-                   "E_loc": E, "K": K, "H": H, "I": I, "pairs": n_tot, "pool_slots": P, "waves_per_step": g},
-        "roofline": {"bound": "mfma", "kernel": f"ffn gate/up GEMM, first step ({b0.n} pairs)", "achieved": round(gu_tf, 1),
-                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(gu_tf / BF16_PEAK_TFLOPS, 4),
-                     "traffic": None, "kernel_us": round(gu0_ms * 1e3, 2)},
-        "waves": per_wave,
-        "note": "per-stage medians of HIP-event intervals on the launch stream; each step is timed alone "
-                "(state reset and remote delivery untimed before it); gate_up_kernel_us and roofline.kernel_us: "
-                "the gate/up GEMM and its finalize alone, from events its dispatches record, in a separate pass",
-    }
-    out["cpu_baseline"] = cpu_baseline_prefill(setup, W.c4_wave(setup, 0, with_remote=False), args.cpu_seconds) \
-        if args.cpu_seconds > 0 else None
+    torch.cuda.set_device(0)
+    if args.workload == "prefill":
+        out = run_prefill(args)
+        if not args.no_decode:
+            out["decode"] = run_decode(args, 10, 50, min(args.cpu_seconds, 5.0))
+    elif args.workload == "decode":
+        d = run_decode(args, args.warmup, args.steps, args.cpu_seconds)
+        out = {"metric": METRIC, "value": d.pop("value"), "unit": d.pop("unit"), "n_gpus": 1,
+               "steps": d.pop("steps"), "warmup": d.pop("warmup"), "ms_per_step": d.pop("ms_per_step"),
+               "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": d.pop("dtype"),
+               "data": "synthetic (seeded; random-init expert weights)", **d}
+    elif args.workload == "skewed":
+        out = run_skewed(args)
+    elif args.workload == "tiny":
+        out = run_tiny(args)
+    else:
+        out = run_stream_bench(args)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -23,7 +23,9 @@
  *
  * Conventions shared by every call
  *   - Memory: the caller allocates every buffer (device memory unless stated).  The
- *     library never allocates, frees or synchronises; it keeps no state between calls.
+ *     library never allocates, frees or synchronises.  Between calls it keeps only read-only
+ *     device properties (compute-unit count, kernel occupancy), cached per device on first
+ *     use with atomic stores, so concurrent calls from several host threads are safe.
  *   - Ordering: all work is enqueued on `stream` in call order.  Calls return as soon as
  *     the work is enqueued.
  *   - Host-side errors: a call validates its arguments first and, on failure, returns a
@@ -258,7 +260,9 @@ int moe_state_reset(const moe_combine_state* st, uint32_t gen0, hipStream_t stre
  *                 (the same inputs give the same bits)
  *   rel_list    = released tokens in ascending order, *rel_count of them (device int32)
  *   state       : mask[t] = 0, tgen[t] += 1
- * Tokens still missing results keep their partial sums.
+ * Tokens still missing results keep their partial sums.  The per-token arrival count of a
+ * token still waiting is popcount(mask[t]) (the results it holds, each position once); the
+ * mask is that count's output, finer than a count since it also names the positions held.
  * Limits: 1 <= K <= 32, 0 <= m <= 2^24, H % 8 == 0, rows/out dtypes F32 or BF16,
  * rel_list holds at least min(m, T_cap) entries; the workspace (device memory, 16-byte
  * aligned) holds moe_combine_workspace_size(m) bytes (16 + 24 m, rounded up to 16).

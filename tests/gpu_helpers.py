@@ -71,3 +71,16 @@ class HipEvents:
 
     def destroy(self, ev: int) -> None:
         self.hip.hipEventDestroy(self.C.c_void_p(ev))
+
+
+def elem_rel_err(gpu: np.ndarray, ref: np.ndarray, frac: float = 0.1) -> float:
+    """Reported beside row_rel_err: max over the elements whose reference is at least
+    `frac` of its row's largest magnitude of |gpu - ref| / |ref| (elementwise relative error
+    away from the near-zero entries, where it is ill-posed)."""
+    gpu = np.asarray(gpu, np.float64).reshape(len(ref), -1)
+    ref = np.asarray(ref, np.float64).reshape(len(ref), -1)
+    big = np.abs(ref) >= frac * np.abs(ref).max(axis=1, keepdims=True)
+    big &= ref != 0
+    if not big.any():
+        return 0.0
+    return float((np.abs(gpu - ref)[big] / np.abs(ref)[big]).max())

@@ -8,7 +8,7 @@ import torch
 import asynchronous_moe_expert_amd as M
 import oracle as O
 import workloads as W
-from gpu_helpers import TOL, HipEvents, decode_tensor, dev, row_rel_err, sync_err
+from gpu_helpers import TOL, HipEvents, decode_tensor, dev, elem_rel_err, row_rel_err, sync_err
 from workloads.device import batch_tensors, to_numpy_bits, weight_tensors
 
 pytestmark = pytest.mark.gpu
@@ -467,49 +467,68 @@ def test_fused_plan_matches_separate_plan():
 
 
 @pytest.fixture(scope="module")
-def c4_setup():
-    return W.c4_prefill_setup()
+def c4_ref():
+    """The prefill setup and the oracle's FFN output of every one of its 16384 tokens
+    (token index = pool slot; each token has one local pair, so E_{expert[t]}(x_t) is fixed
+    per token and serves every wave and every merge of waves).  ffn_rows decodes each
+    expert's fp8 weights once."""
+    s = W.c4_prefill_setup()
+    y = O.ffn_rows(O.decode(s.pool, "bf16"), s.expert, s.weights)
+    return s, y
 
 
-@pytest.mark.parametrize("wave", [0, 1, 2, 3])
-def test_c4_prefill_wave_sampled(c4_setup, wave):
-    """Full-size prefill waves (6554 / 4915 / 3277 / 1638 pairs, 32 experts, fp8 weights):
-    integer parts bit-exact; FFN and combined rows on a seeded sample of about 96 rows /
-    tokens.  Waves 0-2 run the 128-row tiled GEMM, wave 3 the weight-streaming kernel with
-    experts of one row chunk and of several (Zipf-skewed counts)."""
-    _say(f"C4 prefill fp8 wave {wave}")
-    s = c4_setup
-    b = W.c4_wave(s, wave)
-    st, e = _run_config_step(b, s.weights, M.MOE_BF16, M.MOE_FP8_E4M3, T_cap=b.T)
+def _check_c4_batch(b, wts, y_ref_all, tol):
+    """Runs one prefill-shaped batch (remote results delivered first) and checks it against
+    the oracle: integer parts bit-exact, every FFN row and every combined row within tol."""
+    st, e = _run_config_step(b, wts, M.MOE_BF16, M.MOE_FP8_E4M3, T_cap=b.T)
     a = O.assemble(b.slot, b.expert, 0, b.E_loc, b.P)
     assert e == 0 == a["err"]
     assert np.array_equal(st.perm.cpu().numpy()[: b.n], a["perm"])
+    assert np.array_equal(st.pos.cpu().numpy()[: b.n], a["pos"])
     assert np.array_equal(st.offsets.cpu().numpy(), a["offsets"])
+    assert np.array_equal(st.counts.cpu().numpy(), a["counts"])
     n_rel = int(st.rel_count.item())
     assert np.array_equal(st.rel_list[:n_rel].cpu().numpy(), np.sort(b.tok))
-    rng = np.random.default_rng(99)
-    # sample rows across experts: the hot expert, cold experts, chunk boundaries
-    rows = np.unique(np.concatenate([rng.choice(b.n, 80, replace=False), a["offsets"][:-1][a["counts"] > 0][:8],
-                                     (a["offsets"][1:][a["counts"] > 0] - 1)[:8]]))
-    x = O.decode(b.pool[b.slot[a["perm"][rows]]], "bf16")
-    le = np.searchsorted(a["offsets"], rows, side="right") - 1
-    y_ref = O.ffn_rows(x, le, s.weights)
-    ey = row_rel_err(decode_tensor(st.y[torch.as_tensor(rows, device="cuda").long()]), y_ref)
-    # combined rows of the sampled tokens: remote parts + the local result
+    # every batch row: row r holds the pair perm[r], whose token (= pool slot) fixes its output
+    y_ref = y_ref_all[b.tok[a["perm"]]]
+    y_gpu = decode_tensor(st.y[: b.n])
+    ey, ee = row_rel_err(y_gpu, y_ref), elem_rel_err(y_gpu, y_ref)
+    del y_gpu
+    # every released token: its remote results plus the local one, in position order
     r = b.remote
-    r_of = {}
+    parts = {}
     for k in range(r.m):
-        r_of.setdefault(int(r.tok[k]), []).append(k)
-    toks = b.tok[a["perm"][rows]]
-    refs = []
-    for qi, t in enumerate(toks):
-        parts = {int(r.kslot[k]): (r.w[k], O.decode_bf16(r.rows[r.row_idx[k]])) for k in r_of[int(t)]}
-        p = a["perm"][rows[qi]]
-        parts[int(b.kslot[p])] = (b.w[p], y_ref[qi])
-        refs.append(O.combine_token([parts[j] for j in range(b.K)]))
-    eo = row_rel_err(decode_tensor(st.out[torch.as_tensor(toks, device="cuda").long()]), np.array(refs))
-    _say(f"  sampled Y row err {ey:.3e}, combined row err {eo:.3e}")
-    assert ey <= TOL["fp8"] and eo <= TOL["fp8"]
+        parts.setdefault(int(r.tok[k]), {})[int(r.kslot[k])] = (r.w[k], r.row_idx[k])
+    refs = np.empty((b.n, b.H))
+    for i in range(b.n):
+        t = int(b.tok[i])
+        full = {j: (w, O.decode_bf16(r.rows[ri])) for j, (w, ri) in parts[t].items()}
+        full[int(b.kslot[i])] = (b.w[i], y_ref_all[t])
+        refs[i] = O.combine_token([full[j] for j in range(b.K)])
+    out_gpu = decode_tensor(st.out[torch.as_tensor(b.tok, device="cuda").long()])
+    eo, eoe = row_rel_err(out_gpu, refs), elem_rel_err(out_gpu, refs)
+    _say(f"  all {b.n} Y rows: row err {ey:.3e} (elementwise {ee:.3e}); all {n_rel} combined rows: "
+         f"row err {eo:.3e} (elementwise {eoe:.3e})")
+    assert ey <= tol and eo <= tol
+
+
+@pytest.mark.parametrize("wave", [0, 1, 2, 3])
+def test_c4_prefill_wave(c4_ref, wave):
+    """Full-size prefill waves (6554 / 4915 / 3277 / 1638 pairs, 32 experts, fp8 weights):
+    integer parts bit-exact; every FFN row and every combined row against the oracle."""
+    _say(f"C4 prefill fp8 wave {wave}")
+    s, y_all = c4_ref
+    _check_c4_batch(W.c4_wave(s, wave), s.weights, y_all, TOL["fp8"])
+
+
+@pytest.mark.parametrize("waves", [(0, 1), (0, 1, 2, 3)], ids=["waves0-1", "waves0-3"])
+def test_c4_merged_waves(c4_ref, waves):
+    """Prefill waves merged into one ready batch (11469 and 16384 pairs: more row chunks per
+    expert and a longer index pass than any single wave): integer parts bit-exact, every
+    FFN row and every combined row against the oracle."""
+    _say(f"C4 prefill fp8, merged waves {waves}")
+    s, y_all = c4_ref
+    _check_c4_batch(W.merge_batches([W.c4_wave(s, w) for w in waves]), s.weights, y_all, TOL["fp8"])
 
 
 GATHER_CASES = [

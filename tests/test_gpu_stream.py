@@ -1,5 +1,7 @@
 """GPU parity on the multi-layer asynchronous stream (36 layers, 72 queues, 16 simulated
-sources with lognormal message delays, most-tokens-first pick, 1000 expert batches).
+sources with lognormal message delays): 1000 expert batches under the most-tokens-first
+pick, and 300 under each of the first-layer-first pick (which fragments the expert batches:
+most of them under 64 pairs) and the defragmenting score ([SEP] section 4).
 
 The stream drives the HIP path and the oracle in lockstep: after every combine call (the
 messages due at a step, or an expert batch) the release lists must be identical, and the
@@ -26,18 +28,14 @@ class _LayerW:  # host copy of one layer's weights in the oracle's input form
         self.wg, self.wu, self.wd = (to_numpy_bits(d[k]) for k in ("wg", "wu", "wd"))
 
 
-def test_c3_stream_lockstep():
+@pytest.fixture(scope="module")
+def packed_layers():
+    """The 36 layers' packed expert weights (the same seeded draws for every policy)."""
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     M.load()
     cfg = StreamConfig()
-    print(f"C3 stream: {cfg.layers} layers, {cfg.tokens} tokens, {cfg.batches} expert batches", flush=True)
-    sim = StreamSim(cfg)
-    rows_f, xs_f = sim.banks()
-    rows_bits, xs_bits = W.to_bf16_bits(rows_f), W.to_bf16_bits(xs_f)
-    rows_t, xs_t = dev(rows_bits, "bf16"), dev(xs_bits, "bf16")
-    del rows_f, xs_f
-    st = M.ExpertStep(cfg.E_loc, cfg.H, cfg.I, cfg.K, M.MOE_BF16, M.MOE_BF16, cfg.cap, cfg.tokens)
+    st = M.ExpertStep(cfg.E_loc, cfg.H, cfg.I, cfg.K, M.MOE_BF16, M.MOE_BF16, 1, 1)
     packed = []
     for l in range(cfg.layers):
         w = device_layer_weights(cfg.seed, l, cfg.E_loc, cfg.H, cfg.I, 0.02)
@@ -46,12 +44,27 @@ def test_c3_stream_lockstep():
         del w
     torch.cuda.synchronize()
     print("  weights packed for all layers", flush=True)
+    return packed
+
+
+@pytest.mark.parametrize("policy,batches", [("mtfs", 1000), ("flfs", 300), ("defrag", 300)])
+def test_c3_stream_lockstep(packed_layers, policy, batches):
+    cfg = StreamConfig(policy=policy, batches=batches)
+    print(f"C3 stream ({policy}): {cfg.layers} layers, {cfg.tokens} tokens, {cfg.batches} expert batches",
+          flush=True)
+    sim = StreamSim(cfg)
+    rows_f, xs_f = sim.banks()
+    rows_bits, xs_bits = W.to_bf16_bits(rows_f), W.to_bf16_bits(xs_f)
+    rows_t, xs_t = dev(rows_bits, "bf16"), dev(xs_bits, "bf16")
+    del rows_f, xs_f
+    st = M.ExpertStep(cfg.E_loc, cfg.H, cfg.I, cfg.K, M.MOE_BF16, M.MOE_BF16, cfg.cap, cfg.tokens)
+    packed = packed_layers
     pool = torch.empty((cfg.tokens, cfg.H), dtype=torch.bfloat16, device="cuda")
     base = cfg.rank * cfg.E_loc
     ocs = O.CombineState(cfg.tokens, cfg.K)
     zr = np.zeros((cfg.row_bank, 1))
     zb = np.zeros((cfg.cap, 1))
-    sample = {0, 1, 333, 666, cfg.batches - 1}
+    sample = {0, 1, cfg.batches // 3, 2 * cfg.batches // 3, cfg.batches - 1}
     parts: dict[int, list] = {}  # token -> [(j, w, row64 or None)] of its current layer
     counters = dict(calls=0, checked_rows=0, checked_tokens=0)
 
@@ -115,6 +128,8 @@ def test_c3_stream_lockstep():
                 if toks else 0.0
             counters["checked_rows"] += b.n
             counters["checked_tokens"] += len(toks)
+            if not toks and k + 1 < cfg.batches:
+                sample.add(k + 1)  # nothing to compare in this batch: sample the next one too
             print(f"  batch {k} layer {b.layer} n={b.n}: Y row err {ey:.3e}, {len(toks)} combined rows err {eo:.3e}",
                   flush=True)
             assert ey <= TOL["bf16"] and eo <= TOL["bf16"]
