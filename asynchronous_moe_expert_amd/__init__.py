@@ -22,6 +22,7 @@ from ._native import (  # noqa: F401
     combine_call,
     load,
     moe_assemble,
+    moe_combine_noalloc_max_arrivals,
     moe_combine_release,
     moe_combine_workspace_size,
     moe_expert_ffn_grouped,

@@ -60,7 +60,8 @@ class CombineArgs(C.Structure):
 _STRUCTS = [AssembleArgs, PackArgs, FfnArgs, StateC, CombineArgs]
 EXPORTS = ["moe_assemble", "moe_pack_ffn_weights", "moe_ffn_workspace_size", "moe_expert_ffn_grouped",
            "moe_state_reset", "moe_combine_release", "moe_combine_plan", "moe_combine_apply",
-           "moe_combine_workspace_size", "moe_strerror", "moe_version", "moe_struct_size"]
+           "moe_combine_workspace_size", "moe_strerror", "moe_version", "moe_struct_size",
+           "moe_combine_release_noalloc", "moe_combine_noalloc_max_arrivals"]
 
 
 class MoeError(RuntimeError):
@@ -86,6 +87,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
                        ("moe_combine_release", [C.POINTER(CombineArgs), _p]),
                        ("moe_combine_plan", [C.POINTER(CombineArgs), _p]),
                        ("moe_combine_apply", [C.POINTER(CombineArgs), _p]),
+                       ("moe_combine_release_noalloc", [C.POINTER(CombineArgs), _p]),
                        ("moe_version", []), ("moe_strerror", [C.c_int])]:
         f = getattr(lib, name)
         f.argtypes = args
@@ -95,6 +97,8 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     lib.moe_ffn_workspace_size.restype = C.c_size_t
     lib.moe_combine_workspace_size.argtypes = [_i32]
     lib.moe_combine_workspace_size.restype = C.c_size_t
+    lib.moe_combine_noalloc_max_arrivals.argtypes = []
+    lib.moe_combine_noalloc_max_arrivals.restype = C.c_size_t
     lib.moe_struct_size.argtypes = [C.c_int]
     lib.moe_struct_size.restype = C.c_size_t
     for k, s in enumerate(_STRUCTS):
@@ -210,11 +214,16 @@ def moe_combine_workspace_size(m_max: int) -> int:
     return load().moe_combine_workspace_size(m_max)
 
 
+def moe_combine_noalloc_max_arrivals() -> int:
+    return load().moe_combine_noalloc_max_arrivals()
+
+
 def _combine_args(rows, row_idx, tok, kslot, w, gen, K, state, out, rel_list, rel_count, err, workspace, m, n_rows):
     return CombineArgs(int(tok.numel() if m is None else m), K, _ptr(rows), dtype_code(rows), rows.stride(0),
                        rows.shape[0] if n_rows is None else n_rows, _ptr(row_idx), _ptr(tok), _ptr(kslot), _ptr(w),
                        _ptr(gen), state.c(), _ptr(out), dtype_code(out), out.stride(0), _ptr(rel_list),
-                       _ptr(rel_count), _ptr(err), _ptr(workspace), workspace.numel() * workspace.element_size())
+                       _ptr(rel_count), _ptr(err), _ptr(workspace),
+                       0 if workspace is None else workspace.numel() * workspace.element_size())
 
 
 def combine_args(rows, row_idx, tok, kslot, w, gen, K: int, state: CombineState, out, rel_list, rel_count, err,
@@ -228,7 +237,9 @@ def moe_combine_release(rows, row_idx, tok, kslot, w, gen, K: int, state: Combin
                         err, workspace, m: int | None = None, n_rows: int | None = None, stream=None,
                         part: str = "release") -> None:
     """rows: [n_rows][pitch] f32/bf16 result rows; out: [T_cap][pitch] f32/bf16.
-    part = "plan" / "apply" calls moe_combine_plan / moe_combine_apply instead."""
+    part = "plan" / "apply" calls moe_combine_plan / moe_combine_apply instead; part =
+    "noalloc" calls moe_combine_release_noalloc (the library's static scratch; workspace
+    may be None)."""
     a = _combine_args(rows, row_idx, tok, kslot, w, gen, K, state, out, rel_list, rel_count, err, workspace, m,
                       n_rows)
     combine_call(a, part, stream)
@@ -236,5 +247,6 @@ def moe_combine_release(rows, row_idx, tok, kslot, w, gen, K: int, state: Combin
 
 def combine_call(a: CombineArgs, part: str = "release", stream=None) -> None:
     """moe_combine_release / _plan / _apply on an argument struct from combine_args."""
-    fn = {"release": "moe_combine_release", "plan": "moe_combine_plan", "apply": "moe_combine_apply"}[part]
+    fn = {"release": "moe_combine_release", "plan": "moe_combine_plan", "apply": "moe_combine_apply",
+          "noalloc": "moe_combine_release_noalloc"}[part]
     _check(getattr(load(), fn)(C.byref(a), _stream(stream)), fn)

@@ -11,6 +11,7 @@ extern "C" const char* moe_strerror(int status) {
     case MOE_EINVAL_SHAPE: return "H or I is not a multiple of the required granule";
     case MOE_EWORKSPACE: return "workspace missing or too small";
     case MOE_ELAUNCH: return "kernel launch failed";
+    case MOE_ESCRATCH: return "more arrivals than the library's static scratch holds";
     default: return "unknown status";
   }
 }

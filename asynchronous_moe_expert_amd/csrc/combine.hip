@@ -32,6 +32,7 @@
 //      writes the released row or the new partial sum.
 // No linked lists, no per-token flag scan over the whole state, one launch fewer.
 #include <algorithm>
+#include <atomic>
 
 #include "combine_plan.hpp"
 #include "common.hpp"
@@ -544,4 +545,53 @@ extern "C" int moe_combine_release(const moe_combine_args* a, hipStream_t stream
   const int rc = moe_combine_plan(a, stream);
   if (rc != MOE_OK) return rc;
   return moe_combine_apply(a, stream);
+}
+
+// ------------------------------------------------------------ allocation-free variant
+// For callers that cannot allocate (code under graph capture, serving loops that forbid
+// hipMalloc): moe_combine_release with the scratch in a library-owned device array instead of
+// the caller's workspace.  The array is sized for kStaticMaxArrivals arrivals; each device
+// holds its own copy, at an address taken once per device with hipGetSymbolAddress (the
+// array's name is only a host-side stand-in and is never passed to a kernel).
+constexpr int kStaticMaxArrivals = 1 << 17;
+constexpr size_t kStaticScratchBytes = (16 + 24 * (size_t)kStaticMaxArrivals + 15) / 16 * 16;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDev = 64;
+std::atomic<void*> g_scratch[kMaxScratchDev];  // per device: the address of its copy of `scratch`
+
+// The device address of the current device's scratch array (looked up on first use with that
+// device current); nullptr with *rc set on failure.
+void* device_scratch(int* rc) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDev) {
+    *rc = MOE_ELAUNCH;
+    return nullptr;
+  }
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  void* q = nullptr;
+  if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) {
+    *rc = MOE_ELAUNCH;
+    return nullptr;
+  }
+  g_scratch[dev].store(q, std::memory_order_release);  // racing first calls store the same address
+  return q;
+}
+}  // namespace
+
+extern "C" size_t moe_combine_noalloc_max_arrivals(void) { return (size_t)kStaticMaxArrivals; }
+
+extern "C" int moe_combine_release_noalloc(const moe_combine_args* a, hipStream_t stream) {
+  if (!a) return MOE_EINVAL_NULL;
+  if (a->m > kStaticMaxArrivals) return MOE_ESCRATCH;
+  int rc = MOE_OK;
+  void* ws = device_scratch(&rc);
+  if (!ws) return rc;
+  static_assert(kStaticScratchBytes >= 16 + 24 * (size_t)kStaticMaxArrivals, "scratch holds the plan path's records");
+  moe_combine_args b = *a;
+  b.workspace = ws;  // every word of it that a call reads was written earlier in the same call
+  b.workspace_bytes = kStaticScratchBytes;
+  return moe_combine_release(&b, stream);
 }

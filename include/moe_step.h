@@ -64,7 +64,8 @@ typedef enum moe_status {
   MOE_EINVAL_ALIGN = -4,   /* a pointer or pitch is not 16-byte aligned */
   MOE_EINVAL_SHAPE = -5,   /* H or I is not a multiple of the required granule */
   MOE_EWORKSPACE = -6,     /* workspace pointer missing or too small */
-  MOE_ELAUNCH = -7         /* the HIP runtime refused a kernel launch */
+  MOE_ELAUNCH = -7,        /* the HIP runtime refused a kernel launch */
+  MOE_ESCRATCH = -8        /* more work than the library's static scratch holds */
 } moe_status;
 
 /* Device error flags (bits OR-ed into *err). */
@@ -308,6 +309,24 @@ int moe_combine_release(const moe_combine_args* args, hipStream_t stream);
  * arguments as moe_combine_release does. */
 int moe_combine_plan(const moe_combine_args* args, hipStream_t stream);
 int moe_combine_apply(const moe_combine_args* args, hipStream_t stream);
+
+/* moe_combine_release for callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops or harnesses that forbid hipMalloc): the same work and results bit
+ * for bit, but the call's scratch lives in a device array owned by the library instead of
+ * args->workspace (workspace and workspace_bytes are ignored and may be NULL / 0).  The
+ * call allocates nothing (no hipMalloc, hipFree or allocating library routine).
+ *   - Limit: at most moe_combine_noalloc_max_arrivals() arrivals (2^17) per call; a larger
+ *     m returns MOE_ESCRATCH and enqueues nothing.  Other arguments are validated as by
+ *     moe_combine_release.
+ *   - Each GPU the library runs on holds one copy of the array (about 3 MiB) until the
+ *     process ends; its address is looked up once per device, on the first call made with
+ *     that device current (a failure returns MOE_ELAUNCH).
+ *   - Every call on one GPU shares that GPU's array, and the array keeps the last call's
+ *     contents (nothing in it needs clearing: a call reads only what it wrote earlier).
+ *     Calls that overlap on one GPU (on different streams, or from several host threads
+ *     without ordering) race on it; order them on one stream or with events. */
+int moe_combine_release_noalloc(const moe_combine_args* args, hipStream_t stream);
+size_t moe_combine_noalloc_max_arrivals(void);
 
 /* ---------------------------------------------------------------------- helpers -- */
 const char* moe_strerror(int status);
