@@ -1058,13 +1058,343 @@ __global__ __launch_bounds__(256) void ffn_gemm_finalize_kernel(const int32_t* _
   gemm_store_group<MODE>(a, bb, mt, g, m0, mend, col0, hf, l32, sc0, sc1, out, out_ld);
 }
 
+// ------------------------------------------------ prefill GEMM with 256-row units (fp8 weights)
+// One workgroup per CU, 4 waves; a unit is (chunk of up to 256 rows of one expert, 256 packed
+// weight columns), each wave computing all 256 rows x its 64 columns (8 x 2 tiles of
+// v_mfma_f32_32x32x16_bf16, 256 fp32 accumulators).  Per 64-wide k-step a unit moves 32 KiB of
+// activations (through a 4-stage LDS ring, buffer_load ... lds) and 16 KiB of fp8 weights (a
+// 4-deep register ring per wave) for 8.4 MFLOP: twice the weight reuse of a 128-row unit, and
+// twice the matrix-core work per k-step to cover each load's latency.  Activation fragments are
+// read from LDS one k-slice ahead (two register sets), weights widened to bf16 in registers.
+// 32-row tiles past a chunk's last row skip their LDS reads and MFMAs, so a unit costs in
+// proportion to its rows (32-row granularity) and the tail chunks of small experts stay cheap.
+//
+// Work order: each workgroup's work is fixed on the device from `offsets` (no host round trip,
+// no atomics).  The chunks are sorted by cost: every full 256-row chunk first (expert order),
+// then each expert's partial last chunk by its 32-row tile count, descending (ties: expert
+// order); a chunk's 256-column blocks are consecutive units.  Round r gives unit r*G + j to
+// workgroup j (reversed in odd rounds: a snake, so that a workgroup that drew a large unit in
+// one round draws a small one in the next), and workgroup j is the j % Gx-th of XCD j / Gx,
+// so a chunk's column blocks run side by side on one XCD and share its activations in L2.
+constexpr int kG2BM = 256;
+constexpr int kG2MT = kG2BM / 32;
+#ifndef MOE_G2_STAGES
+#define MOE_G2_STAGES 4
+#endif
+constexpr int kG2S = MOE_G2_STAGES;
+static_assert(kG2S >= 2 && kG2S <= 4, "two to four LDS stages");
+
+// Chunks of 256 rows in cost order (above), kept in LDS so that no register holds the table
+// across a unit's contraction: per expert its first and end row, full-chunk count and the
+// sorted position of its first full chunk (non-decreasing in expert order), and for each
+// partial chunk's sorted position past the full ones, its expert.  Built by wave 0.
+struct G2Table {
+  int a0[256], a1[256], nf[256], fs[256], pe[256];
+  int E, F, total;
+};
+
+__device__ __forceinline__ void g2_table_build(G2Table& tb, const int32_t* __restrict__ offsets, int E_loc,
+                                               int n_rows, int lane) {
+  int base = 0, pt[4];
+  static_for<4>([&](auto jc) {
+    constexpr int j = jc();
+    const int e = lane + 64 * j;
+    int lo = 0, hi = 0;
+    if (e < E_loc) {  // clamped to [0, n_rows]: inconsistent offsets never address past the batch
+      lo = min(max(offsets[e], 0), n_rows);
+      hi = min(max(offsets[e + 1], lo), n_rows);
+    }
+    const int nf = (hi - lo) / kG2BM;
+    pt[j] = ((hi - lo) % kG2BM + 31) / 32;
+    int incl = nf;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += v;
+    }
+    if (e < E_loc) {
+      tb.a0[e] = lo;
+      tb.a1[e] = hi;
+      tb.nf[e] = nf;
+      tb.fs[e] = base + incl - nf;
+    }
+    base += __shfl(incl, 63, 64);
+  });
+  int pos = 0;
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int t = kG2MT; t >= 1; --t) {
+    static_for<4>([&](auto jc) {
+      constexpr int j = jc();
+      const uint64_t bal = __ballot(pt[j] == t);
+      if (pt[j] == t) tb.pe[pos + __popcll(bal & below)] = lane + 64 * j;
+      pos += __popcll(bal);
+    });
+  }
+  if (lane == 0) {
+    tb.E = E_loc;
+    tb.F = base;
+    tb.total = base + pos;
+  }
+}
+
+// expert, first row and end row of sorted chunk q (0 <= q < total)
+__device__ __forceinline__ void g2_find(const G2Table& tb, int q, int& e, int& m0, int& mend) {
+  if (q < tb.F) {
+    // the last expert whose first full chunk is at or before q (it has q among its full chunks)
+    int lo = 0, hi = tb.E - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (tb.fs[mid] <= q) lo = mid;
+      else hi = mid - 1;
+    }
+    e = lo;
+    m0 = tb.a0[e] + (q - tb.fs[e]) * kG2BM;
+    mend = m0 + kG2BM;
+  } else {
+    e = tb.pe[q - tb.F];
+    m0 = tb.a0[e] + tb.nf[e] * kG2BM;
+    mend = tb.a1[e];
+  }
+}
+
+template <int MODE, int WDT, int MTT>
+__device__ __forceinline__ void gemm_epilogue_mt(const f32x16 (&acc)[MTT][2], int mt_act, int e, int m0, int mend,
+                                                 int col0, int hf, int l32, const float* __restrict__ s0,
+                                                 const float* __restrict__ s1, uint16_t* __restrict__ out,
+                                                 int out_ld) {
+  float sc0, sc1;
+  gemm_scales<MODE, WDT>(e, col0, l32, s0, s1, out_ld, sc0, sc1);
+  static_for<MTT>([&](auto mt) {
+    if (mt() < mt_act) {
+      static_for<4>([&](auto g) {
+        float a[4], b[4];
+        static_for<4>([&](auto k) {
+          a[k()] = acc[mt()][0][4 * g() + k()];
+          b[k()] = acc[mt()][1][4 * g() + k()];
+        });
+        gemm_store_group<MODE>(a, b, mt(), g(), m0, mend, col0, hf, l32, sc0, sc1, out, out_ld);
+      });
+    }
+  });
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256, 1) void ffn_gemm256_kernel(const uint16_t* __restrict__ A,
+                                                            const int32_t* __restrict__ offsets, int E_loc,
+                                                            const char* __restrict__ W,
+                                                            const float* __restrict__ s0,
+                                                            const float* __restrict__ s1,
+                                                            uint16_t* __restrict__ out, int Kd, int Nw, int out_ld,
+                                                            int n_blocks_N, int n_rows, GatherRows gr) {
+  constexpr int S = kG2S;
+  constexpr int WDT = MOE_FP8_E4M3;
+  // activation k-tiles, one array per stage (so that an LDS read waits only for the copy into
+  // its own stage): 256 rows x 64 k bf16 = 32 KiB each
+  __shared__ u32x4 g2_lds0[kG2BM * 8], g2_lds1[kG2BM * 8], g2_lds2[S > 2 ? kG2BM * 8 : 1],
+      g2_lds3[S > 3 ? kG2BM * 8 : 1];
+  auto stage = [&](auto st) -> u32x4* {
+    if constexpr (st() == 0) return g2_lds0;
+    else if constexpr (st() == 1) return g2_lds1;
+    else if constexpr (st() == 2) return g2_lds2;
+    else return g2_lds3;
+  };
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int KS = Kd / kBK;
+  const int64_t strip_stride = (int64_t)KS * 1024;
+  const int l32 = lane & 31, hf = lane >> 5;
+
+  __shared__ G2Table tab;
+  if (wv == 0) g2_table_build(tab, offsets, E_loc, n_rows, lane);
+  __syncthreads();
+  const int U = tab.total * n_blocks_N;
+  const int G = gridDim.x, Gx = G >> 3, b = blockIdx.x;
+  const int jw = (b & 7) * Gx + (b >> 3);  // logical workgroup: XCD-major
+#pragma clang loop unroll(disable)
+  for (int r = 0;; ++r) {
+    const int u = r * G + ((r & 1) ? G - 1 - jw : jw);
+    if (u >= U) break;
+    const int q = u / n_blocks_N, nb = u - q * n_blocks_N;
+    int e, m0, mend;
+    g2_find(tab, q, e, m0, mend);
+    e = __builtin_amdgcn_readfirstlane(e);
+    m0 = __builtin_amdgcn_readfirstlane(m0);
+    mend = __builtin_amdgcn_readfirstlane(mend);
+    const int mt_act = __builtin_amdgcn_readfirstlane((mend - m0 + 31) / 32);
+    const int col0 = nb * kGemmBN + wv * kGemmWaveN;
+    const bool wact = col0 < Nw;       // the last column block may be partial
+    const int colw = wact ? col0 : 0;  // idle waves stream valid weights (results unused)
+    const __amdgpu_buffer_rsrc_t wrs = buffer_rsrc(W + (int64_t)e * Nw * Kd, (int64_t)Nw * Kd);
+    const int w_end = Nw * Kd;  // (the host keeps an expert's matrix under 2^30 bytes)
+    int wvo[2];
+    static_for<2>([&](auto t) {
+      const int half = l32 >> 4, rr = l32 & 15;
+      const int strip = colw / 16 + (MODE == 0 ? 2 * half + t() : 2 * t() + half);
+      wvo[t()] = (int)(strip * strip_stride) + (32 * hf + rr) * 16;
+    });
+    const __amdgpu_buffer_rsrc_t ars =
+        buffer_rsrc(A, gr.perm ? gr.P * gr.pitch * 2 : (int64_t)n_rows * Kd * 2);
+    // LDS slot of this lane's fragment of k-slice ss in row tile 0 (tile mt adds 256 slots:
+    // rows 32 mt + l32 keep the swizzle term of rows l32)
+    int lds_off[4];
+    static_for<4>([&](auto ss) { lds_off[ss()] = l32 * 8 + ((4 * hf + ss()) ^ ((l32 >> 1) & 7)); });
+
+    // The unit with MTA row tiles of 32 rows (the chunk's rows rounded up to 64): the k-loop is
+    // instantiated for MTA = 2, 4, 6, 8, so that a chunk of few rows copies, reads and multiplies
+    // only its tiles, without per-tile branches inside the loop.
+    auto unit = [&](auto mta) {
+      constexpr int MTA = mta();
+      // activation copies: instruction d of this wave fills the 16-byte slots (4 d + wv) * 64 +
+      // lane of a stage; slot P holds row P / 8, piece (P % 8) ^ ((P / 8 >> 1) & 7) of that row
+      // (rows past the chunk copy its last row; their results are never stored)
+      int avo[MTA];
+      static_for<MTA>([&](auto d) {
+        const int P = (4 * d() + wv) * 64 + lane, row = P >> 3, kq = (P & 7) ^ ((row >> 1) & 7);
+        const int rr = min(m0 + row, mend - 1);
+        avo[d()] = (int)((gr.row_offset(rr, Kd) + kq * 8) * 2);
+      });
+      f32x16 acc[MTA][2];
+      static_for<MTA>([&](auto i) { static_for<2>([&](auto jj) { acc[i()][jj()] = f32x16{}; }); });
+      GemmW<WDT> wr[S];
+      u32x4 af[2][MTA];
+      auto issue_a = [&](auto slot, int ks) {
+        ks = min(ks, KS - 1);
+        static_for<MTA>([&](auto d) {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              ars, (__attribute__((address_space(3))) void*)(stage(slot) + (4 * d() + wv) * 64), 16, avo[d()],
+              ks * kBK * 2, 0, 0);
+        });
+      };
+      // weights of k-step ks; past the contraction the offset lies beyond the expert's matrix,
+      // where buffer loads return zeros, so those steps' MFMAs add nothing
+      auto issue_w = [&](auto slot, int ks) { wr[slot()].load(wrs, wvo, ks < KS ? ks * 1024 : w_end); };
+      auto read = [&](auto stg, auto ss, auto buf) {  // fragments of k-slice ss
+        const u32x4* tile = stage(stg);
+        static_for<MTA>([&](auto mt) { af[buf()][mt()] = tile[mt() * 256 + lds_off[ss()]]; });
+      };
+      bf16x8 bwb[2][2];  // widened weight fragments of two k-slices (this one and the next)
+      auto cvt = [&](auto slot, auto ss, auto dst) {
+        static_for<2>([&](auto t) { bwb[dst()][t()] = wr[slot()].frag(t(), ss()); });
+      };
+      auto mfma = [&](auto buf, auto wbuf) {
+        static_for<MTA>([&](auto mt) {
+          bf16x8 a;
+          __builtin_memcpy(&a, &af[buf()][mt()], 16);
+          static_for<2>([&](auto t) {
+            acc[mt()][t()] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bwb[wbuf()][t()], acc[mt()][t()], 0, 0, 0);
+          });
+        });
+      };
+      // One wave per SIMD issues in order, so an instruction between two MFMAs costs matrix-core
+      // time unless it fits in the shadow of the MFMA before it: the next slice's LDS reads,
+      // weight widening and (at the step boundary) the copies are spread one or two per MFMA.
+      auto interleave = [&]() {
+        static_for<2 * MTA>([&](auto) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x122, 2, 0);  // up to two LDS reads / VALU / VMEM reads
+        });
+      };
+      auto barrier = [&]() {
+        __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      };
+      using I0 = std::integral_constant<int, 0>;
+      using I1 = std::integral_constant<int, 1>;
+      using I2 = std::integral_constant<int, 2>;
+      using I3 = std::integral_constant<int, 3>;
+      constexpr int kA = MTA, kW = GemmW<WDT>::kLoads;
+      // Step i (stage and weight slot i % S): while the MFMAs of slice s run, slice s+1's
+      // activation fragments are read and its weight fragments widened.  After slice 2 this wave
+      // waits for its copy of step i+1 and the workgroup meets at a barrier (then every wave's
+      // copy of step i+1 has landed and every wave has read the stage of step i); slice 3's MFMAs
+      // then cover the copy of step i+S into that stage, slice 0 of step i+1 and the weights of
+      // step i+S, loaded into the slot step i has released.  Behind the copy of step i+1 are its
+      // weights and S-2 later (copy, weights) batches.  Steps past the contraction (when S does
+      // not divide it) copy clamped activations and multiply them by zero weights.
+      static_for<S>([&](auto v) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue_a(v, v());
+        issue_w(v, v());
+      });
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<kW + (S - 1) * (kA + kW)>();  // the copy of step 0
+      barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      read(I0{}, I0{}, I0{});
+      cvt(I0{}, I0{}, I0{});
+      const int n_steps = (KS + S - 1) / S * S;
+#pragma clang loop unroll(disable)
+      for (int it = 0; it < n_steps; it += S) {
+        static_for<S>([&](auto v) {
+          using SL = std::integral_constant<int, v()>;
+          using NX = std::integral_constant<int, (v() + 1) % S>;
+          const int i = it + v();
+          __builtin_amdgcn_sched_barrier(0);
+          read(SL{}, I1{}, I1{});
+          cvt(SL{}, I1{}, I1{});
+          mfma(I0{}, I0{});
+          interleave();
+          __builtin_amdgcn_sched_barrier(0);
+          read(SL{}, I2{}, I0{});
+          cvt(SL{}, I2{}, I0{});
+          mfma(I1{}, I1{});
+          interleave();
+          __builtin_amdgcn_sched_barrier(0);
+          read(SL{}, I3{}, I1{});
+          cvt(SL{}, I3{}, I1{});
+          mfma(I0{}, I0{});
+          interleave();
+          __builtin_amdgcn_sched_barrier(0);
+          wait_vmcnt<kW + (S - 2) * (kA + kW)>();  // the copy of step i+1
+          barrier();
+          __builtin_amdgcn_sched_barrier(0);
+          issue_a(SL{}, i + S);  // the stage of step i is free now
+          read(NX{}, I0{}, I0{});
+          cvt(NX{}, I0{}, I0{});
+          mfma(I1{}, I1{});
+          issue_w(SL{}, i + S);  // (slot SL's raw weights were all widened above)
+          interleave();
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      }
+      // no copy may still be in flight into a stage the next unit's prologue fills, and the
+      // next unit's copies wait for this unit's last LDS reads
+      wait_vmcnt<0>();
+      barrier();
+      if (wact) gemm_epilogue_mt<MODE, WDT, MTA>(acc, MTA, e, m0, mend, col0, hf, l32, s0, s1, out, out_ld);
+    };
+    switch ((mt_act + 1) >> 1) {
+      case 1: unit(std::integral_constant<int, 2>{}); break;
+      case 2: unit(std::integral_constant<int, 4>{}); break;
+      case 3: unit(std::integral_constant<int, 6>{}); break;
+      default: unit(std::integral_constant<int, 8>{}); break;
+    }
+  }
+}
+
 // parts: kGemmSplitSlots partial tiles of workspace, or nullptr (tail units run whole).
 // ev0, ev1: optional timestamps taken by the dispatches themselves, at the start of the GEMM
 // and at the end of the last launch of the projection (the finalize, if any).
+#ifndef MOE_FFN_GEMM256
+#define MOE_FFN_GEMM256 1  // fp8 weights: 256-row units (0: the 128-row two-workgroup kernel)
+#endif
 template <int MODE, int WDT>
 static void launch_gemm(const void* A, const int32_t* offsets, int E_loc, const void* W, const float* s0,
                         const float* s1, void* out, int Kd, int Nw, int out_ld, int n, GatherRows gr, float* parts,
                         hipEvent_t ev0, hipEvent_t ev1, hipStream_t stream) {
+  if constexpr (WDT == MOE_FP8_E4M3 && MOE_FFN_GEMM256) {
+    // (takes_gemm keeps each expert's fp8 matrix under 2^30 bytes: 32-bit weight offsets)
+    constexpr auto k256 = ffn_gemm256_kernel<MODE>;
+    const int n_blocks_N = (Nw + kGemmBN - 1) / kGemmBN;
+    const int64_t chunks_max = (n + (int64_t)(kG2BM - 1) * E_loc) / kG2BM;
+    int64_t grid = std::min<int64_t>(chunks_max * n_blocks_N, resident_workgroups<k256>(256));
+    grid = (grid + 7) / 8 * 8;  // the XCD-major order needs a multiple of 8
+    (void)parts;
+    hipExtLaunchKernelGGL(k256, dim3((unsigned)grid), dim3(256), 0, stream, ev0, ev1, 0, (const uint16_t*)A, offsets,
+                          E_loc, (const char*)W, s0, s1, (uint16_t*)out, Kd, Nw, out_ld, n_blocks_N, n, gr);
+    return;
+  }
   constexpr auto kernel = ffn_gemm_kernel<MODE, WDT>;
   const int n_blocks_N = (Nw + kGemmBN - 1) / kGemmBN;
   const int64_t chunks_max = (n + (int64_t)(kGemmBM - 1) * E_loc) / kGemmBM;
@@ -1126,9 +1456,13 @@ static int pick_mt(int n, int E_loc) {
 
 // whether a projection over n rows takes the tiled GEMM kernel (the GEMM kernel addresses its
 // activation operand with 32-bit byte offsets)
-static bool takes_gemm(int n, int E_loc, int Kd, const GatherRows& gr) {
+// (the tiled kernels address activations with 32-bit byte offsets, and the 256-row kernel
+// an expert's weight matrix too, with zero-returning loads just past its end)
+static bool takes_gemm(int n, int E_loc, int Kd, int Nw, int w_esz, const GatherRows& gr) {
   const int64_t a_bytes = gr.perm ? gr.P * gr.pitch * 2 : (int64_t)n * Kd * 2;
-  return MOE_FFN_MT == 0 && n >= MOE_FFN_GEMM_ROWS * E_loc && a_bytes < ((int64_t)1 << 31);
+  const int64_t w_bytes = (int64_t)Nw * Kd * w_esz;
+  return MOE_FFN_MT == 0 && n >= MOE_FFN_GEMM_ROWS * E_loc && a_bytes < ((int64_t)1 << 31) &&
+         w_bytes < ((int64_t)1 << 30);
 }
 
 // plan: a combine plan for the streaming gate/up launch's spare workgroup (m = 0: none;
@@ -1140,7 +1474,7 @@ static void launch_mfma(const void* A, const int32_t* offsets, int E_loc, const 
   constexpr int NS = MODE == 0 ? MOE_FFN_NS_GU : MOE_FFN_NS_D;
   constexpr int R = MODE == 0 ? MOE_FFN_R_GU : MOE_FFN_R_D;
   constexpr int WV = MODE == 0 ? MOE_FFN_WV_GU : MOE_FFN_WV_D;
-  if (takes_gemm(n, E_loc, Kd, gr)) {
+  if (takes_gemm(n, E_loc, Kd, Nw, WDT == MOE_FP8_E4M3 ? 1 : 2, gr)) {
     launch_gemm<MODE, WDT>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, gr, parts, ev0, ev1, stream);
     return;
   }
@@ -1254,7 +1588,7 @@ extern "C" int moe_expert_ffn_grouped(const moe_ffn_args* a, hipStream_t stream)
     if (a->workspace_bytes >= off + kPartAreaBytes) parts = (float*)((char*)a->workspace + off);
   }
   // the plan joins the gate/up launch of the streaming kernel, else it runs before the FFN
-  if (f32 || takes_gemm(n, E, H, gr)) job.m = 0;
+  if (f32 || takes_gemm(n, E, H, 2 * I, f8 ? 1 : 2, gr)) job.m = 0;
   if (a->plan && job.m == 0) {
     const int rc = moe_combine_plan(a->plan, stream);
     if (rc != MOE_OK) return rc;

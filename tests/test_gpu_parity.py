@@ -721,11 +721,54 @@ def _gemm_split_plan(counts, Nw, Kd, G_res):
     return out
 
 
-@pytest.mark.parametrize("wdt", ["fp8", "bf16"])
+GEMM256_CASES = [
+    # (E, H, I, counts): 256-row units over every tile-count variant (a last chunk of 1..64,
+    # 65..128, 129..192 and 193..255 rows), an empty expert, full chunks, a partial last column
+    # block (Nw = 640: two of four waves active), contractions of 10 and 5 k-steps (not a
+    # multiple of the ring depth) ...
+    (6, 640, 320, [600, 0, 40, 150, 230, 513]),
+    # ... and more units than workgroups (18 chunks x 16 gate/up column blocks: two rounds)
+    (2, 512, 2048, [3000, 1500]),
+]
+
+
+@pytest.mark.parametrize("case", GEMM256_CASES, ids=[f"E{c[0]}_H{c[1]}_I{c[2]}" for c in GEMM256_CASES])
+def test_gemm256_fp8_units(case):
+    """The fp8 tiled FFN (256-row units in cost order): every row against the oracle, the same
+    bits on a second run, and the same bits with a workspace holding only h."""
+    E, H, I, counts = case
+    n = int(sum(counts))
+    _say("gemm256 case", case)
+    rng = np.random.default_rng(H + I + n)
+    wts = W.make_layer_weights(rng, E, H, I, 0.05, "fp8")
+    x_np = W.to_bf16_bits(rng.standard_normal((n, H)).astype(np.float32))
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    st = M.ExpertStep(E, H, I, 2, M.MOE_BF16, M.MOE_FP8_E4M3, n, 4)
+    wt = weight_tensors(wts)
+    st.load_weights(wt["wg"], wt["wu"], wt["wd"], wt["s_gate"], wt["s_up"], wt["s_down"])
+    st.xb[:n].copy_(dev(x_np, "bf16"))
+    st.offsets.copy_(dev(offsets))
+    h_bytes = (n * I * 2 + 255) // 256 * 256
+    ys = []
+    for ws in (st.workspace, st.workspace, st.workspace[:h_bytes]):
+        st.y.zero_()
+        M.moe_expert_ffn_grouped(n, E, H, I, M.MOE_BF16, M.MOE_FP8_E4M3, st.xb, st.offsets, st.w_gu, st.w_d, st.y,
+                                 ws, st.s_gate, st.s_up, st.s_down)
+        torch.cuda.synchronize()
+        ys.append(to_numpy_bits(st.y[:n]))
+    assert np.array_equal(ys[0], ys[1]) and np.array_equal(ys[0], ys[2])
+    y_ref = O.expert_ffn(O.decode(x_np, "bf16"), offsets, wts)
+    y_gpu = O.decode_bf16(ys[0])
+    err, ee = row_rel_err(y_gpu, y_ref), elem_rel_err(y_gpu, y_ref)
+    _say(f"  all {n} rows: row rel err {err:.3e} (elementwise {ee:.3e})")
+    assert err <= TOL["fp8"]
+
+
+@pytest.mark.parametrize("wdt", ["bf16"])
 def test_gemm_split_tail_matches_whole_units(wdt):
-    """Tiled FFN kernel with each XCD's last partial round split along the contraction: the
-    result is deterministic, matches the run with whole tail units (workspace without the
-    partial area) to rounding, and matches the oracle on rows of the split units."""
+    """Tiled FFN kernel for bf16 weights with each XCD's last partial round split along the
+    contraction: the result is deterministic, matches the run with whole tail units (workspace
+    without the partial area) to rounding, and matches the oracle on rows of the split units."""
     # 67 chunks x 16 gate/up column blocks = 134 units per XCD: a tail of 6 whether the kernel
     # runs one workgroup per CU (4 full rounds of 32) or two (2 full rounds of 64)
     E, H, I = 8, 1024, 2048
