@@ -6,7 +6,8 @@
 // grouped FFN sees one contiguous row range per expert.
 //
 // Two kernels:
-//   1. index kernel (one workgroup of 1024 threads, 256 for small queues): per-expert histogram in LDS, a wave scan
+//   1. index kernel (one workgroup of 1024 threads, 256 for small queues; one workgroup per
+//      1024-pair segment for longer queues, see assemble_index_multi_kernel): per-expert histogram in LDS, a wave scan
 //      for the exclusive offsets, then a stable scatter of queue indices.  Stability
 //      inside each chunk of one pair per thread comes from a 9-bit wave "match" (ballot per
 //      key bit) giving each pair its rank among equal keys of lower lanes, plus per-wave
@@ -161,6 +162,141 @@ __global__ __launch_bounds__(kAsmThreads) void assemble_index_kernel(
   if (tid == 0 && s_err) atomicOr(err, s_err);
 }
 
+// Queues of more than one chunk: one workgroup of 1024 threads per 1024-pair segment of the
+// queue.  Every workgroup counts all n keys (a few KiB of L2-resident ids per workgroup), so each
+// one derives the same per-expert counts and offsets, and it also counts the keys before its own
+// segment; it then scatters only its segment, stably, from running positions offsets[e] + (keys
+// of expert e before the segment).  No workgroup waits for another and no scratch is needed.
+// Workgroup 0 writes counts, offsets and the error bits (it sees every key).
+__global__ __launch_bounds__(1024) void assemble_index_multi_kernel(
+    int n, const int32_t* __restrict__ slot, const int32_t* __restrict__ expert, int base, int E_loc, int64_t P,
+    int32_t* __restrict__ perm, int32_t* __restrict__ pos, int32_t* __restrict__ row_slot,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, uint32_t* __restrict__ err) {
+  constexpr int kT = 1024, kWaves = kT / kWave;
+  __shared__ int s_cnt[kMaxElocAsm];     // all keys, per expert
+  __shared__ int s_before[kMaxElocAsm];  // keys before this segment, per expert
+  __shared__ int s_run[kMaxElocAsm];
+  __shared__ int s_wcnt[kWaves][kMaxElocAsm + 1];
+  __shared__ int s_total;
+  __shared__ unsigned s_err;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int seg0 = blockIdx.x * kT;
+  for (int e = tid; e < E_loc; e += kT) {
+    s_cnt[e] = 0;
+    s_before[e] = 0;
+  }
+  if (tid == 0) s_err = 0u;
+  __syncthreads();
+  // pass 1: every key (validated), counted in total and, before this segment, separately
+  // (kU chunks of ids are loaded before any of them is counted: one round trip per kU chunks)
+  constexpr int kU = 8;
+  unsigned myerr = 0u;
+  int my_key = kMaxElocAsm, my_slot = 0;
+  for (int i0 = 0; i0 < n; i0 += kU * kT) {
+    int sv[kU], ev[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = i0 + u * kT + tid;
+      sv[u] = i < n ? slot[i] : 0;
+      ev[u] = i < n ? expert[i] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = i0 + u * kT + tid;
+      if (i < n) {
+        const int e = ev[u] - base;
+        bool ok = true;
+        if (sv[u] < 0 || (int64_t)sv[u] >= P) { myerr |= MOE_ERR_SLOT_RANGE; ok = false; }
+        if (e < 0 || e >= E_loc) { myerr |= MOE_ERR_EXPERT_NONLOCAL; ok = false; }
+        if (ok) {
+          atomicAdd(&s_cnt[e], 1);
+          if (i < seg0) atomicAdd(&s_before[e], 1);
+        }
+        if (i == seg0 + tid) {  // this thread's own pair of the segment
+          my_key = ok ? e : kMaxElocAsm;
+          my_slot = sv[u];
+        }
+      }
+    }
+  }
+  if (blockIdx.x == 0 && myerr) atomicOr(&s_err, myerr);
+  __syncthreads();
+  // exclusive scan of the counts (wave 0; 4 experts per lane covers E_loc <= 256)
+  if (wv == 0) {
+    int v[4], sum = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = lane * 4 + k;
+      v[k] = e < E_loc ? s_cnt[e] : 0;
+      sum += v[k];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int t = __shfl_up(incl, d);
+      if (lane >= d) incl += t;
+    }
+    int run = incl - sum;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = lane * 4 + k;
+      if (e < E_loc) {
+        if (blockIdx.x == 0) {
+          counts[e] = v[k];
+          offsets[e] = run;
+        }
+        s_run[e] = run + s_before[e];  // this segment's first row of expert e
+      }
+      run += v[k];
+    }
+    if (lane == 63) {
+      if (blockIdx.x == 0) offsets[E_loc] = incl;
+      s_total = incl;
+    }
+  }
+  __syncthreads();
+  // pass 2: stable scatter of this segment (one pair per thread): rank among equal keys of
+  // lower lanes from a 9-bit ballot match, plus the counts of the lower waves
+  const int i = seg0 + tid;
+  for (int x = tid; x < kWaves * E_loc; x += kT) s_wcnt[x / E_loc][x % E_loc] = 0;
+  __syncthreads();
+  uint64_t peers = ~0ull;
+#pragma unroll
+  for (int b = 0; b < 9; ++b) {
+    const bool bit = (my_key >> b) & 1;
+    const uint64_t bal = __ballot(bit);
+    peers &= bit ? bal : ~bal;
+  }
+  const int rank = __popcll(peers & ((1ull << lane) - 1ull));
+  if (my_key < kMaxElocAsm && rank == 0) s_wcnt[wv][my_key] = __popcll(peers);
+  __syncthreads();
+  if (tid < E_loc) {
+    int run = s_run[tid];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const int cnt = s_wcnt[w][tid];
+      s_wcnt[w][tid] = run;
+      run += cnt;
+    }
+  }
+  __syncthreads();
+  if (my_key < kMaxElocAsm) {
+    const int r = s_wcnt[wv][my_key] + rank;
+    perm[r] = i;
+    if (pos) pos[i] = r;
+    if (row_slot) row_slot[r] = my_slot;
+  } else if (i < n && pos) {
+    pos[i] = -1;
+  }
+  // rows past the accepted pairs, split over the workgroups by segment
+  const int total = s_total;
+  if (i < n && i >= total) {
+    perm[i] = -1;
+    if (row_slot) row_slot[i] = -1;
+  }
+  if (blockIdx.x == 0 && tid == 0 && s_err) atomicOr(err, s_err);
+}
+
 __global__ __launch_bounds__(256) void gather_rows_kernel(const int32_t* __restrict__ perm,
                                                            const int32_t* __restrict__ slot,
                                                            const int32_t* __restrict__ n_valid_ptr,
@@ -198,9 +334,13 @@ extern "C" int moe_assemble(const moe_assemble_args* a, hipStream_t stream) {
   if (a->n <= 256)
     hipLaunchKernelGGL(assemble_index_kernel<256>, dim3(1), dim3(256), 0, stream, a->n, a->slot, a->expert,
                        a->expert_base, a->E_loc, a->P, a->perm, a->pos, a->row_slot, a->counts, a->offsets, a->err);
-  else
+  else if (a->n <= 1024)
     hipLaunchKernelGGL(assemble_index_kernel<1024>, dim3(1), dim3(1024), 0, stream, a->n, a->slot, a->expert,
                        a->expert_base, a->E_loc, a->P, a->perm, a->pos, a->row_slot, a->counts, a->offsets, a->err);
+  else
+    hipLaunchKernelGGL(assemble_index_multi_kernel, dim3((unsigned)((a->n + 1023) / 1024)), dim3(1024), 0, stream,
+                       a->n, a->slot, a->expert, a->expert_base, a->E_loc, a->P, a->perm, a->pos, a->row_slot,
+                       a->counts, a->offsets, a->err);
   if (a->n == 0 || !a->xb) return launch_status();  // no xb: the FFN gathers on load
   const int cpr = row_bytes / 16;
   const int64_t work = (int64_t)a->n * cpr;

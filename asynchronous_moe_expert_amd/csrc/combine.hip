@@ -85,6 +85,7 @@ constexpr int kCmbThreads = 384;
 #endif
 constexpr int kMergeThreads = MOE_MERGE_THREADS;  // merge workgroup (one per arrival)
 constexpr int kMaxChain = 64;  // arrivals of one token handled per pass of the merge
+constexpr int kMergeVec = 4;   // 8-element vectors per thread loaded in one batch (rows up to 8192 wide)
 
 // Kernel 1: one thread per arrival.  Range and generation checks, then a push onto the
 // token's arrival list (head[t] = newest arrival, next[i] = the one pushed before it).
@@ -139,7 +140,10 @@ __global__ __launch_bounds__(kMergeThreads) void combine_merge_kernel(
   const float w_i = wgt[i];
   const int64_t r_i = row_idx[i];
   if (nx == -2) return;       // rejected by the range/generation checks
-  if (head[t] != i) return;   // another arrival owns this token
+  // the list head and the token's mask in one round trip (the mask is used only by the owner)
+  const int h_t = head[t];
+  const uint32_t m_t = mask[t];
+  if (h_t != i) return;   // another arrival owns this token
   const uint32_t full = K >= 32 ? 0xffffffffu : ((1u << K) - 1u);
   float* a = acc + (int64_t)t * H;
   TO* o = out + (int64_t)t * out_pitch;
@@ -147,26 +151,55 @@ __global__ __launch_bounds__(kMergeThreads) void combine_merge_kernel(
   if (nx == -1) {
     // the token's only arrival of this call (every token of a prefill wave): no list to
     // walk or sort, the same accept rule and the same fp32 operations as below
-    const uint32_t m_old = mask[t], bit = 1u << j_i;
+    const uint32_t m_old = m_t, bit = 1u << j_i;
     const bool dup = (m_old & bit) != 0u;
     const uint32_t m_new = m_old | bit;
     const bool complete = !dup && m_new == full;
     if (!dup) {
       const bool started = m_old != 0u;
       const TR* x_row = rows + r_i * row_pitch;
-      for (int v = tid; v < nv; v += kMergeThreads) {
-        float sum[8], x[8];
-        if (started) {
-          RowIO<float>::load8(a + v * 8, sum);
-        } else {
+      if (nv <= kMergeVec * kMergeThreads) {
+        // rows of up to kMergeVec vectors per thread: every load is issued before the first
+        // sum, so one round trip covers the held partial sum and the result row
+        float sum[kMergeVec][8], x[kMergeVec][8];
 #pragma unroll
-          for (int k = 0; k < 8; ++k) sum[k] = 0.f;
+        for (int q = 0; q < kMergeVec; ++q) {
+          const int v = tid + q * kMergeThreads;
+          if (v < nv) {
+            if (started) {
+              RowIO<float>::load8(a + v * 8, sum[q]);
+            } else {
+#pragma unroll
+              for (int k = 0; k < 8; ++k) sum[q][k] = 0.f;
+            }
+            RowIO<TR>::load8(x_row + v * 8, x[q]);
+          }
         }
-        RowIO<TR>::load8(x_row + v * 8, x);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) sum[k] = fmaf(w_i, x[k], sum[k]);
-        if (complete) RowIO<TO>::store8(o + v * 8, sum);
-        else RowIO<float>::store8(a + v * 8, sum);
+        for (int q = 0; q < kMergeVec; ++q) {
+          const int v = tid + q * kMergeThreads;
+          if (v < nv) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) sum[q][k] = fmaf(w_i, x[q][k], sum[q][k]);
+            if (complete) RowIO<TO>::store8(o + v * 8, sum[q]);
+            else RowIO<float>::store8(a + v * 8, sum[q]);
+          }
+        }
+      } else {
+        for (int v = tid; v < nv; v += kMergeThreads) {
+          float sum[8], x[8];
+          if (started) {
+            RowIO<float>::load8(a + v * 8, sum);
+          } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) sum[k] = 0.f;
+          }
+          RowIO<TR>::load8(x_row + v * 8, x);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) sum[k] = fmaf(w_i, x[k], sum[k]);
+          if (complete) RowIO<TO>::store8(o + v * 8, sum);
+          else RowIO<float>::store8(a + v * 8, sum);
+        }
       }
     }
     if (tid == 0) {
@@ -185,7 +218,7 @@ __global__ __launch_bounds__(kMergeThreads) void combine_merge_kernel(
   const int cursor = i;  // list head
   int lo = -1;      // arrivals with index <= lo are already merged
   bool have = false;  // acc values of this call live in `a` (not yet in registers)
-  if (tid == 0) s_mask0 = mask[t];
+  if (tid == 0) s_mask0 = m_t;
   __syncthreads();
   uint32_t m_now = s_mask0;
   bool started = m_now != 0u;  // acc[t] holds earlier results
@@ -283,14 +316,41 @@ constexpr int kRelThreads = 1024;
 // Kernel 3: ascending compaction of the tokens whose release flag is set: 16 flags per
 // thread per pass (one 16-byte load), a workgroup-wide exclusive scan of the per-thread
 // counts, then each thread writes its tokens in order and clears their flags.
-__global__ __launch_bounds__(kRelThreads) void combine_release_kernel(int T_cap, uint8_t* __restrict__ rflag,
+// Only tokens that this call's arrivals name can hold a flag, so the scan covers the 16-token
+// groups from the smallest to the largest such token (clamped into the state) rather than
+// the whole state.
+__global__ __launch_bounds__(kRelThreads) void combine_release_kernel(int T_cap, int m, const int32_t* __restrict__ tok,
+                                                                      uint8_t* __restrict__ rflag,
                                                                       int32_t* __restrict__ rel_list,
                                                                       int32_t* __restrict__ rel_count) {
   __shared__ int s_wtot[kRelThreads / 64];
+  __shared__ int s_lo[kRelThreads / 64], s_hi[kRelThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int nvec = (T_cap + 15) >> 4;
+  int lo = T_cap, hi = -1;
+  for (int x = tid; x < m; x += kRelThreads) {
+    const int t = min(max(tok[x], 0), T_cap - 1);
+    lo = min(lo, t);
+    hi = max(hi, t);
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    lo = min(lo, __shfl_xor(lo, d));
+    hi = max(hi, __shfl_xor(hi, d));
+  }
+  if (lane == 0) {
+    s_lo[wv] = lo;
+    s_hi[wv] = hi;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kRelThreads / 64; ++w) {
+    lo = min(lo, s_lo[w]);
+    hi = max(hi, s_hi[w]);
+  }
+  const int vlo = hi < 0 ? 0 : lo >> 4;
+  const int nvec = hi < 0 ? 0 : (hi >> 4) + 1;
   int base = 0;
-  for (int v0 = 0; v0 < nvec; v0 += kRelThreads) {
+  for (int v0 = vlo; v0 < nvec; v0 += kRelThreads) {
     const int v = v0 + tid;
     uint4 f = make_uint4(0u, 0u, 0u, 0u);
     if (v < nvec) f = reinterpret_cast<const uint4*>(rflag)[v];
@@ -536,8 +596,8 @@ extern "C" int moe_combine_apply(const moe_combine_args* a, hipStream_t stream) 
     else if (ob) launch_merge<float, uint16_t>(a, stream);
     else launch_merge<float, float>(a, stream);
   }
-  hipLaunchKernelGGL(combine_release_kernel, dim3(1), dim3(kRelThreads), 0, stream, a->state.T_cap, a->state.rflag,
-                     a->rel_list, a->rel_count);
+  hipLaunchKernelGGL(combine_release_kernel, dim3(1), dim3(kRelThreads), 0, stream, a->state.T_cap, a->m, a->tok,
+                     a->state.rflag, a->rel_list, a->rel_count);
   return launch_status();
 }
 
