@@ -224,6 +224,40 @@ class StepRunner:
         self.check(W + K - 1)
         return t0.elapsed_time(t1), sum(self.batch(s).n for s in range(W, W + K))
 
+    def timed_graph(self, W: int, K: int):
+        """The same K steps captured as one HIP graph (after W eager warm-up steps) and timed as
+        one replay; a first replay warms the graph up, then the state is reset and the remote
+        results delivered again, so the timed replay starts from the same state.  Returns (ms,
+        sum of pairs)."""
+        torch, M = self.torch, self.M
+        M.moe_state_reset(self.st.state, 0)
+        for s in range(W + K):
+            self.deliver(s)
+        for s in range(W):
+            self.step(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for s in range(W, W + K):
+                self.step(s)
+        g.replay()
+        torch.cuda.synchronize()
+        self.check(W + K - 1)
+        M.moe_state_reset(self.st.state, 0)
+        for s in range(W, W + K):
+            self.deliver(s)
+        torch.cuda.synchronize()
+        assert int(self.st.rel_count.item()) == 0
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        self.check(W + K - 1)
+        del g
+        return t0.elapsed_time(t1), sum(self.batch(s).n for s in range(W, W + K))
+
     def stages(self, ev: HipEvents, reps: int, flush: bool = False):
         """Per-stage HIP-event intervals of each batch of the cycle (state reset and delivery
         untimed before each step), plus the gate/up projection's own kernel time from the
@@ -365,6 +399,7 @@ def run_decode(args, W_steps: int, K_steps: int, cpu_seconds: float) -> dict:
     total_ms, pairs = run.timed(W_steps, K_steps)
     ev = HipEvents()
     stg = run.stages(ev, max(1, min(K_steps, 20)))[0]
+    g_ms, g_pairs = run.timed_graph(W_steps, K_steps)
     counts = run.st.counts.cpu().numpy()
     active = int((counts > 0).sum())
     H, I, n = b.H, wts.I, b.n
@@ -383,6 +418,8 @@ def run_decode(args, W_steps: int, K_steps: int, cpu_seconds: float) -> dict:
                      "traffic": stored_traffic("decode"), "algorithmic_bytes": gu_bytes,
                      "kernel_us": round(gu_ms * 1e3, 2)},
         "stages_us": {k: round(v * 1e3, 2) for k, v in stg.items()},
+        "graph": {"value": round(g_pairs / (g_ms * 1e-3), 1), "ms_per_step": round(g_ms / K_steps, 5),
+                  "note": "the same K steps captured as one HIP graph and replayed once"},
     }
     out["cpu_baseline"] = cpu_baseline_decode(b, wts, cpu_seconds) if cpu_seconds > 0 else None
     return out
@@ -405,6 +442,7 @@ def run_prefill(args) -> dict:
     total_ms, pairs = run.timed(W_steps, K_steps)
     ev = HipEvents()
     stg = run.stages(ev, max(1, min(K_steps // nw, 5)), flush=True)
+    g_ms, g_pairs = run.timed_graph(W_steps, K_steps)
     per_wave = []
     for w, b in enumerate(waves):
         m, n = stg[w], b.n
@@ -435,6 +473,8 @@ def run_prefill(args) -> dict:
                      "achieved": round(gu_tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gu_tf / BF16_PEAK_TFLOPS, 4), "traffic": stored_traffic("prefill"),
                      "algorithmic_bytes": gu_alg, "kernel_us": round(gu0_ms * 1e3, 2)},
+        "graph": {"value": round(g_pairs / (g_ms * 1e-3), 1), "ms_per_step": round(g_ms / K_steps, 5),
+                  "note": "the same K steps captured as one HIP graph and replayed once"},
         "waves": per_wave,
         "note": "value: K steps timed back to back (step s = wave s mod 4, its remote results delivered before "
                 "the timed region); waves[].us: per-stage medians of HIP-event intervals, each step alone; "
