@@ -27,6 +27,9 @@ Other workloads (--workload):
   tiny     8 experts, top-2, hidden 64, intermediate 128, fp32 (launch-latency bound)
   stream   36 layers, 72 micro-queues, 16 simulated sources with lognormal delays, under a
            queue pick --policy (most tokens first, first layer first, defragmenting score)
+  launch   the prefill waves arriving after seeded gaps (--gaps), launched by three policies:
+           each wave early, all merged, or at a minimum batch (--min-batch); per-token latency
+           and throughput from device-measured step times
 """
 from __future__ import annotations
 
@@ -543,6 +546,74 @@ def run_tiny(args) -> dict:
             "roofline": None, "cpu_baseline": None}
 
 
+def run_launch(args) -> dict:
+    """Prefill launch policies on the HIP path: seeded wave arrival times, the GPU running one
+    step at a time, each step's duration measured on the device for the batch the policy
+    formed (state reset and remote delivery untimed before it; median of 3 runs, cached per
+    batch)."""
+    import torch
+
+    import asynchronous_moe_expert_amd as M
+    import workloads as W
+    from workloads.device import batch_tensors, tensor, weight_tensors
+    from workloads.launch import run_policy, summarize, wave_arrivals
+
+    setup = W.c4_prefill_setup()
+    waves = [W.c4_wave(setup, w) for w in range(4)]
+    sizes = [b.n for b in waves]
+    E, H, I, K, P = setup.weights.E, setup.weights.H, setup.weights.I, waves[0].K, waves[0].P
+    st = M.ExpertStep(E, H, I, K, M.MOE_BF16, M.MOE_FP8_E4M3, sum(sizes), P)
+    wt = weight_tensors(setup.weights)
+    st.load_weights(wt["wg"], wt["wu"], wt["wd"], wt["s_gate"], wt["s_up"], wt["s_down"])
+    del wt
+    pool = tensor(setup.pool, "bf16")
+    ev = HipEvents()
+    stream = torch.cuda.current_stream().cuda_stream
+    e0, e1 = ev.create(), ev.create()
+    cache: dict = {}
+
+    def step_ms(combo) -> float:
+        if combo in cache:
+            return cache[combo]
+        b = W.merge_batches([waves[w] for w in combo])
+        d = batch_tensors(b)
+        d.pop("pool")
+        ts = []
+        for _ in range(3):
+            M.moe_state_reset(st.state, 0)
+            st.combine(d["r_rows"], d["r_idx"], d["r_tok"], d["r_kslot"], d["r_w"], d["r_gen"])
+            ev.record(e0, stream)
+            st.run(d["slot"], d["expert"], 0, pool, d["tok"], d["kslot"], d["w"], d["gen"], n=b.n)
+            ev.record(e1, stream)
+            torch.cuda.synchronize()
+            assert int(st.err.item()) == 0 and int(st.rel_count.item()) == b.n
+            ts.append(ev.ms(e0, e1))
+        cache[combo] = float(np.median(ts))
+        return cache[combo]
+
+    results = {}
+    for gap in args.gaps:
+        arr = wave_arrivals(20261202 + 4, 4, gap)
+        row = {"arrivals_ms": [round(float(a), 4) for a in arr]}
+        for policy, mb in [("early", 0), ("all", 0)] + [("minbatch", b) for b in args.min_batch]:
+            key = policy if policy != "minbatch" else f"minbatch_{mb}"
+            row[key] = summarize(run_policy(policy, arr, sizes, step_ms, mb), arr, sizes)
+        results[f"mean_gap_{gap}ms"] = row
+    mid = results[f"mean_gap_{args.gaps[len(args.gaps) // 2]}ms"][f"minbatch_{args.min_batch[-1]}"]
+    return {"metric": METRIC, "value": mid["pairs_per_gpu_s"], "unit": "expert tokens/s", "n_gpus": 1,
+            "steps": None, "warmup": 0, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16 activations, fp8 e4m3 weights, fp32 accumulate", "data": "synthetic (seeded)",
+            "config": {"workload": "prefill launch policies: the four prefill waves (6554/4915/3277/1638 "
+                                   "pairs) arriving after seeded Exponential gaps; launch each wave early, "
+                                   "merge all, or launch at a minimum batch", "mean_gaps_ms": args.gaps,
+                       "min_batch": args.min_batch},
+            "step_ms_by_batch": {"+".join(map(str, k)): round(v, 4) for k, v in sorted(cache.items())},
+            "policies": results,
+            "note": "value: pairs per GPU-second of the minimum-batch policy at the middle gap; pairs_per_s "
+                    "divides by the makespan from the first arrival; token latency = completion of the "
+                    "step carrying the token minus its wave's arrival"}
+
+
 def run_stream_bench(args) -> dict:
     """The multi-layer stream on the HIP path under one queue-pick policy.  Every expert
     batch and message delivery is one combine call whose release list feeds the queues
@@ -638,7 +709,12 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=4)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle CPU-baseline budget (0 = skip)")
-    ap.add_argument("--workload", choices=["prefill", "decode", "skewed", "tiny", "stream"], default="prefill")
+    ap.add_argument("--workload", choices=["prefill", "decode", "skewed", "tiny", "stream", "launch"],
+                    default="prefill")
+    ap.add_argument("--gaps", type=float, nargs="+", default=[0.1, 0.3, 1.0],
+                    help="launch: mean gaps (ms) between prefill waves")
+    ap.add_argument("--min-batch", type=int, nargs="+", default=[4096, 8192],
+                    help="launch: minimum-batch thresholds (pairs)")
     ap.add_argument("--policy", choices=["mtfs", "flfs", "defrag"], default="mtfs",
                     help="queue pick of the stream workload")
     ap.add_argument("--batches", type=int, default=1000, help="expert batches of the stream workload")
@@ -677,6 +753,8 @@ def main() -> int:
         out = run_skewed(args)
     elif args.workload == "tiny":
         out = run_tiny(args)
+    elif args.workload == "launch":
+        out = run_launch(args)
     else:
         out = run_stream_bench(args)
     print(json.dumps(out), flush=True)

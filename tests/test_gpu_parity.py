@@ -521,11 +521,13 @@ def test_c4_prefill_wave(c4_ref, wave):
     _check_c4_batch(W.c4_wave(s, wave), s.weights, y_all, TOL["fp8"])
 
 
-@pytest.mark.parametrize("waves", [(0, 1), (0, 1, 2, 3)], ids=["waves0-1", "waves0-3"])
+@pytest.mark.parametrize("waves", [(0, 1), (1, 2), (2, 3), (0, 1, 2), (1, 2, 3), (0, 1, 2, 3)],
+                         ids=lambda w: "waves" + "".join(map(str, w)))
 def test_c4_merged_waves(c4_ref, waves):
-    """Prefill waves merged into one ready batch (11469 and 16384 pairs: more row chunks per
-    expert and a longer index pass than any single wave): integer parts bit-exact, every
-    FFN row and every combined row against the oracle."""
+    """Prefill waves merged into one ready batch (every run of consecutive waves a launch policy
+    can form, up to all 16384 pairs: more row chunks per expert and a longer index pass than
+    any single wave): integer parts bit-exact, every FFN row and every combined row against
+    the oracle."""
     _say(f"C4 prefill fp8, merged waves {waves}")
     s, y_all = c4_ref
     _check_c4_batch(W.merge_batches([W.c4_wave(s, w) for w in waves]), s.weights, y_all, TOL["fp8"])
