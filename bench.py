@@ -436,6 +436,8 @@ def run_prefill(args) -> dict:
     setup = W.c4_prefill_setup()
     g = args.merge
     waves = [W.merge_batches([W.c4_wave(setup, w) for w in range(i, i + g)]) for i in range(0, 4, g)]
+    if args.waves is not None:  # a subset of the cycle (profiling one wave's kernels)
+        waves = [waves[i] for i in args.waves]
     nw = len(waves)
     K_steps, W_steps = args.steps, args.warmup
     run = StepRunner(waves, setup.weights, 1, 2, W_steps + K_steps)
@@ -724,6 +726,8 @@ def main() -> int:
                     help="decode/skewed: packed copies of the layer's weights the steps cycle through (so that no "
                          "step finds weights left in the caches by the one before, as in a model of many layers)")
     ap.add_argument("--no-decode", action="store_true", help="prefill: skip the decode sub-object")
+    ap.add_argument("--waves", type=int, nargs="+", default=None,
+                    help="prefill: run only these steps of the cycle (e.g. 0 for the 6554-pair wave)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="copy 256 MiB device to device once before the warm-up (reference dispatch for "
                          "rocprofv3 byte counters)")
