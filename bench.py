@@ -338,6 +338,31 @@ def cpu_baseline_decode(b, wts, seconds: float) -> dict:
                       f"8 experts, combine incl. the delivery of the remote results), {el:.1f} s"}
 
 
+def cpu_baseline_batches(batches, wts, seconds: float, what: str) -> dict:
+    """The oracle on whole steps of the given batches in order (assemble, FFN, combine with the
+    delivery of their remote results), until `seconds`."""
+    import oracle as O
+
+    t0 = time.perf_counter()
+    pairs = steps = 0
+    for b in batches:
+        a = O.assemble(b.slot, b.expert, b.expert_base, b.E_loc, b.P)
+        xb = O.decode(O.gather_rows(b.pool, b.slot, a["perm"], b.n), b.act)
+        y = O.expert_ffn(xb, a["offsets"], wts)
+        cs = O.CombineState(b.T, b.K)
+        if b.remote is not None:
+            r = b.remote
+            O.combine_release(cs, O.decode(r.rows, r.dtype), r.row_idx, r.tok, r.kslot, r.w, r.gen)
+        O.combine_release(cs, y, a["pos"], b.tok, b.kslot, b.w, b.gen)
+        pairs += b.n
+        steps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    return {"value": pairs / el, "unit": "expert tokens/s", "cores": blas_threads(), "kind": "oracle", **cpu_info(),
+            "sample": f"{steps} whole steps ({pairs} token-expert pairs) of the {what}, in order, {el:.1f} s"}
+
+
 def _oracle_subqueue(b, wts, experts):
     """One oracle pass over the pairs of `experts` in batch b: assemble, gather, FFN (each
     expert's weights decoded once), combine of the local and remote results; returns pairs."""
@@ -530,7 +555,9 @@ def run_skewed(args) -> dict:
             "config": {"workload": "skewed ragged routing: decode layer shape, Zipf(1.2) over 8 local experts, "
                                    "200 batches of U{8..512} pairs", "pairs": int(sizes.sum()),
                        "batch_pairs_mean": float(sizes.mean()), "weight_copies": len(run.w_copies)},
-            "roofline": None, "cpu_baseline": None}
+            "roofline": None,
+            "cpu_baseline": cpu_baseline_batches(batches, wts, args.cpu_seconds, "skewed batches")
+            if args.cpu_seconds > 0 else None}
 
 
 def run_tiny(args) -> dict:
@@ -545,7 +572,9 @@ def run_tiny(args) -> dict:
             "data": "synthetic (seeded)",
             "config": {"workload": "tiny single MoE layer: 8 experts, top-2, hidden 64, intermediate 128, fp32, "
                                    "64 pairs", "pairs": b.n},
-            "roofline": None, "cpu_baseline": None}
+            "roofline": None,
+            "cpu_baseline": cpu_baseline_batches([b] * 100000, wts, min(args.cpu_seconds, 5.0), "tiny layer")
+            if args.cpu_seconds > 0 else None}
 
 
 def run_launch(args) -> dict:
