@@ -168,28 +168,36 @@ __global__ __launch_bounds__(kAsmThreads) void assemble_index_kernel(
 // segment; it then scatters only its segment, stably, from running positions offsets[e] + (keys
 // of expert e before the segment).  No workgroup waits for another and no scratch is needed.
 // Workgroup 0 writes counts, offsets and the error bits (it sees every key).
-__global__ __launch_bounds__(1024) void assemble_index_multi_kernel(
+// Each key is counted by one LDS atomic into one of kIdxCopies counters of its expert (chosen by
+// lane): a Zipf-skewed queue puts a quarter of all pairs on one expert, and lanes of a wave that
+// add to one address are served one after another (one counter per expert, and a second atomic
+// for the keys before the segment, made this kernel 7.2 instead of 5.5 us at 6554 pairs and 11.9
+// instead of 7.4 us at 16384).
+constexpr int kIdxT = 1024;    // threads per workgroup = pairs per segment
+constexpr int kIdxCopies = 4;  // LDS counters per expert
+__global__ __launch_bounds__(kIdxT) void assemble_index_multi_kernel(
     int n, const int32_t* __restrict__ slot, const int32_t* __restrict__ expert, int base, int E_loc, int64_t P,
     int32_t* __restrict__ perm, int32_t* __restrict__ pos, int32_t* __restrict__ row_slot,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, uint32_t* __restrict__ err) {
-  constexpr int kT = 1024, kWaves = kT / kWave;
-  __shared__ int s_cnt[kMaxElocAsm];     // all keys, per expert
-  __shared__ int s_before[kMaxElocAsm];  // keys before this segment, per expert
+  constexpr int kT = kIdxT, kWaves = kT / kWave, kC = kIdxCopies, kCS = kC + 1;
+  __shared__ int s_bef[kMaxElocAsm * kCS];  // keys before this segment: expert e, copy c at e * kCS + c
+  __shared__ int s_aft[kMaxElocAsm * kCS];  // keys from this segment on
   __shared__ int s_run[kMaxElocAsm];
   __shared__ int s_wcnt[kWaves][kMaxElocAsm + 1];
   __shared__ int s_total;
   __shared__ unsigned s_err;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int seg0 = blockIdx.x * kT;
-  for (int e = tid; e < E_loc; e += kT) {
-    s_cnt[e] = 0;
-    s_before[e] = 0;
+  for (int x = tid; x < E_loc * kCS; x += kT) {
+    s_bef[x] = 0;
+    s_aft[x] = 0;
   }
+  for (int x = tid; x < kWaves * E_loc; x += kT) s_wcnt[x / E_loc][x % E_loc] = 0;
   if (tid == 0) s_err = 0u;
   __syncthreads();
-  // pass 1: every key (validated), counted in total and, before this segment, separately
-  // (kU chunks of ids are loaded before any of them is counted: one round trip per kU chunks)
+  // every key (validated) in batches of kU chunks whose ids are loaded before any is counted
   constexpr int kU = 8;
+  const int cp = lane % kC;
   unsigned myerr = 0u;
   int my_key = kMaxElocAsm, my_slot = 0;
   for (int i0 = 0; i0 < n; i0 += kU * kT) {
@@ -202,17 +210,14 @@ __global__ __launch_bounds__(1024) void assemble_index_multi_kernel(
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int i = i0 + u * kT + tid;
-      if (i < n) {
+      const int c0 = i0 + u * kT;  // first pair of this chunk (uniform)
+      if (c0 + tid < n) {
         const int e = ev[u] - base;
         bool ok = true;
         if (sv[u] < 0 || (int64_t)sv[u] >= P) { myerr |= MOE_ERR_SLOT_RANGE; ok = false; }
-        if (e < 0 || e >= E_loc) { myerr |= MOE_ERR_EXPERT_NONLOCAL; ok = false; }
-        if (ok) {
-          atomicAdd(&s_cnt[e], 1);
-          if (i < seg0) atomicAdd(&s_before[e], 1);
-        }
-        if (i == seg0 + tid) {  // this thread's own pair of the segment
+        if ((unsigned)e >= (unsigned)E_loc) { myerr |= MOE_ERR_EXPERT_NONLOCAL; ok = false; }
+        if (ok) atomicAdd(&(c0 < seg0 ? s_bef : s_aft)[e * kCS + cp], 1);
+        if (c0 == seg0) {  // this thread's own pair of the segment
           my_key = ok ? e : kMaxElocAsm;
           my_slot = sv[u];
         }
@@ -221,13 +226,22 @@ __global__ __launch_bounds__(1024) void assemble_index_multi_kernel(
   }
   if (blockIdx.x == 0 && myerr) atomicOr(&s_err, myerr);
   __syncthreads();
-  // exclusive scan of the counts (wave 0; 4 experts per lane covers E_loc <= 256)
+  // wave 0: exclusive scan of the counts (4 experts per lane covers E_loc <= 256)
   if (wv == 0) {
-    int v[4], sum = 0;
+    int v[4], bf[4], sum = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int e = lane * 4 + k;
-      v[k] = e < E_loc ? s_cnt[e] : 0;
+      v[k] = 0;
+      bf[k] = 0;
+      if (e < E_loc) {
+#pragma unroll
+        for (int c = 0; c < kC; ++c) {
+          bf[k] += s_bef[e * kCS + c];
+          v[k] += s_aft[e * kCS + c];
+        }
+        v[k] += bf[k];
+      }
       sum += v[k];
     }
     int incl = sum;
@@ -245,7 +259,7 @@ __global__ __launch_bounds__(1024) void assemble_index_multi_kernel(
           counts[e] = v[k];
           offsets[e] = run;
         }
-        s_run[e] = run + s_before[e];  // this segment's first row of expert e
+        s_run[e] = run + bf[k];  // this segment's first row of expert e
       }
       run += v[k];
     }
@@ -254,12 +268,10 @@ __global__ __launch_bounds__(1024) void assemble_index_multi_kernel(
       s_total = incl;
     }
   }
-  __syncthreads();
-  // pass 2: stable scatter of this segment (one pair per thread): rank among equal keys of
-  // lower lanes from a 9-bit ballot match, plus the counts of the lower waves
+  // meanwhile the other waves: this segment's stable order, i.e. each pair's rank among equal
+  // keys of lower lanes from a 9-bit ballot match, and each wave's count per expert (rejected
+  // pairs and lanes past n carry kMaxElocAsm)
   const int i = seg0 + tid;
-  for (int x = tid; x < kWaves * E_loc; x += kT) s_wcnt[x / E_loc][x % E_loc] = 0;
-  __syncthreads();
   uint64_t peers = ~0ull;
 #pragma unroll
   for (int b = 0; b < 9; ++b) {
@@ -270,7 +282,7 @@ __global__ __launch_bounds__(1024) void assemble_index_multi_kernel(
   const int rank = __popcll(peers & ((1ull << lane) - 1ull));
   if (my_key < kMaxElocAsm && rank == 0) s_wcnt[wv][my_key] = __popcll(peers);
   __syncthreads();
-  if (tid < E_loc) {
+  if (tid < E_loc) {  // each expert's first row for each wave of this segment
     int run = s_run[tid];
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
@@ -338,7 +350,7 @@ extern "C" int moe_assemble(const moe_assemble_args* a, hipStream_t stream) {
     hipLaunchKernelGGL(assemble_index_kernel<1024>, dim3(1), dim3(1024), 0, stream, a->n, a->slot, a->expert,
                        a->expert_base, a->E_loc, a->P, a->perm, a->pos, a->row_slot, a->counts, a->offsets, a->err);
   else
-    hipLaunchKernelGGL(assemble_index_multi_kernel, dim3((unsigned)((a->n + 1023) / 1024)), dim3(1024), 0, stream,
+    hipLaunchKernelGGL(assemble_index_multi_kernel, dim3((unsigned)((a->n + kIdxT - 1) / kIdxT)), dim3(kIdxT), 0, stream,
                        a->n, a->slot, a->expert, a->expert_base, a->E_loc, a->P, a->perm, a->pos, a->row_slot,
                        a->counts, a->offsets, a->err);
   if (a->n == 0 || !a->xb) return launch_status();  // no xb: the FFN gathers on load
