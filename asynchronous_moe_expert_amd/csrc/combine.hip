@@ -12,10 +12,12 @@
 // so there are no device-scope fences (on this GPU a fence writes back and invalidates the
 // XCD's whole L2) and no float atomics:
 //   1. link: one thread per arrival.  Index/generation checks, then a lock-free push onto
-//      the token's arrival list (head[t], next[i]).
-//   2. merge: one workgroup per arrival; the workgroup holding the list head owns the token
-//      for the call.  It sorts the token's arrivals by index, accepts top-k positions in
-//      that order (a position already held is a duplicate), and computes
+//      the token's arrival list (head[t], next[i]); it also copies the token's mask (the
+//      held positions before this call) next to the arrival.
+//   2. merge: one workgroup per arrival; the workgroup of the token's first pushed arrival
+//      (the list's tail) owns the token for the call.  It sorts the token's arrivals by
+//      index, accepts top-k positions in that order (a position already held is a
+//      duplicate), and computes
 //      acc + sum w_a * row_a in fp32 in the same order (bit-reproducible).  If the token is
 //      complete it writes out[t] = RNE(sum), clears mask[t], advances tgen[t] and sets its
 //      release flag; otherwise it stores the partial sum back into acc[t].
@@ -86,6 +88,7 @@ constexpr int kCmbThreads = 384;
 constexpr int kMergeThreads = MOE_MERGE_THREADS;  // merge workgroup (one per arrival)
 constexpr int kMaxChain = 64;  // arrivals of one token handled per pass of the merge
 constexpr int kMergeVec = 4;   // 8-element vectors per thread loaded in one batch (rows up to 8192 wide)
+constexpr int kRowBatch = 4;   // result rows of one token loaded before they are summed (list and plan paths)
 
 // Kernel 1: one thread per arrival.  Range and generation checks, then a push onto the
 // token's arrival list (head[t] = newest arrival, next[i] = the one pushed before it).
@@ -94,9 +97,10 @@ __global__ __launch_bounds__(256) void combine_link_kernel(int m, int K, int64_t
                                                            const int32_t* __restrict__ tok,
                                                            const int32_t* __restrict__ kslot,
                                                            const uint32_t* __restrict__ gen,
-                                                           const uint32_t* __restrict__ tgen, int T_cap,
+                                                           const uint32_t* __restrict__ tgen,
+                                                           const uint32_t* __restrict__ mask, int T_cap,
                                                            int32_t* __restrict__ head, int32_t* __restrict__ next,
-                                                           uint32_t* __restrict__ err) {
+                                                           uint32_t* __restrict__ mpre, uint32_t* __restrict__ err) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= m) return;
   const int t = tok[i], j = kslot[i];
@@ -105,123 +109,141 @@ __global__ __launch_bounds__(256) void combine_link_kernel(int m, int K, int64_t
   if (t < 0 || t >= T_cap) flag |= MOE_ERR_TOKEN_RANGE;
   if (j < 0 || j >= K) flag |= MOE_ERR_KSLOT_RANGE;
   if (r < 0 || r >= n_rows) flag |= MOE_ERR_ROW_RANGE;
-  if (!flag && gen[i] != tgen[t]) flag |= MOE_ERR_STALE_GEN;
+  uint32_t m_t = 0u;
+  if (!flag) {
+    m_t = mask[t];  // (fetched with the generation; no kernel of this call has changed it yet)
+    if (gen[i] != tgen[t]) flag |= MOE_ERR_STALE_GEN;
+  }
   if (flag) {
     atomicOr(err, flag);
     next[i] = -2;  // not linked
     return;
   }
+  mpre[i] = m_t;
   next[i] = atomicExch(&head[t], i);
 }
 
-// Kernel 2: one workgroup per arrival; the workgroup whose arrival heads its token's list
-// owns the token for this call (exactly one per touched token), all others exit.  The
-// owner sorts the token's arrivals by index, accepts top-k positions in that order (a
-// repeat of a held position is a duplicate), and sums acc + w_a * row_a in the same
-// order in fp32, so results do not depend on scheduling.  acc[t] is only read while the
-// token holds earlier results (mask != 0): a fresh token starts from zero.
-template <typename TR, typename TO>
+// Kernel 2: one workgroup per arrival; the workgroup of the token's first pushed arrival (the
+// one whose list link is -1: exactly one per touched token) owns the token for this call, all
+// others exit after their first round trip.  The owner sorts the token's arrivals by index,
+// accepts top-k positions in that order (a repeat of a held position is a duplicate), and
+// sums acc + w_a * row_a in the same order in fp32, so results do not depend on scheduling.
+// acc[t] is only read while the token holds earlier results (mask != 0): a fresh token starts
+// from zero.  The owner loads the list head together with its own result row and the held
+// sum, so a token's only arrival of the call (every token of a prefill wave) costs two
+// dependent round trips (its metadata, then head and rows) instead of three.
+// Empty asm statements that read values: every load those values come from is then issued, and
+// waited for, at that point.  Without them the compiler sinks loads past the branches that
+// follow (each value is used on one side only), and the merge's one round trip for an
+// arrival's metadata became four dependent ones, its rows one per 256 vectors.
+template <int VPT>
+__device__ __forceinline__ void hold_rows(const float (&s)[VPT][8], const float (&x)[VPT][8], int h) {
+  if constexpr (VPT == 1) {
+    asm volatile("" ::"v"(s[0][0]), "v"(s[0][4]), "v"(x[0][0]), "s"(h));
+  } else if constexpr (VPT == 2) {
+    asm volatile("" ::"v"(s[0][0]), "v"(s[0][4]), "v"(x[0][0]), "v"(s[1][0]), "v"(s[1][4]), "v"(x[1][0]), "s"(h));
+  } else {
+    static_assert(VPT == 4, "1, 2 or 4 vectors per thread");
+    asm volatile("" ::"v"(s[0][0]), "v"(s[0][4]), "v"(x[0][0]), "v"(s[1][0]), "v"(s[1][4]), "v"(x[1][0]),
+                 "v"(s[2][0]), "v"(s[2][4]), "v"(x[2][0]), "v"(s[3][0]), "v"(s[3][4]), "v"(x[3][0]), "s"(h));
+  }
+}
+
+// VPT: 8-element vectors per thread of a row when the whole row fits one batch of loads (1, 2
+// or 4: the host picks the smallest that covers H / 8 vectors), else 0.  Vector indices past the
+// row are clamped to its last vector, so that every load of a batch is issued, unconditionally,
+// before the first is used; their values are never stored.
+template <typename TR, typename TO, int VPT>
 __global__ __launch_bounds__(kMergeThreads) void combine_merge_kernel(
     int K, int H, const TR* __restrict__ rows, int64_t row_pitch, const int32_t* __restrict__ row_idx,
     const int32_t* __restrict__ tok, const int32_t* __restrict__ kslot, const float* __restrict__ wgt,
     float* __restrict__ acc, uint32_t* __restrict__ mask, uint32_t* __restrict__ tgen,
     uint8_t* __restrict__ rflag, int32_t* __restrict__ head, const int32_t* __restrict__ next,
-    TO* __restrict__ out, int64_t out_pitch, uint32_t* __restrict__ err) {
+    const uint32_t* __restrict__ mpre, TO* __restrict__ out, int64_t out_pitch, uint32_t* __restrict__ err) {
   __shared__ int s_list[kMaxChain];
   __shared__ int s_buf[kMaxChain];
   __shared__ int s_n, s_more, s_first;
-  __shared__ uint32_t s_mask0, s_mask1;
+  __shared__ uint32_t s_mask1;
   const int tid = threadIdx.x;
   const int i = blockIdx.x;
   // everything indexed by the arrival in one round trip (all in range: i < m)
-  const int nx = next[i];
+  int nx = next[i];
   const int t = tok[i];
   const int j_i = kslot[i];
   const float w_i = wgt[i];
-  const int64_t r_i = row_idx[i];
-  if (nx == -2) return;       // rejected by the range/generation checks
-  // the list head and the token's mask in one round trip (the mask is used only by the owner)
-  const int h_t = head[t];
-  const uint32_t m_t = mask[t];
-  if (h_t != i) return;   // another arrival owns this token
+  const int r32 = row_idx[i];
+  const uint32_t m_t = mpre[i];
+  // (the kernel arguments the owner needs next are fetched in the same round trip; nx is an
+  // in/out operand so that the test below cannot be scheduled between these loads)
+  asm volatile("" : "+s"(nx) : "s"(t), "s"(j_i), "s"(w_i), "s"(r32), "s"(m_t), "s"(rows), "s"(acc), "s"(head),
+               "s"(out), "s"(row_pitch), "s"(out_pitch), "s"(H), "s"(K));
+  const int64_t r_i = r32;
+  if (nx != -1) return;  // rejected by the range/generation checks (-2), or not the tail
   const uint32_t full = K >= 32 ? 0xffffffffu : ((1u << K) - 1u);
   float* a = acc + (int64_t)t * H;
   TO* o = out + (int64_t)t * out_pitch;
   const int nv = H >> 3;
-  if (nx == -1) {
-    // the token's only arrival of this call (every token of a prefill wave): no list to
-    // walk or sort, the same accept rule and the same fp32 operations as below
-    const uint32_t m_old = m_t, bit = 1u << j_i;
-    const bool dup = (m_old & bit) != 0u;
-    const uint32_t m_new = m_old | bit;
-    const bool complete = !dup && m_new == full;
-    if (!dup) {
-      const bool started = m_old != 0u;
-      const TR* x_row = rows + r_i * row_pitch;
-      if (nv <= kMergeVec * kMergeThreads) {
-        // rows of up to kMergeVec vectors per thread: every load is issued before the first
-        // sum, so one round trip covers the held partial sum and the result row
-        float sum[kMergeVec][8], x[kMergeVec][8];
+  const bool started = m_t != 0u;  // acc[t] holds earlier results
+  if constexpr (VPT > 0) {
+    // the held sum and this arrival's row are loaded with the list head, before it is known
+    // whether other arrivals joined the list
+    const TR* x_row = rows + r_i * row_pitch;
+    int vq[VPT];
 #pragma unroll
-        for (int q = 0; q < kMergeVec; ++q) {
-          const int v = tid + q * kMergeThreads;
-          if (v < nv) {
-            if (started) {
-              RowIO<float>::load8(a + v * 8, sum[q]);
-            } else {
+    for (int q = 0; q < VPT; ++q) vq[q] = min(tid + q * kMergeThreads, nv - 1);
+    float sum[VPT][8], x[VPT][8];
+    if (started) {
 #pragma unroll
-              for (int k = 0; k < 8; ++k) sum[q][k] = 0.f;
-            }
-            RowIO<TR>::load8(x_row + v * 8, x[q]);
-          }
-        }
+      for (int q = 0; q < VPT; ++q) RowIO<float>::load8(a + vq[q] * 8, sum[q]);
+    } else {
 #pragma unroll
-        for (int q = 0; q < kMergeVec; ++q) {
-          const int v = tid + q * kMergeThreads;
-          if (v < nv) {
+      for (int q = 0; q < VPT; ++q)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sum[q][k] = 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < VPT; ++q) RowIO<TR>::load8(x_row + vq[q] * 8, x[q]);
+    const int h_t = head[t];
+    hold_rows<VPT>(sum, x, h_t);
+    if (h_t == i) {
+      // the token's only arrival of this call: no list to walk or sort, the same accept rule
+      // and the same fp32 operations as below
+      const uint32_t bit = 1u << j_i;
+      const bool dup = (m_t & bit) != 0u;
+      const uint32_t m_new = m_t | bit;
+      const bool complete = !dup && m_new == full;
+      if (!dup) {
+#pragma unroll
+        for (int q = 0; q < VPT; ++q) {
+          if (tid + q * kMergeThreads < nv) {
 #pragma unroll
             for (int k = 0; k < 8; ++k) sum[q][k] = fmaf(w_i, x[q][k], sum[q][k]);
-            if (complete) RowIO<TO>::store8(o + v * 8, sum[q]);
-            else RowIO<float>::store8(a + v * 8, sum[q]);
+            if (complete) RowIO<TO>::store8(o + vq[q] * 8, sum[q]);
+            else RowIO<float>::store8(a + vq[q] * 8, sum[q]);
           }
         }
-      } else {
-        for (int v = tid; v < nv; v += kMergeThreads) {
-          float sum[8], x[8];
-          if (started) {
-            RowIO<float>::load8(a + v * 8, sum);
-          } else {
-#pragma unroll
-            for (int k = 0; k < 8; ++k) sum[k] = 0.f;
-          }
-          RowIO<TR>::load8(x_row + v * 8, x);
-#pragma unroll
-          for (int k = 0; k < 8; ++k) sum[k] = fmaf(w_i, x[k], sum[k]);
-          if (complete) RowIO<TO>::store8(o + v * 8, sum);
-          else RowIO<float>::store8(a + v * 8, sum);
+      }
+      // every wave has read head[t] (its branch above needed the value) before thread 0 resets
+      // it: a wave that read the reset value would take the list path below alone
+      __syncthreads();
+      if (tid == 0) {
+        if (dup) atomicOr(err, MOE_ERR_DUPLICATE);
+        head[t] = -1;
+        if (complete) {
+          mask[t] = 0u;
+          tgen[t] = tgen[t] + 1u;
+          rflag[t] = 1;
+        } else {
+          mask[t] = m_new;
         }
       }
+      return;
     }
-    if (tid == 0) {
-      if (dup) atomicOr(err, MOE_ERR_DUPLICATE);
-      head[t] = -1;
-      if (complete) {
-        mask[t] = 0u;
-        tgen[t] = tgen[t] + 1u;
-        rflag[t] = 1;
-      } else {
-        mask[t] = m_new;
-      }
-    }
-    return;
   }
-  const int cursor = i;  // list head
+  const int cursor = head[t];  // list head (the newest arrival)
   int lo = -1;      // arrivals with index <= lo are already merged
   bool have = false;  // acc values of this call live in `a` (not yet in registers)
-  if (tid == 0) s_mask0 = m_t;
-  __syncthreads();
-  uint32_t m_now = s_mask0;
-  bool started = m_now != 0u;  // acc[t] holds earlier results
+  uint32_t m_now = m_t;
   while (true) {
     // collect the next batch of up to kMaxChain arrivals with the smallest indices > lo
     if (tid == 0) {
@@ -282,13 +304,23 @@ __global__ __launch_bounds__(kMergeThreads) void combine_merge_kernel(
 #pragma unroll
         for (int k = 0; k < 8; ++k) sum[k] = 0.f;
       }
-      for (int q = 0; q < na; ++q) {
-        const int arr = s_list[q];
-        const float w = wgt[arr];
-        float x[8];
-        RowIO<TR>::load8(rows + (int64_t)row_idx[arr] * row_pitch + v * 8, x);
+      // kRowBatch rows in flight at a time (the batch's last slots repeat its last row and are
+      // not added), summed in arrival-index order
+      for (int q0 = 0; q0 < na; q0 += kRowBatch) {
+        float x[kRowBatch][8], w[kRowBatch];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) sum[k] = fmaf(w, x[k], sum[k]);
+        for (int u = 0; u < kRowBatch; ++u) {
+          const int arr = s_list[min(q0 + u, na - 1)];
+          w[u] = wgt[arr];
+          RowIO<TR>::load8(rows + (int64_t)row_idx[arr] * row_pitch + v * 8, x[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < kRowBatch; ++u) {
+          if (q0 + u < na) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) sum[k] = fmaf(w[u], x[u][k], sum[k]);
+          }
+        }
       }
       if (complete) RowIO<TO>::store8(o + v * 8, sum);
       else RowIO<float>::store8(a + v * 8, sum);
@@ -445,12 +477,20 @@ __global__ __launch_bounds__(kCmbThreads) void combine_apply_kernel(int H, const
 #pragma unroll
       for (int k = 0; k < 8; ++k) sum[k] = 0.f;
     }
-    for (int q = 0; q < na; ++q) {
-      float x[8];
-      RowIO<TR>::load8(rows + s_row[q] * row_pitch + v * 8, x);
-      const float w = s_w[q];
+    // kRowBatch rows in flight at a time (the batch's last slots repeat its last row and are not
+    // added), summed in arrival-index order
+    for (int q0 = 0; q0 < na; q0 += kRowBatch) {
+      float x[kRowBatch][8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) sum[k] = fmaf(w, x[k], sum[k]);
+      for (int u = 0; u < kRowBatch; ++u) RowIO<TR>::load8(rows + s_row[min(q0 + u, na - 1)] * row_pitch + v * 8, x[u]);
+#pragma unroll
+      for (int u = 0; u < kRowBatch; ++u) {
+        if (q0 + u < na) {
+          const float w = s_w[q0 + u];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) sum[k] = fmaf(w, x[u][k], sum[k]);
+        }
+      }
     }
     if (complete) RowIO<TO>::store8(o + v * 8, sum);
     else RowIO<float>::store8(at + v * 8, sum);
@@ -466,12 +506,22 @@ static void launch_apply(const moe_combine_args* a, hipStream_t stream) {
                      (TO*)a->out, a->out_pitch);
 }
 
+template <typename TR, typename TO, int VPT>
+static void launch_merge_vpt(const moe_combine_args* a, hipStream_t stream) {
+  const moe_combine_state& s = a->state;
+  hipLaunchKernelGGL((combine_merge_kernel<TR, TO, VPT>), dim3((unsigned)a->m), dim3(kMergeThreads), 0, stream, a->K,
+                     s.H, (const TR*)a->rows, a->row_pitch, a->row_idx, a->tok, a->kslot, a->w, s.acc, s.mask, s.tgen,
+                     s.rflag, s.head, (const int32_t*)a->workspace, (const uint32_t*)a->workspace + a->m, (TO*)a->out,
+                     a->out_pitch, a->err);
+}
+
 template <typename TR, typename TO>
 static void launch_merge(const moe_combine_args* a, hipStream_t stream) {
-  const moe_combine_state& s = a->state;
-  hipLaunchKernelGGL((combine_merge_kernel<TR, TO>), dim3((unsigned)a->m), dim3(kMergeThreads), 0, stream, a->K, s.H,
-                     (const TR*)a->rows, a->row_pitch, a->row_idx, a->tok, a->kslot, a->w, s.acc, s.mask, s.tgen,
-                     s.rflag, s.head, (const int32_t*)a->workspace, (TO*)a->out, a->out_pitch, a->err);
+  const int vpt = (a->state.H / 8 + kMergeThreads - 1) / kMergeThreads;
+  if (vpt <= 1) launch_merge_vpt<TR, TO, 1>(a, stream);
+  else if (vpt <= 2) launch_merge_vpt<TR, TO, 2>(a, stream);
+  else if (vpt <= kMergeVec) launch_merge_vpt<TR, TO, kMergeVec>(a, stream);
+  else launch_merge_vpt<TR, TO, 0>(a, stream);
 }
 
 static int check_state(const moe_combine_state* s) {
@@ -487,10 +537,11 @@ static int check_state(const moe_combine_state* s) {
 using namespace moe;
 
 extern "C" size_t moe_combine_workspace_size(int32_t m_max) {
-  // the larger of the two paths' needs: next[m] (list path) and the plan records
+  // the larger of the two paths' needs: next[m] and the tokens' masks before the call (list
+  // path), and the plan records
   if (m_max <= 0) return 16;
   const size_t plan = (size_t)plan_list_offset(m_max) * 4 + (size_t)m_max * 8;
-  return (std::max(plan, (size_t)m_max * 4) + 15) / 16 * 16;
+  return (std::max(plan, (size_t)m_max * 8) + 15) / 16 * 16;
 }
 
 extern "C" int moe_state_reset(const moe_combine_state* st, uint32_t gen0, hipStream_t stream) {
@@ -573,8 +624,8 @@ extern "C" int moe_combine_plan(const moe_combine_args* a, hipStream_t stream) {
       hipLaunchKernelGGL(combine_plan_kernel<kPlanThreads>, dim3(1), dim3(kPlanThreads), 0, stream, job);
   } else if (a->m > 0) {
     hipLaunchKernelGGL(combine_link_kernel, dim3((unsigned)((a->m + 255) / 256)), dim3(256), 0, stream, a->m, a->K,
-                       a->n_rows, a->row_idx, a->tok, a->kslot, a->gen, s.tgen, s.T_cap, s.head,
-                       (int32_t*)a->workspace, a->err);
+                       a->n_rows, a->row_idx, a->tok, a->kslot, a->gen, s.tgen, s.mask, s.T_cap, s.head,
+                       (int32_t*)a->workspace, (uint32_t*)a->workspace + a->m, a->err);
   }
   return launch_status();
 }
