@@ -265,20 +265,24 @@ class StepRunner:
         """Per-stage HIP-event intervals of each batch of the cycle (state reset and delivery
         untimed before each step), plus the gate/up projection's own kernel time from the
         events its dispatch records, in a pass of its own so that they stay out of the stage
-        intervals; with flush, the combine is also timed after a 512 MiB write that evicts
-        the last-level cache (cold)."""
+        intervals; with flush, the combine is also timed cold: after a 512 MiB write and two
+        read passes over it, which leave the 256 MB last-level cache full of clean lines
+        (combine_cold), and after the write alone (combine_cold_dirty: then every miss of the
+        combine first writes back a dirty line of that buffer, which on its own took the same
+        traffic pattern from ~43 to ~75 us in a probe)."""
         torch, M, st = self.torch, self.M, self.st
         nb = len(self.batches)
         names = ["assemble", "gate_up", "down", "combine"]
         evs = [ev.create() for _ in range(5)]
         gs, ge, c0, c1 = ev.create(), ev.create(), ev.create(), ev.create()
         scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda") if flush else None
-        times = {w: {k: [] for k in names + ["gate_up_kernel", "combine_cold"]} for w in range(nb)}
+        times = {w: {k: [] for k in names + ["gate_up_kernel", "combine_cold", "combine_cold_dirty"]}
+                 for w in range(nb)}
         for _ in range(reps):
             for w in range(nb):
                 b, d = self.batches[w], self.d[w]
                 self.st.w_gu, self.st.w_d = self.w_copies[w % len(self.w_copies)]
-                for p in range(2):
+                for p in range(3 if flush else 2):
                     M.moe_state_reset(st.state, 0)
                     self.deliver(w)
                     tok = self.tok[w]
@@ -294,9 +298,12 @@ class StepRunner:
                     else:
                         st.assemble(d["slot"], d["expert"], self.base, self.pool, n=b.n)
                         plan = st.local_combine_args(tok, d["kslot"], d["w"], d["gen"], b.n)
-                        st.ffn(b.n, plan=plan, ev_gu=(gs, ge))
+                        st.ffn(b.n, plan=plan, ev_gu=(gs, ge) if p == 1 else None)
                         if scratch is not None:
                             scratch.fill_(1.0)
+                            if p == 2:
+                                for _ in range(2):
+                                    scratch.sum()
                         ev.record(c0, self.stream)
                         M.combine_call(plan, "apply")
                         ev.record(c1, self.stream)
@@ -305,10 +312,12 @@ class StepRunner:
                     if p == 0:
                         for k, nm in enumerate(names):
                             times[w][nm].append(ev.ms(evs[k], evs[k + 1]))
-                    else:
+                    elif p == 1:
                         times[w]["gate_up_kernel"].append(ev.ms(gs, ge))
                         if scratch is not None:
-                            times[w]["combine_cold"].append(ev.ms(c0, c1))
+                            times[w]["combine_cold_dirty"].append(ev.ms(c0, c1))
+                    else:
+                        times[w]["combine_cold"].append(ev.ms(c0, c1))
         return {w: {k: float(np.median(v)) for k, v in t.items() if v} for w, t in times.items()}
 
 
@@ -483,7 +492,9 @@ def run_prefill(args) -> dict:
                          "gate_up_mfma_frac": round(4.0 * n * H * I / (m["gate_up_kernel"] * 1e-3) / 1e12
                                                     / BF16_PEAK_TFLOPS, 4),
                          "combine_hbm_frac": round(c_bytes / (m["combine"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                         "combine_cold_hbm_frac": round(c_bytes / (m["combine_cold"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+                         "combine_cold_hbm_frac": round(c_bytes / (m["combine_cold"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "combine_cold_dirty_hbm_frac": round(c_bytes / (m["combine_cold_dirty"] * 1e-3) / 1e9
+                                                              / HBM_PEAK_GBS, 4)})
     b0 = waves[0]
     gu0_ms = stg[0]["gate_up_kernel"]
     gu_tf = 4.0 * b0.n * H * I / (gu0_ms * 1e-3) / 1e12
@@ -509,7 +520,9 @@ def run_prefill(args) -> dict:
         "note": "value: K steps timed back to back (step s = wave s mod 4, its remote results delivered before "
                 "the timed region); waves[].us: per-stage medians of HIP-event intervals, each step alone; "
                 "gate_up_kernel and roofline.kernel_us: the gate/up projection alone, from events its dispatch "
-                "records; combine_cold: the combine after a 512 MiB cache-evicting write",
+                "records; combine_cold: the combine after a 512 MiB write and two read passes over it (caches "
+                "hold clean lines of another buffer); combine_cold_dirty: after the write alone (every miss then "
+                "also writes back a dirty line)",
     }
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline_prefill(W.c4_wave(setup, 0), setup.weights, args.cpu_seconds,

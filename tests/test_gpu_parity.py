@@ -724,11 +724,13 @@ def _gemm_split_plan(counts, Nw, Kd, G_res):
 
 
 GEMM256_CASES = [
-    # (E, H, I, counts): 256-row units over every tile-count variant (a last chunk of 1..64,
-    # 65..128, 129..192 and 193..255 rows), an empty expert, full chunks, a partial last column
-    # block (Nw = 640: two of four waves active), contractions of 10 and 5 k-steps (not a
-    # multiple of the ring depth) ...
+    # (E, H, I, counts): 256-row units over every tile-count variant (last chunks of 88, 40,
+    # 150, 230 and 1 rows: 3, 2, 5, 8 and 1 tiles of 32 rows), an empty expert, full chunks, a
+    # partial last column block (Nw = 640: two of four waves active), contractions of 10 and 5
+    # k-steps (not a multiple of the ring depth) ...
     (6, 640, 320, [600, 0, 40, 150, 230, 513]),
+    # ... the other tile counts (4, 6, 7: chunks of 100, 170 and 200 rows) ...
+    (3, 512, 256, [100, 170, 200]),
     # ... and more units than workgroups (18 chunks x 16 gate/up column blocks: two rounds)
     (2, 512, 2048, [3000, 1500]),
 ]
