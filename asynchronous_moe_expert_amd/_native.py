@@ -43,7 +43,7 @@ class FfnArgs(C.Structure):
                 ("xb", _p), ("offsets", _p), ("w_gu", _p), ("w_d", _p), ("s_gate", _p), ("s_up", _p),
                 ("s_down", _p), ("y", _p), ("workspace", _p), ("workspace_bytes", C.c_size_t), ("ev_mid", _p),
                 ("perm", _p), ("slot", _p), ("pool", _p), ("P", _i64), ("pool_pitch", _i64), ("row_slot", _p),
-                ("plan", _p), ("ev_gu_start", _p), ("ev_gu_stop", _p)]
+                ("plan", _p), ("ev_gu_start", _p), ("ev_gu_stop", _p), ("index", _p)]
 
 
 class StateC(C.Structure):
@@ -150,14 +150,22 @@ def moe_ffn_workspace_size(n_max: int, E_loc: int, H: int, I: int, act_dtype: in
     return load().moe_ffn_workspace_size(n_max, E_loc, H, I, act_dtype)
 
 
+def assemble_args(slot, expert, expert_base: int, E_loc: int, pool, perm, pos, counts, offsets, xb, err,
+                  n: int | None = None, row_slot=None, H: int | None = None) -> AssembleArgs:
+    """The moe_assemble argument struct (for moe_assemble, or as moe_ffn_args.index)."""
+    if H is None:
+        H = pool.shape[1] if xb is None else xb.shape[1]
+    return AssembleArgs(int(slot.numel() if n is None else n), _ptr(slot), _ptr(expert), expert_base, E_loc,
+                        _ptr(pool), pool.shape[0], pool.stride(0), H, dtype_code(pool), _ptr(perm),
+                        _ptr(pos), _ptr(counts), _ptr(offsets), _ptr(xb), _ptr(err), _ptr(row_slot))
+
+
 def moe_assemble(slot, expert, expert_base: int, E_loc: int, pool, perm, pos, counts, offsets, xb, err,
                  n: int | None = None, stream=None, row_slot=None) -> None:
     """pool: [P][pitch] (f32 or bf16); xb: [>= n][H] of the same dtype (or None);
     row_slot: optional [>= n] int32 output, the pool slot of each batch row."""
-    H = pool.shape[1] if xb is None else xb.shape[1]
-    a = AssembleArgs(int(slot.numel() if n is None else n), _ptr(slot), _ptr(expert), expert_base, E_loc,
-                     _ptr(pool), pool.shape[0], pool.stride(0), H, dtype_code(pool), _ptr(perm),
-                     _ptr(pos), _ptr(counts), _ptr(offsets), _ptr(xb), _ptr(err), _ptr(row_slot))
+    a = assemble_args(slot, expert, expert_base, E_loc, pool, perm, pos, counts, offsets, xb, err, n=n,
+                      row_slot=row_slot)
     _check(load().moe_assemble(C.byref(a), _stream(stream)), "moe_assemble")
 
 
@@ -170,12 +178,14 @@ def moe_pack_ffn_weights(wg, wu, wd, w_gu, w_d, w_dtype: int, stream=None) -> No
 def moe_expert_ffn_grouped(n: int, E_loc: int, H: int, I: int, act_dtype: int, w_dtype: int, xb, offsets, w_gu,
                            w_d, y, workspace, s_gate=None, s_up=None, s_down=None, ev_mid: int | None = None,
                            stream=None, gather=None, plan: "CombineArgs | None" = None,
-                           ev_gu: tuple[int, int] | None = None) -> None:
+                           ev_gu: tuple[int, int] | None = None, index: "AssembleArgs | None" = None) -> None:
     """gather=(perm, slot, pool) or (perm, slot, pool, row_slot): read batch rows from the pool
     (gather-on-load; with row_slot, pool row row_slot[r] and perm/slot unused); xb may be None.
     plan: the arguments (combine_args) of a moe_combine_plan call that this call enqueues as
     well, inside the gate/up launch where it fits.  ev_gu: (start, stop) hipEvent_t handles
-    that the weight-streaming gate/up kernel records around itself."""
+    that the weight-streaming gate/up kernel records around itself.  index: the arguments
+    (assemble_args, xb None) of a moe_assemble call that this call does as well, inside the
+    gate/up launch where it fits; offsets and gather are then taken from it."""
     perm = slot = pool = row_slot = None
     P = pitch = 0
     if gather is not None:
@@ -185,7 +195,8 @@ def moe_expert_ffn_grouped(n: int, E_loc: int, H: int, I: int, act_dtype: int, w
     a = FfnArgs(n, E_loc, H, I, act_dtype, w_dtype, _ptr(xb), _ptr(offsets), _ptr(w_gu), _ptr(w_d),
                 _ptr(s_gate), _ptr(s_up), _ptr(s_down), _ptr(y), _ptr(workspace),
                 workspace.numel() * workspace.element_size(), ev_mid, _ptr(perm), _ptr(slot), _ptr(pool), P, pitch,
-                _ptr(row_slot), None if plan is None else C.addressof(plan), *(ev_gu or (None, None)))
+                _ptr(row_slot), None if plan is None else C.addressof(plan), *(ev_gu or (None, None)),
+                None if index is None else C.addressof(index))
     _check(load().moe_expert_ffn_grouped(C.byref(a), _stream(stream)), "moe_expert_ffn_grouped")
 
 

@@ -328,7 +328,7 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const int32_t* __restr
 
 using namespace moe;
 
-extern "C" int moe_assemble(const moe_assemble_args* a, hipStream_t stream) {
+int moe::check_assemble_args(const moe_assemble_args* a) {
   if (!a) return MOE_EINVAL_NULL;
   if (a->n < 0 || a->n > (1 << 24) || a->E_loc < 1 || a->E_loc > kMaxElocAsm || a->H < 1 || a->P < 0 ||
       a->pool_pitch < a->H)
@@ -336,13 +336,20 @@ extern "C" int moe_assemble(const moe_assemble_args* a, hipStream_t stream) {
   if (a->act_dtype != MOE_F32 && a->act_dtype != MOE_BF16) return MOE_EINVAL_DTYPE;
   if (!a->counts || !a->offsets || !a->err) return MOE_EINVAL_NULL;
   const int esz = dtype_size(a->act_dtype);
-  const int row_bytes = a->H * esz;
-  const int64_t pitch_bytes = a->pool_pitch * esz;
-  if (row_bytes % 16 || pitch_bytes % 16) return MOE_EINVAL_ALIGN;
+  if ((a->H * esz) % 16 || (a->pool_pitch * esz) % 16) return MOE_EINVAL_ALIGN;
   if (a->n > 0) {
     if (!a->slot || !a->expert || !a->perm || !a->pool) return MOE_EINVAL_NULL;
     if (!aligned16(a->pool) || (a->xb && !aligned16(a->xb))) return MOE_EINVAL_ALIGN;
   }
+  return MOE_OK;
+}
+
+extern "C" int moe_assemble(const moe_assemble_args* a, hipStream_t stream) {
+  const int rc = check_assemble_args(a);
+  if (rc != MOE_OK) return rc;
+  const int esz = dtype_size(a->act_dtype);
+  const int row_bytes = a->H * esz;
+  const int64_t pitch_bytes = a->pool_pitch * esz;
   if (a->n <= 256)
     hipLaunchKernelGGL(assemble_index_kernel<256>, dim3(1), dim3(256), 0, stream, a->n, a->slot, a->expert,
                        a->expert_base, a->E_loc, a->P, a->perm, a->pos, a->row_slot, a->counts, a->offsets, a->err);

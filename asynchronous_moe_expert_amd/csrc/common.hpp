@@ -51,4 +51,8 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 inline int launch_status() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH; }
 
+// Host-side argument checks of moe_assemble (MOE_OK or the status it returns); also used by
+// moe_expert_ffn_grouped for a queue index it enqueues itself.
+int check_assemble_args(const moe_assemble_args* a);
+
 }  // namespace moe

@@ -90,6 +90,131 @@ struct GatherRows {
   }
 };
 
+// The queue index of a moe_assemble call (index only) derived inside the gate/up launch of a
+// decode-sized batch (at most kQueueFusedMax pairs): every workgroup computes it in LDS from
+// the raw slot and expert ids of the queue, and one extra workgroup writes the call's outputs.
+constexpr int kQueueFusedMax = 256;
+constexpr int kQueueMaxE = 256;
+struct QueueIdx {
+  const int32_t* slot;    // nullptr: no fused index
+  const int32_t* expert;
+  int base;
+  int n;
+  int64_t P;
+  int32_t* perm;
+  int32_t* pos;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* row_slot;
+  uint32_t* err;
+};
+
+// [SEP] (marsggbo, "SOSP'26 | StreamEP") section 3: the scattered ready inputs of the queue
+// become one batch grouped by expert.  The same stable order as the index kernels of
+// moe_assemble: per-expert counts, exclusive offsets, and within an expert queue order (a
+// 9-bit ballot match ranks a pair among equal keys of lower lanes; the per-wave counts are
+// scanned across the waves).  Pairs live in threads 0..n-1 (n <= 256: waves 0..3).  Outputs
+// in LDS: s_off [E_loc + 1], s_rs (pool slot of each batch row), s_pos (batch row of each
+// queue entry, -1 for a rejected one); with `writer`, the moe_assemble outputs as well.  Every
+// thread of the workgroup calls it (it has workgroup barriers).
+template <int NT>
+__device__ __forceinline__ void queue_index_lds(const QueueIdx& q, int E_loc, int* s_off, int* s_rs, int* s_pos,
+                                                int (*s_wc)[kQueueMaxE + 1], unsigned* s_err, bool writer) {
+  static_assert(NT >= kQueueFusedMax, "one pair per thread");
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n = q.n;
+  for (int x = tid; x < 4 * E_loc; x += NT) s_wc[x / E_loc][x % E_loc] = 0;
+  if (tid == 0) *s_err = 0u;
+  int key = kQueueMaxE, sv = 0;
+  unsigned bad = 0u;
+  if (tid < n) {
+    sv = q.slot[tid];
+    const int e = q.expert[tid] - q.base;
+    bool ok = true;
+    if (sv < 0 || (int64_t)sv >= q.P) { bad |= MOE_ERR_SLOT_RANGE; ok = false; }
+    if (e < 0 || e >= E_loc) { bad |= MOE_ERR_EXPERT_NONLOCAL; ok = false; }
+    if (ok) key = e;
+  }
+  __syncthreads();
+  uint64_t peers = ~0ull;
+#pragma unroll
+  for (int b = 0; b < 9; ++b) {
+    const bool bit = (key >> b) & 1;
+    const uint64_t bal = __ballot(bit);
+    peers &= bit ? bal : ~bal;
+  }
+  const int rank = __popcll(peers & ((1ull << lane) - 1ull));
+  if (key < kQueueMaxE && rank == 0) s_wc[wv][key] = __popcll(peers);  // (key < 256 only on waves 0..3)
+  if (bad) atomicOr(s_err, bad);
+  __syncthreads();
+  if (wv == 0) {  // exclusive scan over the experts (4 per lane), then each wave's first row per expert
+    int c[4][4], v[4], sum = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = lane * 4 + k;
+      v[k] = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        c[k][w] = e < E_loc ? s_wc[w][e] : 0;
+        v[k] += c[k][w];
+      }
+      sum += v[k];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int t = __shfl_up(incl, d);
+      if (lane >= d) incl += t;
+    }
+    int run = incl - sum;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = lane * 4 + k;
+      if (e < E_loc) {
+        s_off[e] = run;
+        if (writer) {
+          q.counts[e] = v[k];
+          q.offsets[e] = run;
+        }
+        int r = run;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          s_wc[w][e] = r;
+          r += c[k][w];
+        }
+      }
+      run += v[k];
+    }
+    if (lane == 63) {
+      s_off[E_loc] = incl;
+      if (writer) q.offsets[E_loc] = incl;
+    }
+  }
+  __syncthreads();
+  if (key < kQueueMaxE) {
+    const int r = s_wc[wv][key] + rank;
+    s_rs[r] = sv;
+    s_pos[tid] = r;
+    if (writer) {
+      q.perm[r] = tid;
+      if (q.pos) q.pos[tid] = r;
+      if (q.row_slot) q.row_slot[r] = sv;
+    }
+  } else if (tid < n) {
+    s_pos[tid] = -1;
+    if (writer && q.pos) q.pos[tid] = -1;
+  }
+  if (writer) {
+    const int total = s_off[E_loc];
+    if (tid < n && tid >= total) {  // batch rows past the accepted pairs
+      q.perm[tid] = -1;
+      if (q.row_slot) q.row_slot[tid] = -1;
+    }
+    if (tid == 0 && *s_err) atomicOr(q.err, *s_err);
+  }
+  __syncthreads();
+}
+
 // --------------------------------------------------------------- expert lookup helpers
 __device__ __forceinline__ int expert_of_row(const int32_t* __restrict__ offsets, int E_loc, int r) {
   for (int e = 0; e < E_loc; ++e)
@@ -316,12 +441,17 @@ __device__ __forceinline__ int next_unit(const int32_t* __restrict__ offsets, in
 // weights of the same k-step) and shared through a double-buffered LDS tile.  The grid is
 // at most what the device holds at once and strides over the units, so every unit of a
 // decode-sized batch starts in the first round and no workgroup slot goes to an idle unit.
-template <int MODE, int WDT, int NS, int MT, int R, int WV>
-__global__ __launch_bounds__(64 * WV) void ffn_mfma_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets,
+// FQ (gate/up only): the queue index is derived in the launch itself (queue_index_lds): every
+// workgroup reads its chunk table and batch rows from its own LDS copy, and the last workgroup
+// writes moe_assemble's outputs and then runs the combine plan, if any, on the batch rows it
+// derived.
+template <int MODE, int WDT, int NS, int MT, int R, int WV, bool FQ>
+__global__ __launch_bounds__(64 * WV) void ffn_mfma_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets_g,
                                                     int E_loc, const char* __restrict__ W,
                                                     const float* __restrict__ s0, const float* __restrict__ s1,
                                                     uint16_t* __restrict__ out, int Kd, int Nw, int out_ld,
-                                                    int n_blocks_N, int n_rows, GatherRows gr, PlanJob plan) {
+                                                    int n_blocks_N, int n_rows, GatherRows gr_g, PlanJob plan,
+                                                    QueueIdx qi) {
   constexpr int BM = MT * 16;
   static_assert(MODE == 1 || NS % 2 == 0, "gate/up waves own (gate, up) strip pairs");
   using AP = APart<MT, 64 * WV>;
@@ -334,15 +464,35 @@ __global__ __launch_bounds__(64 * WV) void ffn_mfma_kernel(const uint16_t* __res
   const int64_t blk_bytes = 1024 * esz;
   const int64_t strip_stride = (int64_t)KS * blk_bytes;
 
-  // With a combine plan (gate/up only, m <= 256) the grid has one workgroup more than the
-  // FFN needs; that last workgroup runs the plan beside the units (a decode-sized batch has
-  // fewer units than compute units).
+  // With a combine plan (gate/up only, m <= 256) or a fused queue index the grid has one
+  // workgroup more than the FFN needs; that last workgroup runs the plan (and writes the
+  // index) beside the units (a decode-sized batch has fewer units than compute units).
   const bool with_plan = MODE == 0 && plan.m > 0;
-  if constexpr (MODE == 0) {
+  const int32_t* offsets = offsets_g;
+  GatherRows gr = gr_g;
+  if constexpr (MODE == 0 && !FQ) {
     if (with_plan && (int)blockIdx.x == (int)gridDim.x - 1) {
       combine_plan_body<64 * WV>(plan);
       return;
     }
+  }
+  if constexpr (MODE == 0 && FQ) {
+    __shared__ int s_qoff[kQueueMaxE + 1], s_qrs[kQueueFusedMax], s_qpos[kQueueFusedMax];
+    __shared__ int s_qwc[4][kQueueMaxE + 1];
+    __shared__ unsigned s_qerr;
+    const bool writer = (int)blockIdx.x == (int)gridDim.x - 1;
+    queue_index_lds<64 * WV>(qi, E_loc, s_qoff, s_qrs, s_qpos, s_qwc, &s_qerr, writer);
+    if (writer) {
+      if (with_plan) {
+        PlanJob pj = plan;
+        pj.row_idx = s_qpos;  // moe_assemble's pos, as derived here
+        combine_plan_body<64 * WV>(pj);
+      }
+      return;
+    }
+    offsets = s_qoff;
+    gr.perm = s_qrs;  // (batch row r reads pool row s_qrs[r])
+    gr.row_slot = s_qrs;
   }
 
   // XCD-aware order: physical workgroup b runs on XCD b % 8.  Each XCD gets an equal,
@@ -350,7 +500,7 @@ __global__ __launch_bounds__(64 * WV) void ffn_mfma_kernel(const uint16_t* __res
   // L2), and its G/8 workgroups stride through that range.  The chunk table is built once
   // for the first unit and again for each later one, so that it holds no registers across
   // the contraction.
-  const int G = (int)gridDim.x - (with_plan ? 1 : 0), b = blockIdx.x, xcd = b & 7;
+  const int G = (int)gridDim.x - (with_plan || FQ ? 1 : 0), b = blockIdx.x, xcd = b & 7;
   int total, u, u_end, nb = 0, e = -1, m0 = 0, mend = 0, nce = 0;
   {
     ChunkTable tab;
@@ -515,23 +665,24 @@ static int resident_workgroups(int threads) {
   return r;
 }
 
-template <int MODE, int WDT, int NS, int MT, int R, int WV>
+template <int MODE, int WDT, int NS, int MT, int R, int WV, bool FQ>
 static void launch_mfma_t(const void* A, const int32_t* offsets, int E_loc, const void* W, const float* s0,
                           const float* s1, void* out, int Kd, int Nw, int out_ld, int n, GatherRows gr,
-                          const PlanJob& plan, hipEvent_t ev0, hipEvent_t ev1, hipStream_t stream) {
+                          const PlanJob& plan, const QueueIdx& qi, hipEvent_t ev0, hipEvent_t ev1,
+                          hipStream_t stream) {
   constexpr int BM = MT * 16;
-  constexpr auto kernel = ffn_mfma_kernel<MODE, WDT, NS, MT, R, WV>;
+  constexpr auto kernel = ffn_mfma_kernel<MODE, WDT, NS, MT, R, WV, FQ>;
   static_assert(MODE == 1 || kPlanFusedMax <= 64 * WV, "a fused plan rounds m up to a power of two <= the threads");
   static_assert((kPlanFusedMax & (kPlanFusedMax - 1)) == 0, "kPlanFusedMax is a power of two");
   const int n_blocks_N = (Nw / 16 + WV * NS - 1) / (WV * NS);
   const int64_t chunks_max = (n + (int64_t)(BM - 1) * E_loc) / BM;  // ragged worst case
   int64_t grid = std::min<int64_t>(chunks_max * n_blocks_N, resident_workgroups<kernel>(64 * WV));
   grid = (grid + 7) / 8 * 8;  // the XCD-aware order needs a multiple of 8
-  if (MODE == 0 && plan.m > 0) grid += 1;  // the plan's workgroup
+  if (MODE == 0 && (plan.m > 0 || FQ)) grid += 1;  // the plan's (and index's) workgroup
   // (ev0, ev1: timestamps taken by the dispatch itself, or none)
   hipExtLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(64 * WV), 0, stream, ev0, ev1, 0, (const uint16_t*)A,
                         offsets, E_loc, (const char*)W, s0, s1, (uint16_t*)out, Kd, Nw, out_ld, n_blocks_N, n, gr,
-                        plan);
+                        plan, qi);
 }
 
 // ------------------------------------------------------------ prefill GEMM path
@@ -1475,7 +1626,8 @@ static bool takes_gemm(int n, int E_loc, int Kd, int Nw, int w_esz, const Gather
 template <int MODE, int WDT>
 static void launch_mfma(const void* A, const int32_t* offsets, int E_loc, const void* W, const float* s0,
                         const float* s1, void* out, int Kd, int Nw, int out_ld, int n, GatherRows gr, float* parts,
-                        const PlanJob& plan, hipEvent_t ev0, hipEvent_t ev1, hipStream_t stream) {
+                        const PlanJob& plan, const QueueIdx& qi, hipEvent_t ev0, hipEvent_t ev1,
+                        hipStream_t stream) {
   constexpr int NS = MODE == 0 ? MOE_FFN_NS_GU : MOE_FFN_NS_D;
   constexpr int R = MODE == 0 ? MOE_FFN_R_GU : MOE_FFN_R_D;
   constexpr int WV = MODE == 0 ? MOE_FFN_WV_GU : MOE_FFN_WV_D;
@@ -1483,14 +1635,25 @@ static void launch_mfma(const void* A, const int32_t* offsets, int E_loc, const 
     launch_gemm<MODE, WDT>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, gr, parts, ev0, ev1, stream);
     return;
   }
-  switch (pick_mt(n, E_loc)) {
-    case 2:
-      launch_mfma_t<MODE, WDT, NS, 2, R, WV>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, gr, plan, ev0, ev1,
-                                             stream);
+  // (the caller passes a fused queue index only for the gate/up projection of a batch that
+  // takes the weight-streaming kernel)
+  const bool fq = MODE == 0 && qi.slot != nullptr;
+  switch (pick_mt(n, E_loc) * 2 + (fq ? 1 : 0)) {
+    case 4:
+      launch_mfma_t<MODE, WDT, NS, 2, R, WV, false>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, gr, plan, qi,
+                                                    ev0, ev1, stream);
+      break;
+    case 5:
+      launch_mfma_t<MODE, WDT, NS, 2, R, WV, MODE == 0>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, gr, plan,
+                                                        qi, ev0, ev1, stream);
+      break;
+    case 7:
+      launch_mfma_t<MODE, WDT, NS, 3, R, WV, MODE == 0>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, gr, plan,
+                                                        qi, ev0, ev1, stream);
       break;
     default:
-      launch_mfma_t<MODE, WDT, NS, 3, R, WV>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, gr, plan, ev0, ev1,
-                                             stream);
+      launch_mfma_t<MODE, WDT, NS, 3, R, WV, false>(A, offsets, E_loc, W, s0, s1, out, Kd, Nw, out_ld, n, gr, plan, qi,
+                                                    ev0, ev1, stream);
       break;
   }
 }
@@ -1548,7 +1711,18 @@ extern "C" int moe_expert_ffn_grouped(const moe_ffn_args* a, hipStream_t stream)
   const bool bf = a->act_dtype == MOE_BF16 && a->w_dtype == MOE_BF16;
   const bool f8 = a->act_dtype == MOE_BF16 && a->w_dtype == MOE_FP8_E4M3;
   if (!f32 && !bf && !f8) return MOE_EINVAL_DTYPE;
-  if (!a->offsets) return MOE_EINVAL_NULL;
+  // the queue index to enqueue with the FFN (a moe_assemble call, index only): validated like
+  // moe_assemble, so that an invalid one enqueues nothing; its buffers then replace offsets
+  // and the gather fields of a
+  const moe_assemble_args* ix = a->index;
+  if (ix) {
+    const int rc = check_assemble_args(ix);
+    if (rc != MOE_OK) return rc;
+    if (ix->xb || ix->n != a->n || ix->E_loc != a->E_loc || ix->H != a->H || ix->act_dtype != a->act_dtype)
+      return MOE_EINVAL_SIZE;
+  }
+  const int32_t* offsets = ix ? ix->offsets : a->offsets;
+  if (!offsets) return MOE_EINVAL_NULL;
   // the combine plan to enqueue with the FFN: validated here, so that an invalid one
   // enqueues nothing; job.m > 0 when it may run inside the gate/up launch
   PlanJob job{};
@@ -1557,6 +1731,10 @@ extern "C" int moe_expert_ffn_grouped(const moe_ffn_args* a, hipStream_t stream)
     if (rc != MOE_OK) return rc;
   }
   if (a->n == 0) {
+    if (ix) {
+      const int rc = moe_assemble(ix, stream);
+      if (rc != MOE_OK) return rc;
+    }
     if (a->plan) {
       const int rc = moe_combine_plan(a->plan, stream);
       if (rc != MOE_OK) return rc;
@@ -1567,15 +1745,20 @@ extern "C" int moe_expert_ffn_grouped(const moe_ffn_args* a, hipStream_t stream)
   // the rows the gate/up projection reads: the batch xb, or pool rows through the queue
   GatherRows gr{nullptr, nullptr, 0, 0, nullptr};
   const void* x_src = a->xb;
-  if (a->perm || a->row_slot) {
+  const int32_t* g_perm = ix ? ix->perm : a->perm;
+  const int32_t* g_slot = ix ? ix->slot : a->slot;
+  const int32_t* g_row_slot = ix ? ix->row_slot : a->row_slot;
+  const void* g_pool = ix ? ix->pool : a->pool;
+  const int64_t g_P = ix ? ix->P : a->P, g_pitch = ix ? ix->pool_pitch : a->pool_pitch;
+  if (g_perm || g_row_slot) {
     const int esz = dtype_size(a->act_dtype);
-    if ((!a->row_slot && !a->slot) || !a->pool) return MOE_EINVAL_NULL;
-    if (a->P < 1 || a->pool_pitch < a->H) return MOE_EINVAL_SIZE;
-    if (!f32 && (double)a->P * (double)a->pool_pitch * esz >= 2147483648.0) return MOE_EINVAL_SIZE;
-    if (!aligned16(a->pool) || (a->pool_pitch * esz) % 16) return MOE_EINVAL_ALIGN;
+    if ((!g_row_slot && !g_slot) || !g_pool) return MOE_EINVAL_NULL;
+    if (g_P < 1 || g_pitch < a->H) return MOE_EINVAL_SIZE;
+    if (!f32 && (double)g_P * (double)g_pitch * esz >= 2147483648.0) return MOE_EINVAL_SIZE;
+    if (!aligned16(g_pool) || (g_pitch * esz) % 16) return MOE_EINVAL_ALIGN;
     // (perm only marks the gather when row_slot is given; it is then never read)
-    gr = GatherRows{a->perm ? a->perm : a->row_slot, a->slot, a->pool_pitch, a->P, a->row_slot};
-    x_src = a->pool;
+    gr = GatherRows{g_perm ? g_perm : g_row_slot, g_slot, g_pitch, g_P, g_row_slot};
+    x_src = g_pool;
   }
   if (!x_src || !a->w_gu || !a->w_d || !a->y) return MOE_EINVAL_NULL;
   if (f8 && (!a->s_gate || !a->s_up || !a->s_down)) return MOE_EINVAL_NULL;
@@ -1592,9 +1775,25 @@ extern "C" int moe_expert_ffn_grouped(const moe_ffn_args* a, hipStream_t stream)
     const size_t off = h_bytes(n, I, dtype_size(a->act_dtype));
     if (a->workspace_bytes >= off + kPartAreaBytes) parts = (float*)((char*)a->workspace + off);
   }
-  // the plan joins the gate/up launch of the streaming kernel, else it runs before the FFN
-  if (f32 || takes_gemm(n, E, H, 2 * I, f8 ? 1 : 2, gr)) job.m = 0;
-  if (a->plan && job.m == 0) {
+  // the queue index joins the gate/up launch of the streaming kernel for queues of up to
+  // kQueueFusedMax pairs, else moe_assemble runs first; the plan joins the same launch, else
+  // it runs before the FFN (after the gate/up launch when that launch derives the index, since
+  // the plan reads its pos)
+  const bool streaming = !f32 && !takes_gemm(n, E, H, 2 * I, f8 ? 1 : 2, gr);
+  QueueIdx qi{};
+  if (ix && streaming && n <= kQueueFusedMax) {
+    qi = QueueIdx{ix->slot, ix->expert, ix->expert_base, n, ix->P, ix->perm, ix->pos,
+                  ix->counts, ix->offsets, ix->row_slot, ix->err};
+  } else if (ix) {
+    const int rc = moe_assemble(ix, stream);
+    if (rc != MOE_OK) return rc;
+  }
+  if (!streaming) job.m = 0;
+  // (a plan that runs in the launch deriving the index reads the batch rows derived there, so
+  // only a plan over the index's own pos joins it)
+  if (qi.slot && a->plan && a->plan->row_idx != ix->pos) job.m = 0;
+  const bool plan_after_gu = a->plan && qi.slot && job.m == 0;
+  if (a->plan && job.m == 0 && !plan_after_gu) {
     const int rc = moe_combine_plan(a->plan, stream);
     if (rc != MOE_OK) return rc;
   }
@@ -1605,24 +1804,30 @@ extern "C" int moe_expert_ffn_grouped(const moe_ffn_args* a, hipStream_t stream)
   if (f32) {
     const int64_t t1 = (int64_t)n * I, t2 = (int64_t)n * H;
     hipLaunchKernelGGL(gateup_f32_kernel, dim3((unsigned)((t1 + 255) / 256)), dim3(256), 0, stream,
-                       (const float*)x_src, a->offsets, E, n, H, I, (const float*)a->w_gu, (float*)a->workspace, gr);
+                       (const float*)x_src, offsets, E, n, H, I, (const float*)a->w_gu, (float*)a->workspace, gr);
     if (a->ev_mid) (void)hipEventRecord(a->ev_mid, stream);
     hipLaunchKernelGGL(down_f32_kernel, dim3((unsigned)((t2 + 255) / 256)), dim3(256), 0, stream,
-                       (const float*)a->workspace, a->offsets, E, n, H, I, (const float*)a->w_d, (float*)a->y);
+                       (const float*)a->workspace, offsets, E, n, H, I, (const float*)a->w_d, (float*)a->y);
     return launch_status();
   }
+  const QueueIdx no_q{};
   if (bf) {
-    launch_mfma<0, MOE_BF16>(x_src, a->offsets, E, a->w_gu, nullptr, nullptr, a->workspace, H, 2 * I, I, n, gr, parts,
-                             job, ev0, ev1, stream);
-    if (a->ev_mid) (void)hipEventRecord(a->ev_mid, stream);
-    launch_mfma<1, MOE_BF16>(a->workspace, a->offsets, E, a->w_d, nullptr, nullptr, a->y, I, H, H, n, none, parts,
-                             no_plan, nullptr, nullptr, stream);
+    launch_mfma<0, MOE_BF16>(x_src, offsets, E, a->w_gu, nullptr, nullptr, a->workspace, H, 2 * I, I, n, gr, parts, job,
+                             qi, ev0, ev1, stream);
   } else {
-    launch_mfma<0, MOE_FP8_E4M3>(x_src, a->offsets, E, a->w_gu, a->s_gate, a->s_up, a->workspace, H, 2 * I, I, n, gr,
-                                 parts, job, ev0, ev1, stream);
-    if (a->ev_mid) (void)hipEventRecord(a->ev_mid, stream);
-    launch_mfma<1, MOE_FP8_E4M3>(a->workspace, a->offsets, E, a->w_d, a->s_down, nullptr, a->y, I, H, H, n, none,
-                                 parts, no_plan, nullptr, nullptr, stream);
+    launch_mfma<0, MOE_FP8_E4M3>(x_src, offsets, E, a->w_gu, a->s_gate, a->s_up, a->workspace, H, 2 * I, I, n, gr,
+                                 parts, job, qi, ev0, ev1, stream);
   }
+  if (plan_after_gu) {
+    const int rc = moe_combine_plan(a->plan, stream);
+    if (rc != MOE_OK) return rc;
+  }
+  if (a->ev_mid) (void)hipEventRecord(a->ev_mid, stream);
+  if (bf)
+    launch_mfma<1, MOE_BF16>(a->workspace, offsets, E, a->w_d, nullptr, nullptr, a->y, I, H, H, n, none, parts, no_plan,
+                             no_q, nullptr, nullptr, stream);
+  else
+    launch_mfma<1, MOE_FP8_E4M3>(a->workspace, offsets, E, a->w_d, a->s_down, nullptr, a->y, I, H, H, n, none, parts,
+                                 no_plan, no_q, nullptr, nullptr, stream);
   return launch_status();
 }

@@ -32,7 +32,8 @@ _TORCH = {N.MOE_F32: torch.float32, N.MOE_BF16: torch.bfloat16, N.MOE_FP8_E4M3: 
 
 class ExpertStep:
     def __init__(self, E_loc: int, H: int, I: int, K: int, act_dtype: int, w_dtype: int, n_max: int, T_cap: int,
-                 device="cuda", gather_on_load: bool = True, overlap: bool = False, fuse_plan: bool = True):
+                 device="cuda", gather_on_load: bool = True, overlap: bool = False, fuse_plan: bool = True,
+                 fuse_index: bool = True):
         self.E_loc, self.H, self.I, self.K = E_loc, H, I, K
         self.act_dtype, self.w_dtype, self.n_max, self.T_cap = act_dtype, w_dtype, n_max, T_cap
         dev = torch.device(device)
@@ -58,6 +59,7 @@ class ExpertStep:
         self.gather_on_load = gather_on_load
         self._gather = None  # (perm, slot, pool, row_slot) of the last assemble when gathering on load
         self.fuse_plan = fuse_plan
+        self.fuse_index = fuse_index and gather_on_load  # the queue index derived in the FFN call
         self.side = torch.cuda.Stream(device=dev) if overlap else None
         self._ev_asm = torch.cuda.Event() if overlap else None
         self._ev_plan = torch.cuda.Event() if overlap else None
@@ -79,10 +81,19 @@ class ExpertStep:
                        xb, self.err, n=n, stream=stream, row_slot=rs)
         self._gather = (self.perm, slot, pool, rs) if self.gather_on_load else None
 
-    def ffn(self, n: int, ev_mid: int | None = None, stream=None, plan=None, ev_gu=None) -> None:
+    def ffn(self, n: int, ev_mid: int | None = None, stream=None, plan=None, ev_gu=None, index=None) -> None:
         N.moe_expert_ffn_grouped(n, self.E_loc, self.H, self.I, self.act_dtype, self.w_dtype, self.xb, self.offsets,
                                  self.w_gu, self.w_d, self.y, self.workspace, self.s_gate, self.s_up, self.s_down,
-                                 ev_mid=ev_mid, stream=stream, gather=self._gather, plan=plan, ev_gu=ev_gu)
+                                 ev_mid=ev_mid, stream=stream, gather=self._gather, plan=plan, ev_gu=ev_gu,
+                                 index=index)
+
+    def index_args(self, slot, expert, expert_base: int, pool, n: int):
+        """The moe_assemble arguments (index only) of this step's queue, for ffn(index=...): the
+        FFN call then derives the queue index itself (inside its gate/up launch for decode-sized
+        queues) and gathers the rows through it."""
+        self._gather = (self.perm, slot, pool, self.row_slot)
+        return N.assemble_args(slot, expert, expert_base, self.E_loc, pool, self.perm, self.pos, self.counts,
+                               self.offsets, None, self.err, n=n, row_slot=self.row_slot, H=self.H)
 
     def _combine_room(self, m: int) -> None:
         if m > self.cmb_ws_m:  # plumbing: grow the caller-owned scratch (outside any timed loop)
@@ -108,14 +119,17 @@ class ExpertStep:
             ev_mid: int | None = None, stream=None) -> None:
         """The whole step on one batch: assemble, FFN, combine of the local results."""
         n = int(slot.numel() if n is None else n)
-        self.assemble(slot, expert, expert_base, pool, n=n, stream=stream)
         if self.side is None and self.fuse_plan:
-            # the combine plan rides in the FFN call (inside the gate/up launch where it fits);
-            # the same argument struct then drives the apply
+            # the queue index and the combine plan ride in the FFN call (inside the gate/up
+            # launch where they fit); the plan's argument struct then drives the apply
+            index = self.index_args(slot, expert, expert_base, pool, n) if self.fuse_index else None
+            if index is None:
+                self.assemble(slot, expert, expert_base, pool, n=n, stream=stream)
             plan = self.local_combine_args(tok, kslot, w, gen, n)
-            self.ffn(n, ev_mid=ev_mid, stream=stream, plan=plan)
+            self.ffn(n, ev_mid=ev_mid, stream=stream, plan=plan, index=index)
             N.combine_call(plan, "apply", stream)
             return
+        self.assemble(slot, expert, expert_base, pool, n=n, stream=stream)
         if self.side is None:
             self.ffn(n, ev_mid=ev_mid, stream=stream)
             self.combine(self.y, self.pos, tok, kslot, w, gen, m=n, n_rows=n, stream=stream)

@@ -287,11 +287,16 @@ class StepRunner:
                     self.deliver(w)
                     tok = self.tok[w]
                     if p == 0:
+                        # the calls of ExpertStep.run: with the queue index derived in the FFN
+                        # call, the assemble interval holds no launch
                         ev.record(evs[0], self.stream)
-                        st.assemble(d["slot"], d["expert"], self.base, self.pool, n=b.n)
+                        index = (st.index_args(d["slot"], d["expert"], self.base, self.pool, b.n)
+                                 if st.fuse_index else None)
+                        if index is None:
+                            st.assemble(d["slot"], d["expert"], self.base, self.pool, n=b.n)
                         ev.record(evs[1], self.stream)
                         plan = st.local_combine_args(tok, d["kslot"], d["w"], d["gen"], b.n)
-                        st.ffn(b.n, ev_mid=evs[2], plan=plan)
+                        st.ffn(b.n, ev_mid=evs[2], plan=plan, index=index)
                         ev.record(evs[3], self.stream)
                         M.combine_call(plan, "apply")
                         ev.record(evs[4], self.stream)

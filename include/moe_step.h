@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MOE_STEP_VERSION 1
+#define MOE_STEP_VERSION 2  /* 2: moe_ffn_args.index */
 
 /* Element storage types.  MOE_BF16 is bfloat16; MOE_FP8_E4M3 is OCP 8-bit float E4M3
  * (bias 7, max 448, no infinities), used for weights only, with one fp32 scale per
@@ -191,7 +191,24 @@ int moe_pack_ffn_weights(const moe_pack_args* args, hipStream_t stream);
  * otherwise it is launched on the stream before the FFN.  Either way it reads only the
  * arrival metadata (including row_idx, so moe_assemble's pos must already be enqueued) and
  * the token state, and it is complete when the down projection starts; follow it with
- * moe_combine_apply(plan, ...) ordered after this call. */
+ * moe_combine_apply(plan, ...) ordered after this call.
+ *
+ * index: optional (NULL: none).  The arguments of a moe_assemble call for this batch (index
+ * only: its xb must be NULL; n, E_loc, H and act_dtype equal to this call's, MOE_EINVAL_SIZE
+ * otherwise); the call then does that moe_assemble's work as well, with the same outputs and
+ * validation (invalid index arguments return moe_assemble's status and enqueue nothing).
+ * offsets, perm, slot, pool, P, pool_pitch and row_slot of this struct are then ignored: the
+ * FFN uses the index's offsets and gathers batch rows from its pool (the ABI's
+ * gather-on-load above, through its row_slot when given).  For queues of at most 256 pairs on
+ * the weight-streaming path (bf16 activations, fewer than 96 E_loc rows) every gate/up
+ * workgroup derives the index itself from slot and expert, in its local memory, before its
+ * work units, and one extra workgroup writes the moe_assemble outputs (perm, pos, counts,
+ * offsets, row_slot, err), so the index costs no launch of its own ([SEP] section 6 counts the
+ * regrouping among the costs that asynchrony adds); a plan given with it then runs in that
+ * workgroup on the batch rows it derived (or, when the plan cannot join the launch, is
+ * launched right after the gate/up kernel, as it reads pos).  Otherwise moe_assemble is
+ * launched on the stream before the FFN.  Either way the outputs are complete when the down
+ * projection starts. */
 struct moe_combine_args;
 typedef struct moe_ffn_args {
   int32_t n, E_loc, H, I;
@@ -217,6 +234,7 @@ typedef struct moe_ffn_args {
   const struct moe_combine_args* plan; /* optional combine plan to run with the FFN (above) */
   hipEvent_t ev_gu_start;  /* optional, with ev_gu_stop: gate/up kernel duration (above) */
   hipEvent_t ev_gu_stop;
+  const struct moe_assemble_args* index; /* optional queue index to derive with the FFN (above) */
 } moe_ffn_args;
 
 size_t moe_ffn_workspace_size(int32_t n_max, int32_t E_loc, int32_t H, int32_t I, int32_t act_dtype);

@@ -821,3 +821,77 @@ def test_gemm_split_tail_matches_whole_units(wdt):
     err = row_rel_err(O.decode_bf16(ys[0][rows]), y_ref)
     _say(f"  {len(plan)} split tail units; oracle row rel err on {len(rows)} rows {err:.3e}")
     assert err <= TOL[wdt]
+
+
+def _fused_index_batch(case):
+    if case.startswith("c1"):
+        b, wts = W.c1_decode()
+        act, wc = M.MOE_BF16, M.MOE_BF16
+    else:  # fp8 weights on the weight-streaming path: the first 256 pairs of the last prefill wave
+        setup = W.c4_prefill_setup()
+        b = W.merge_batches([W.c4_wave(setup, 3)])
+        wts = setup.weights
+        act, wc = M.MOE_BF16, M.MOE_FP8_E4M3
+        keep = np.arange(256)
+        b = W.subset_batch(b, keep)
+    if case == "c1_bad_ragged":
+        keep = np.arange(200)
+        b = W.subset_batch(b, keep)
+        b.slot = b.slot.copy()
+        b.expert = b.expert.copy()
+        b.slot[[3, 77, 150]] = [b.P, -1, b.P + 9]          # slots outside the pool
+        b.expert[[10, 120]] = [b.expert_base - 1, b.expert_base + b.E_loc]  # experts of another rank
+    return b, wts, act, wc
+
+
+@pytest.mark.parametrize("case", ["c1_bf16", "c1_bad_ragged", "c4_fp8_256"])
+def test_fused_queue_index(case):
+    """moe_ffn_args.index: the queue index derived inside the gate/up launch gives the same bits
+    as moe_assemble followed by the FFN (index outputs, error word, FFN rows, release list,
+    released rows and combine state), and its integer outputs match the oracle; also with no
+    combine plan in the call."""
+    _say(f"fused queue index vs separate moe_assemble: {case}")
+    b, wts, act, wc = _fused_index_batch(case)
+    d = batch_tensors(b)
+    wt = weight_tensors(wts)
+    n = b.n
+    steps = []
+    for fuse in (True, False):
+        st = M.ExpertStep(b.E_loc, b.H, wts.I, b.K, act, wc, n, b.T, fuse_index=fuse)
+        st.load_weights(wt["wg"], wt["wu"], wt["wd"], wt.get("s_gate"), wt.get("s_up"), wt.get("s_down"))
+        if "r_rows" in d:
+            st.combine(d["r_rows"], d["r_idx"], d["r_tok"], d["r_kslot"], d["r_w"], d["r_gen"])
+        st.err.zero_()
+        st.run(d["slot"], d["expert"], b.expert_base, d["pool"], d["tok"], d["kslot"], d["w"], d["gen"])
+        torch.cuda.synchronize()
+        steps.append(st)
+    f, s = steps
+    a = O.assemble(b.slot, b.expert, b.expert_base, b.E_loc, b.P)
+    ef, es = sync_err(f.err), sync_err(s.err)
+    assert ef == es and (ef & 3) == a["err"], (ef, es, a["err"])
+    assert np.array_equal(f.perm.cpu().numpy()[:n], a["perm"])
+    assert np.array_equal(f.pos.cpu().numpy()[:n], a["pos"])
+    assert np.array_equal(f.counts.cpu().numpy(), a["counts"])
+    assert np.array_equal(f.offsets.cpu().numpy(), a["offsets"])
+    nv = int(a["offsets"][-1])
+    rs = f.row_slot.cpu().numpy()[:n]
+    assert np.array_equal(rs[:nv], b.slot[a["perm"][:nv]]) and (rs[nv:] == -1).all()
+    for name in ("perm", "pos", "counts", "offsets", "row_slot"):
+        assert np.array_equal(getattr(f, name).cpu().numpy()[:n], getattr(s, name).cpu().numpy()[:n]), name
+    assert np.array_equal(to_numpy_bits(f.y[:nv]), to_numpy_bits(s.y[:nv])), "FFN rows differ"
+    nr = int(f.rel_count.item())
+    assert nr == int(s.rel_count.item())
+    rel = f.rel_list[:nr]
+    assert torch.equal(rel, s.rel_list[:nr])
+    if nr:
+        assert np.array_equal(to_numpy_bits(f.out[rel.long()]), to_numpy_bits(s.out[rel.long()]))
+    assert torch.equal(f.state.mask, s.state.mask) and torch.equal(f.state.tgen, s.state.tgen)
+    # the FFN call with the index and no combine plan
+    f.err.zero_()
+    f.y.zero_()
+    ix = f.index_args(d["slot"], d["expert"], b.expert_base, d["pool"], n)
+    f.ffn(n, index=ix)
+    torch.cuda.synchronize()
+    assert sync_err(f.err) == a["err"]
+    assert np.array_equal(f.perm.cpu().numpy()[:n], a["perm"])
+    assert np.array_equal(to_numpy_bits(f.y[:nv]), to_numpy_bits(s.y[:nv])), "FFN rows differ without a plan"

@@ -50,7 +50,7 @@ def test_struct_layout_and_version(lib):
     for k, s in enumerate(N._STRUCTS):
         assert lib.moe_struct_size(k) == C.sizeof(s)
     assert lib.moe_struct_size(99) == 0
-    assert M.moe_version() == 1
+    assert M.moe_version() == 2  # 2: moe_ffn_args.index
     assert M.moe_strerror(0) == "ok" and "NULL" in M.moe_strerror(-1)
 
 

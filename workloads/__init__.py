@@ -23,7 +23,7 @@ from .gen import (  # noqa: F401
     c4_prefill_setup,
     c4_wave,
     make_layer_weights,
-    merge_batches,
+    merge_batches, subset_batch,
     to_bf16_bits,
     to_e4m3_codes,
     zipf_probs,

@@ -343,3 +343,11 @@ def merge_batches(batches: list) -> Batch:
                        rcat("tok"), rcat("kslot"), rcat("w"), rcat("gen"))
     return Batch(b0.act, b0.H, b0.K, b0.E_loc, b0.expert_base, b0.P, b0.pool, cat("slot"), cat("expert"),
                  cat("tok"), cat("kslot"), cat("w"), cat("gen"), b0.T, rem)
+
+
+def subset_batch(b: Batch, keep) -> Batch:
+    """The queue entries `keep` of a batch (in that order), with its pool, token range and remote
+    results unchanged: tokens whose local pairs are dropped stay incomplete."""
+    keep = np.asarray(keep)
+    return Batch(b.act, b.H, b.K, b.E_loc, b.expert_base, b.P, b.pool, b.slot[keep].copy(), b.expert[keep].copy(),
+                 b.tok[keep].copy(), b.kslot[keep].copy(), b.w[keep].copy(), b.gen[keep].copy(), b.T, b.remote)
