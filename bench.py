@@ -287,11 +287,12 @@ class StepRunner:
                     self.deliver(w)
                     tok = self.tok[w]
                     if p == 0:
-                        # the calls of ExpertStep.run: with the queue index derived in the FFN
-                        # call, the assemble interval holds no launch
+                        # the calls of ExpertStep.run; where the queue index is derived inside the
+                        # gate/up launch (queues of at most 256 pairs) the assemble interval holds
+                        # no launch, elsewhere moe_assemble is timed on its own
                         ev.record(evs[0], self.stream)
                         index = (st.index_args(d["slot"], d["expert"], self.base, self.pool, b.n)
-                                 if st.fuse_index else None)
+                                 if st.fuse_index and b.n <= 256 else None)
                         if index is None:
                             st.assemble(d["slot"], d["expert"], self.base, self.pool, n=b.n)
                         ev.record(evs[1], self.stream)
