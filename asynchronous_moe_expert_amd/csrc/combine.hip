@@ -359,10 +359,22 @@ __global__ __launch_bounds__(kRelThreads) void combine_release_kernel(int T_cap,
   __shared__ int s_lo[kRelThreads / 64], s_hi[kRelThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   int lo = T_cap, hi = -1;
-  for (int x = tid; x < m; x += kRelThreads) {
-    const int t = min(max(tok[x], 0), T_cap - 1);
-    lo = min(lo, t);
-    hi = max(hi, t);
+  // (eight loads in flight per thread: one round trip per 8192 arrivals; m >= 1 here, as the
+  // loop does not run for m = 0)
+  for (int x0 = 0; x0 < m; x0 += 8 * kRelThreads) {
+    int tv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      tv[u] = tok[min(x0 + u * kRelThreads + tid, m - 1)];  // (unconditional: no wait between the loads)
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (x0 + u * kRelThreads + tid < m) {
+        const int t = min(max(tv[u], 0), T_cap - 1);
+        lo = min(lo, t);
+        hi = max(hi, t);
+      }
+    }
   }
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) {
@@ -456,22 +468,40 @@ __global__ __launch_bounds__(kCmbThreads) void combine_apply_kernel(int H, const
   __shared__ float s_w[32];
   __shared__ int64_t s_row[32];
   const int sidx = blockIdx.x, tid = threadIdx.x;
-  if (sidx >= ws[0]) return;
+  // the segment count and this workgroup's record in one round trip (the record slot exists for
+  // every workgroup: the grid is at most m); cnt is an in/out asm operand so that the test below
+  // cannot be scheduled between the two loads
+  int cnt = ws[0];
   const int4 sg = reinterpret_cast<const int4*>(ws + 4)[sidx];
+  asm volatile("" : "+s"(cnt) : "s"(sg.x), "s"(sg.y), "s"(sg.z), "s"(sg.w), "s"(H), "s"(m), "s"(acc), "s"(rows),
+               "s"(row_pitch), "s"(out), "s"(out_pitch));
+  if (sidx >= cnt) return;
   const int t = sg.x, na = sg.z;
   const bool complete = sg.w & 1, started = sg.w & 2;
+  float* at = acc + (int64_t)t * H;
+  TO* o = out + (int64_t)t * out_pitch;
+  const int nv = H >> 3;
+  // this thread's first vector of the held sum is loaded with the list entries (the barrier
+  // below waits for both)
+  float sum0[8];
+  if (started && tid < nv) {
+    RowIO<float>::load8(at + tid * 8, sum0);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) sum0[k] = 0.f;
+  }
   if (tid < na) {
     const int2 rw = reinterpret_cast<const int2*>(ws + plan_list_offset(m))[sg.y + tid];
     s_row[tid] = rw.x;
     s_w[tid] = __int_as_float(rw.y);
   }
   __syncthreads();
-  float* at = acc + (int64_t)t * H;
-  TO* o = out + (int64_t)t * out_pitch;
-  const int nv = H >> 3;
   for (int v = tid; v < nv; v += kCmbThreads) {
     float sum[8];
-    if (started) {
+    if (v == tid) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sum[k] = sum0[k];
+    } else if (started) {
       RowIO<float>::load8(at + v * 8, sum);
     } else {
 #pragma unroll
