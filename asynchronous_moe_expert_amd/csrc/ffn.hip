@@ -1229,6 +1229,7 @@ __global__ __launch_bounds__(256) void ffn_gemm_finalize_kernel(const int32_t* _
 // so a chunk's column blocks run side by side on one XCD and share its activations in L2.
 constexpr int kG2BM = 256;
 constexpr int kG2MT = kG2BM / 32;
+constexpr int kG2RankRounds = 8;
 #ifndef MOE_G2_STAGES
 #define MOE_G2_STAGES 4
 #endif
@@ -1238,9 +1239,10 @@ static_assert(kG2S >= 2 && kG2S <= 4, "two to four LDS stages");
 // Chunks of 256 rows in cost order (above), kept in LDS so that no register holds the table
 // across a unit's contraction: per expert its first and end row, full-chunk count and the
 // sorted position of its first full chunk (non-decreasing in expert order), and for each
-// partial chunk's sorted position past the full ones, its expert.  Built by wave 0.
+// partial chunk's sorted position past the full ones, its expert and 32-row tile count.
+// Built by wave 0.
 struct G2Table {
-  int a0[256], a1[256], nf[256], fs[256], pe[256];
+  int a0[256], a1[256], nf[256], fs[256], pe[256], pt[256];
   int E, F, total;
 };
 
@@ -1277,7 +1279,10 @@ __device__ __forceinline__ void g2_table_build(G2Table& tb, const int32_t* __res
     static_for<4>([&](auto jc) {
       constexpr int j = jc();
       const uint64_t bal = __ballot(pt[j] == t);
-      if (pt[j] == t) tb.pe[pos + __popcll(bal & below)] = lane + 64 * j;
+      if (pt[j] == t) {
+        tb.pe[pos + __popcll(bal & below)] = lane + 64 * j;
+        tb.pt[pos + __popcll(bal & below)] = t;
+      }
       pos += __popcll(bal);
     });
   }
@@ -1361,9 +1366,43 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm256_kernel(const uint16_t* __r
   const int U = tab.total * n_blocks_N;
   const int G = gridDim.x, Gx = G >> 3, b = blockIdx.x;
   const int jw = (b & 7) * Gx + (b >> 3);  // logical workgroup: XCD-major
+  // The last, partial round (T = U mod G units, the cheapest) goes to the workgroups the full
+  // rounds loaded least: its unit i to the workgroup of rank i in (model cost, logical index)
+  // order, a unit of t row tiles costing t + 1 (measured unit times on prefill waves: 13 +
+  // 12.4 t us for gate/up, 6 + 7.6 t for down).  The snake alone hands the last round to the
+  // workgroups that drew the largest units of round 0 (up to 30 us longer on the prefill waves
+  // of 3277-4915 pairs).  For more than kG2RankRounds full rounds the snake order is kept.
+  const int R = U / G;
+  const bool ranked = R >= 1 && R <= kG2RankRounds && U > R * G && G <= 256;
+  int tail_u = -1;  // this workgroup's unit of the last round, if any
+  if (ranked) {
+    // model cost of logical workgroup w's full rounds
+    auto cost_of = [&](int w) {
+      int c = 0;
+      for (int r = 0; r < R; ++r) {
+        const int q = (r * G + ((r & 1) ? G - 1 - w : w)) / n_blocks_N;
+        c += q < tab.F ? kG2MT + 1 : tab.pt[q - tab.F] + 1;
+      }
+      return c;
+    };
+    // each wave ranks 64 workgroups (one per lane) against this one
+    __shared__ int s_below[4];
+    const int mine = cost_of(jw), w = wv * 64 + lane;
+    int ahead = 0;
+    if (w < G) {
+      const int c = cost_of(w);
+      ahead = c < mine || (c == mine && w < jw);
+    }
+    const int cnt = __popcll(__ballot(ahead));
+    if (lane == 0) s_below[wv] = cnt;
+    __syncthreads();
+    const int rank = s_below[0] + s_below[1] + s_below[2] + s_below[3];
+    if (rank < U - R * G) tail_u = R * G + rank;
+  }
 #pragma clang loop unroll(disable)
   for (int r = 0;; ++r) {
-    const int u = r * G + ((r & 1) ? G - 1 - jw : jw);
+    int u = r * G + ((r & 1) ? G - 1 - jw : jw);
+    if (r == R && ranked) u = tail_u < 0 ? U : tail_u;
     if (u >= U) break;
     const int q = u / n_blocks_N, nb = u - q * n_blocks_N;
     int e, m0, mend;
