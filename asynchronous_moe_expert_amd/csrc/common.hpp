@@ -18,12 +18,13 @@ constexpr int kWave = 64;
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
+// fp32 -> bf16, round to nearest even; NaN stays a NaN (gfx950's v_cvt_pk_bf16_f32; the
+// integer rounding sequence with its NaN branch cost a dozen instructions per value)
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  const __bf16 h = (__bf16)f;
+  uint16_t r;
+  __builtin_memcpy(&r, &h, 2);
+  return r;
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {

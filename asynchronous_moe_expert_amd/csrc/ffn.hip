@@ -1234,7 +1234,7 @@ constexpr int kG2RankRounds = 8;
 #define MOE_G2_STAGES 4
 #endif
 constexpr int kG2S = MOE_G2_STAGES;
-static_assert(kG2S >= 2 && kG2S <= 4, "two to four LDS stages");
+static_assert(kG2S == 4, "four LDS stages (the epilogue takes one per wave)");
 
 // Chunks of 256 rows in cost order (above), kept in LDS so that no register holds the table
 // across a unit's contraction: per expert its first and end row, full-chunk count and the
@@ -1332,6 +1332,67 @@ __device__ __forceinline__ void gemm_epilogue_mt(const f32x16 (&acc)[MTT][2], in
       });
     }
   });
+}
+
+// Epilogue of a 256-row unit through LDS.  Each wave converts its tile (down: 256 rows x 64
+// output columns; gate/up: 256 x 32 h values) to bf16 in its own activation stage, free once
+// the k-loop's last barrier has passed, reads it back row by row and stores 16 bytes per lane
+// (down: 8 rows of 128 B per instruction, gate/up: 16 rows of 64 B) through a buffer resource
+// that ends at the chunk's last row, so the stores of rows past it are dropped without a
+// branch.  Every per-lane value is derived here: left to the compiler, the row addresses were
+// computed ahead of the contraction and kept in scratch across it, and each reload's wait for
+// the memory counter then also waited for the stores issued before it (2-byte stores straight
+// from the MFMA layout took ~2 us per 32-row tile this way, 13-17 us of an 8-tile unit).  The
+// barrier after the read-back keeps the next unit's copies out of the stages until every wave
+// has read its tile.
+template <int MODE, int MTA>
+__device__ __forceinline__ void g2_epilogue(const f32x16 (&acc)[MTA][2], u32x4* st, bool wact, int e, int m0,
+                                           int mend, int col0, int lane_in, const float* __restrict__ s0,
+                                           const float* __restrict__ s1, uint16_t* __restrict__ out,
+                                           int out_ld) {
+  constexpr int CW = MODE == 0 ? 32 : 64;  // output columns of a wave
+  constexpr int LPR = CW * 2 / 16;         // lanes per row on the read-back (16 bytes each)
+  constexpr int RPI = 64 / LPR;            // rows per read-back instruction
+  int lane = lane_in;
+  asm volatile("" : "+v"(lane));
+  const int l32 = lane & 31, hf = lane >> 5;
+  if (wact) {
+    float sc0, sc1;
+    gemm_scales<MODE, MOE_FP8_E4M3>(e, col0, l32, s0, s1, out_ld, sc0, sc1);
+    uint16_t* t16 = reinterpret_cast<uint16_t*>(st) + 4 * hf * CW + l32;
+    static_for<MTA>([&](auto mt) {
+      static_for<4>([&](auto g) {
+        static_for<4>([&](auto k) {
+          constexpr int row = mt() * 32 + 8 * g() + k();  // + 4 hf (in t16)
+          const float a = acc[mt()][0][4 * g() + k()], b = acc[mt()][1][4 * g() + k()];
+          if constexpr (MODE == 0) {
+            t16[row * CW] = f32_to_bf16(silu_mul_fast(a * sc0, b * sc1));
+          } else {
+            t16[row * CW] = f32_to_bf16(a * sc0);
+            t16[row * CW + 32] = f32_to_bf16(b * sc1);
+          }
+        });
+      });
+    });
+  }
+  __syncthreads();
+  if (wact) {
+    const int rr = lane / LPR, cq = lane - rr * LPR;
+    const __amdgpu_buffer_rsrc_t ors =
+        buffer_rsrc(out + (int64_t)m0 * out_ld + (MODE == 0 ? col0 / 2 : col0), (int64_t)(mend - m0) * out_ld * 2);
+    const int voff = (rr * out_ld + cq * 8) * 2;
+    const u32x4* src = st + rr * LPR + cq;
+    constexpr int NI = MTA * 32 / RPI;  // read-backs, in groups of up to 8 (reads, then stores)
+    static_for<(NI + 7) / 8>([&](auto gi) {
+      constexpr int i0 = gi() * 8, NG = NI - i0 < 8 ? NI - i0 : 8;
+      u32x4 v[NG];
+      static_for<NG>([&](auto j) { v[j()] = src[(i0 + j()) * RPI * LPR]; });
+      static_for<NG>([&](auto j) {
+        __builtin_amdgcn_raw_buffer_store_b128(v[j()], ors, voff, (i0 + j()) * RPI * out_ld * 2, 0);
+      });
+    });
+  }
+  __syncthreads();
 }
 
 template <int MODE>
@@ -1553,7 +1614,8 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm256_kernel(const uint16_t* __r
       // next unit's copies wait for this unit's last LDS reads
       wait_vmcnt<0>();
       barrier();
-      if (wact) gemm_epilogue_mt<MODE, WDT, MTA>(acc, MTA, e, m0, mend, col0, hf, l32, s0, s1, out, out_ld);
+      u32x4* est = wv == 0 ? g2_lds0 : wv == 1 ? g2_lds1 : wv == 2 ? g2_lds2 : g2_lds3;
+      g2_epilogue<MODE, MTA>(acc, est, wact, e, m0, mend, col0, lane, s0, s1, out, out_ld);
     };
     switch (mt_act) {
       case 1: unit(std::integral_constant<int, 1>{}); break;
