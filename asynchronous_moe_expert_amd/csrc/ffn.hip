@@ -1248,9 +1248,10 @@ struct G2Table {
 
 __device__ __forceinline__ void g2_table_build(G2Table& tb, const int32_t* __restrict__ offsets, int E_loc,
                                                int n_rows, int lane) {
-  int base = 0, pt[4];
+  int base = 0, pt[4] = {0, 0, 0, 0};
   static_for<4>([&](auto jc) {
     constexpr int j = jc();
+    if (j > 0 && 64 * j >= E_loc) return;  // (no expert in this group of 64)
     const int e = lane + 64 * j;
     int lo = 0, hi = 0;
     if (e < E_loc) {  // clamped to [0, n_rows]: inconsistent offsets never address past the batch
@@ -1278,6 +1279,7 @@ __device__ __forceinline__ void g2_table_build(G2Table& tb, const int32_t* __res
   for (int t = kG2MT; t >= 1; --t) {
     static_for<4>([&](auto jc) {
       constexpr int j = jc();
+      if (j > 0 && 64 * j >= E_loc) return;
       const uint64_t bal = __ballot(pt[j] == t);
       if (pt[j] == t) {
         tb.pe[pos + __popcll(bal & below)] = lane + 64 * j;
@@ -1339,17 +1341,17 @@ __device__ __forceinline__ void gemm_epilogue_mt(const f32x16 (&acc)[MTT][2], in
 // the k-loop's last barrier has passed, reads it back row by row and stores 16 bytes per lane
 // (down: 8 rows of 128 B per instruction, gate/up: 16 rows of 64 B) through a buffer resource
 // that ends at the chunk's last row, so the stores of rows past it are dropped without a
-// branch.  Every per-lane value is derived here: left to the compiler, the row addresses were
-// computed ahead of the contraction and kept in scratch across it, and each reload's wait for
-// the memory counter then also waited for the stores issued before it (2-byte stores straight
+// branch.  sc0, sc1: the lane's fp8 row scales (loaded ahead of the contraction).  Every
+// per-lane address is derived here: left to the compiler, the row addresses were computed
+// ahead of the contraction and kept in scratch across it, and each reload's wait for the
+// memory counter then also waited for the stores issued before it (2-byte stores straight
 // from the MFMA layout took ~2 us per 32-row tile this way, 13-17 us of an 8-tile unit).  The
 // barrier after the read-back keeps the next unit's copies out of the stages until every wave
 // has read its tile.
 template <int MODE, int MTA>
-__device__ __forceinline__ void g2_epilogue(const f32x16 (&acc)[MTA][2], u32x4* st, bool wact, int e, int m0,
-                                           int mend, int col0, int lane_in, const float* __restrict__ s0,
-                                           const float* __restrict__ s1, uint16_t* __restrict__ out,
-                                           int out_ld) {
+__device__ __forceinline__ void g2_epilogue(const f32x16 (&acc)[MTA][2], u32x4* st, bool wact, int m0, int mend,
+                                           int col0, int lane_in, float sc0, float sc1,
+                                           uint16_t* __restrict__ out, int out_ld) {
   constexpr int CW = MODE == 0 ? 32 : 64;  // output columns of a wave
   constexpr int LPR = CW * 2 / 16;         // lanes per row on the read-back (16 bytes each)
   constexpr int RPI = 64 / LPR;            // rows per read-back instruction
@@ -1357,8 +1359,6 @@ __device__ __forceinline__ void g2_epilogue(const f32x16 (&acc)[MTA][2], u32x4* 
   asm volatile("" : "+v"(lane));
   const int l32 = lane & 31, hf = lane >> 5;
   if (wact) {
-    float sc0, sc1;
-    gemm_scales<MODE, MOE_FP8_E4M3>(e, col0, l32, s0, s1, out_ld, sc0, sc1);
     uint16_t* t16 = reinterpret_cast<uint16_t*>(st) + 4 * hf * CW + l32;
     static_for<MTA>([&](auto mt) {
       static_for<4>([&](auto g) {
@@ -1475,6 +1475,9 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm256_kernel(const uint16_t* __r
     const int col0 = nb * kGemmBN + wv * kGemmWaveN;
     const bool wact = col0 < Nw;       // the last column block may be partial
     const int colw = wact ? col0 : 0;  // idle waves stream valid weights (results unused)
+    // the epilogue's fp8 row scales, loaded ahead of the contraction (idle waves: valid ones)
+    float sc0, sc1;
+    gemm_scales<MODE, WDT>(e, colw, l32, s0, s1, out_ld, sc0, sc1);
     const __amdgpu_buffer_rsrc_t wrs = buffer_rsrc(W + (int64_t)e * Nw * Kd, (int64_t)Nw * Kd);
     const int w_end = Nw * Kd;  // (the host keeps an expert's matrix under 2^30 bytes)
     int wvo[2];
@@ -1615,7 +1618,7 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm256_kernel(const uint16_t* __r
       wait_vmcnt<0>();
       barrier();
       u32x4* est = wv == 0 ? g2_lds0 : wv == 1 ? g2_lds1 : wv == 2 ? g2_lds2 : g2_lds3;
-      g2_epilogue<MODE, MTA>(acc, est, wact, e, m0, mend, col0, lane, s0, s1, out, out_ld);
+      g2_epilogue<MODE, MTA>(acc, est, wact, m0, mend, col0, lane, sc0, sc1, out, out_ld);
     };
     switch (mt_act) {
       case 1: unit(std::integral_constant<int, 1>{}); break;
