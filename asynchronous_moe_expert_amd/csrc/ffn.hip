@@ -745,10 +745,12 @@ template <>
 struct GemmW<MOE_FP8_E4M3> {
   static constexpr int kLoads = 4;
   u32x4 raw[2][2];  // [tile][piece]: piece p holds k = 32hf + 16p + 0..15 of the lane's column
+  // AUX: the loads' cache policy (2: non-temporal, for weights read once per launch)
+  template <int AUX = 0>
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t w, const int* voff, int soff) {
     static_for<2>([&](auto t) {
-      raw[t()][0] = __builtin_amdgcn_raw_buffer_load_b128(w, voff[t()], soff, 0);
-      raw[t()][1] = __builtin_amdgcn_raw_buffer_load_b128(w, voff[t()] + 256, soff, 0);
+      raw[t()][0] = __builtin_amdgcn_raw_buffer_load_b128(w, voff[t()], soff, AUX);
+      raw[t()][1] = __builtin_amdgcn_raw_buffer_load_b128(w, voff[t()] + 256, soff, AUX);
     });
   }
   __device__ __forceinline__ bf16x8 frag(int t, int s) const {
@@ -1497,7 +1499,7 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm256_kernel(const uint16_t* __r
     // instantiated for MTA = 1..8, so that a chunk of few rows copies, reads and multiplies only
     // its tiles, without per-tile branches inside the loop (rounding to 64 rows instead executed
     // 6-11% more rows on prefill waves of 3277-6554 pairs: gate/up 2-5% slower).
-    auto unit = [&](auto mta) {
+    auto unit = [&](auto mta, auto nt) {
       constexpr int MTA = mta();
       // activation copies: instruction d of this wave fills the 16-byte slots (4 d + wv) * 64 +
       // lane of a stage; slot P holds row P / 8, piece (P % 8) ^ ((P / 8 >> 1) & 7) of that row
@@ -1522,7 +1524,9 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm256_kernel(const uint16_t* __r
       };
       // weights of k-step ks; past the contraction the offset lies beyond the expert's matrix,
       // where buffer loads return zeros, so those steps' MFMAs add nothing
-      auto issue_w = [&](auto slot, int ks) { wr[slot()].load(wrs, wvo, ks < KS ? ks * 1024 : w_end); };
+      auto issue_w = [&](auto slot, int ks) {
+        wr[slot()].template load<nt() ? 2 : 0>(wrs, wvo, ks < KS ? ks * 1024 : w_end);
+      };
       auto read = [&](auto stg, auto ss, auto buf) {  // fragments of k-slice ss
         const u32x4* tile = stage(stg);
         static_for<MTA>([&](auto mt) { af[buf()][mt()] = tile[mt() * 256 + lds_off[ss()]]; });
@@ -1620,16 +1624,24 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm256_kernel(const uint16_t* __r
       u32x4* est = wv == 0 ? g2_lds0 : wv == 1 ? g2_lds1 : wv == 2 ? g2_lds2 : g2_lds3;
       g2_epilogue<MODE, MTA>(acc, est, wact, m0, mend, col0, lane, sc0, sc1, out, out_ld);
     };
-    switch (mt_act) {
-      case 1: unit(std::integral_constant<int, 1>{}); break;
-      case 2: unit(std::integral_constant<int, 2>{}); break;
-      case 3: unit(std::integral_constant<int, 3>{}); break;
-      case 4: unit(std::integral_constant<int, 4>{}); break;
-      case 5: unit(std::integral_constant<int, 5>{}); break;
-      case 6: unit(std::integral_constant<int, 6>{}); break;
-      case 7: unit(std::integral_constant<int, 7>{}); break;
-      default: unit(std::integral_constant<int, 8>{}); break;
-    }
+    // an expert of a single chunk has its weight tiles read by one unit each in this launch:
+    // they are loaded non-temporally, so that they do not displace the activation rows the
+    // chunk's other column blocks read through the same L2
+    const bool once = q >= tab.F && tab.nf[e] == 0;
+    auto run = [&](auto nt) {
+      switch (mt_act) {
+        case 1: unit(std::integral_constant<int, 1>{}, nt); break;
+        case 2: unit(std::integral_constant<int, 2>{}, nt); break;
+        case 3: unit(std::integral_constant<int, 3>{}, nt); break;
+        case 4: unit(std::integral_constant<int, 4>{}, nt); break;
+        case 5: unit(std::integral_constant<int, 5>{}, nt); break;
+        case 6: unit(std::integral_constant<int, 6>{}, nt); break;
+        case 7: unit(std::integral_constant<int, 7>{}, nt); break;
+        default: unit(std::integral_constant<int, 8>{}, nt); break;
+      }
+    };
+    if (once) run(std::true_type{});
+    else run(std::false_type{});
   }
 }
 
