@@ -27,8 +27,9 @@
 //     sums are exact dot products over all k.
 //   * fp8 e4m3 weights are widened to bf16 in registers (exact: every e4m3 value is a
 //     bf16 value) and the per-row scale is applied to the fp32 result in the epilogue.
-//   * Units are spread XCD-aware: each XCD gets an equal contiguous range of unit ids, so
-//     the chunks that share a weight tile run on one XCD's L2 (reuse for big experts).
+//   * Units are spread XCD-aware: each XCD gets an equal contiguous range of unit ids,
+//     numbered chunk-major, so a chunk's column blocks run on one XCD and read its rows
+//     through that XCD's L2.
 #include <hip/hip_ext.h>
 
 #include <algorithm>
@@ -364,6 +365,9 @@ struct ChunkTable {
     int base = 0;
     static_for<4>([&](auto jc) {
       constexpr int j = jc();
+      a0[j] = a1[j] = nc[j] = 0;
+      start[j] = base;
+      if (j > 0 && 64 * j >= E_loc) return;  // (no expert in this group of 64)
       const int e = lane + 64 * j;
       int lo = 0, hi = 0;
       if (e < E_loc) {
@@ -419,15 +423,16 @@ __device__ __forceinline__ void wg_barrier() {
 constexpr int kFfnWaves = 4;
 
 // expert (or -1), column block and rows of unit u of the batch, when u < u_end.  Units are
-// numbered column-block-major (u = nb * total + chunk).
+// numbered chunk-major (u = chunk * n_blocks_N + nb).
 __device__ __forceinline__ int next_unit(const int32_t* __restrict__ offsets, int E_loc, int n_rows, int BM, int lane,
-                                         int u, int u_end, int total, int& nb, int& m0, int& mend, int& nce) {
+                                         int u, int u_end, int n_blocks_N, int& nb, int& m0, int& mend, int& nce) {
   int e = -1;
   if (u < u_end) {
     ChunkTable tab;
     tab.build(offsets, E_loc, n_rows, BM, lane);
-    nb = u / total;
-    tab.find(u - nb * total, BM, e, m0, mend, nce);
+    const int c = u / n_blocks_N;
+    nb = u - c * n_blocks_N;
+    tab.find(c, BM, e, m0, mend, nce);
   }
   return e;
 }
@@ -496,10 +501,13 @@ __global__ __launch_bounds__(64 * WV) void ffn_mfma_kernel(const uint16_t* __res
   }
 
   // XCD-aware order: physical workgroup b runs on XCD b % 8.  Each XCD gets an equal,
-  // contiguous range of unit ids (so the chunks that share a weight tile run on one XCD's
-  // L2), and its G/8 workgroups stride through that range.  The chunk table is built once
-  // for the first unit and again for each later one, so that it holds no registers across
-  // the contraction.
+  // contiguous range of unit ids, numbered chunk-major, and its G/8 workgroups stride through
+  // that range: a chunk's column blocks share its activation rows in the XCD's L2.  (Numbered
+  // column-block-major instead, so that an expert's chunks shared each weight strip, the
+  // prefill wave of 1638 pairs ran its gate/up 10 us slower: the rows are re-read by every
+  // column block, the strips only by a big expert's few chunks, and the strips of single-chunk
+  // experts are loaded non-temporally.)  The chunk table is built once for the first unit and
+  // again for each later one, so that it holds no registers across the contraction.
   const int G = (int)gridDim.x - (with_plan || FQ ? 1 : 0), b = blockIdx.x, xcd = b & 7;
   int total, u, u_end, nb = 0, e = -1, m0 = 0, mend = 0, nce = 0;
   {
@@ -510,12 +518,13 @@ __global__ __launch_bounds__(64 * WV) void ffn_mfma_kernel(const uint16_t* __res
     u = (int)((int64_t)U * xcd / 8) + (b >> 3);
     u_end = (int)((int64_t)U * (xcd + 1) / 8);
     if (u < u_end) {
-      nb = u / total;
-      tab.find(u - nb * total, BM, e, m0, mend, nce);
+      const int c = u / n_blocks_N;
+      nb = u - c * n_blocks_N;
+      tab.find(c, BM, e, m0, mend, nce);
     }
   }
   for (; u < u_end;
-       u += G >> 3, e = next_unit(offsets, E_loc, n_rows, BM, lane, u, u_end, total, nb, m0, mend, nce)) {
+       u += G >> 3, e = next_unit(offsets, E_loc, n_rows, BM, lane, u, u_end, n_blocks_N, nb, m0, mend, nce)) {
     if (e < 0) break;  // not reachable: the table is the same on every build
     const int strip0 = (nb * WV + wv) * NS;  // this wave's first strip
     const bool wact = strip0 < n_strips;            // (the last block may be partial)
