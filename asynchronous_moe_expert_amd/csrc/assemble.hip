@@ -16,6 +16,7 @@
 //      that consecutive lanes copy consecutive bytes of a row (fully coalesced reads of each
 //      pool row and writes of each batch row).
 #include "common.hpp"
+#include "combine_link.hpp"
 
 namespace moe {
 
@@ -175,10 +176,13 @@ __global__ __launch_bounds__(kAsmThreads) void assemble_index_kernel(
 // instead of 7.4 us at 16384).
 constexpr int kIdxT = 1024;    // threads per workgroup = pairs per segment
 constexpr int kIdxCopies = 4;  // LDS counters per expert
+// link (m > 0): the combine's link step for the queue's own arrivals (arrival i = pair i, its
+// batch row the pos[i] derived here): the arrival's metadata is loaded with the first keys, its
+// token's state after the count, and the push made once the row is known.
 __global__ __launch_bounds__(kIdxT) void assemble_index_multi_kernel(
     int n, const int32_t* __restrict__ slot, const int32_t* __restrict__ expert, int base, int E_loc, int64_t P,
     int32_t* __restrict__ perm, int32_t* __restrict__ pos, int32_t* __restrict__ row_slot,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, uint32_t* __restrict__ err) {
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, uint32_t* __restrict__ err, LinkJob link) {
   constexpr int kT = kIdxT, kWaves = kT / kWave, kC = kIdxCopies, kCS = kC + 1;
   __shared__ int s_bef[kMaxElocAsm * kCS];  // keys before this segment: expert e, copy c at e * kCS + c
   __shared__ int s_aft[kMaxElocAsm * kCS];  // keys from this segment on
@@ -195,6 +199,9 @@ __global__ __launch_bounds__(kIdxT) void assemble_index_multi_kernel(
   for (int x = tid; x < kWaves * E_loc; x += kT) s_wcnt[x / E_loc][x % E_loc] = 0;
   if (tid == 0) s_err = 0u;
   __syncthreads();
+  const bool linking = link.m > 0 && seg0 + tid < link.m;
+  LinkIn la;
+  if (linking) la = link_load_meta(link, seg0 + tid);
   // every key (validated) in batches of kU chunks whose ids are loaded before any is counted
   constexpr int kU = 8;
   const int cp = lane % kC;
@@ -225,6 +232,7 @@ __global__ __launch_bounds__(kIdxT) void assemble_index_multi_kernel(
     }
   }
   if (blockIdx.x == 0 && myerr) atomicOr(&s_err, myerr);
+  if (linking) link_load_state(link, la);
   __syncthreads();
   // wave 0: exclusive scan of the counts (4 experts per lane covers E_loc <= 256)
   if (wv == 0) {
@@ -292,14 +300,17 @@ __global__ __launch_bounds__(kIdxT) void assemble_index_multi_kernel(
     }
   }
   __syncthreads();
+  int my_row = -1;
   if (my_key < kMaxElocAsm) {
     const int r = s_wcnt[wv][my_key] + rank;
+    my_row = r;
     perm[r] = i;
     if (pos) pos[i] = r;
     if (row_slot) row_slot[r] = my_slot;
   } else if (i < n && pos) {
     pos[i] = -1;
   }
+  if (linking) link_push(link, i, my_row, la);
   // rows past the accepted pairs, split over the workgroups by segment
   const int total = s_total;
   if (i < n && i >= total) {
@@ -344,9 +355,9 @@ int moe::check_assemble_args(const moe_assemble_args* a) {
   return MOE_OK;
 }
 
-extern "C" int moe_assemble(const moe_assemble_args* a, hipStream_t stream) {
-  const int rc = check_assemble_args(a);
-  if (rc != MOE_OK) return rc;
+// moe_assemble's launches (arguments already checked); link.m > 0 only with the multi-segment
+// index kernel (n > kIdxT)
+static int assemble_launch(const moe_assemble_args* a, const LinkJob& link, hipStream_t stream) {
   const int esz = dtype_size(a->act_dtype);
   const int row_bytes = a->H * esz;
   const int64_t pitch_bytes = a->pool_pitch * esz;
@@ -359,7 +370,7 @@ extern "C" int moe_assemble(const moe_assemble_args* a, hipStream_t stream) {
   else
     hipLaunchKernelGGL(assemble_index_multi_kernel, dim3((unsigned)((a->n + kIdxT - 1) / kIdxT)), dim3(kIdxT), 0, stream,
                        a->n, a->slot, a->expert, a->expert_base, a->E_loc, a->P, a->perm, a->pos, a->row_slot,
-                       a->counts, a->offsets, a->err);
+                       a->counts, a->offsets, a->err, link);
   if (a->n == 0 || !a->xb) return launch_status();  // no xb: the FFN gathers on load
   const int cpr = row_bytes / 16;
   const int64_t work = (int64_t)a->n * cpr;
@@ -368,4 +379,19 @@ extern "C" int moe_assemble(const moe_assemble_args* a, hipStream_t stream) {
   hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a->perm, a->slot,
                      a->offsets + a->E_loc, (const char*)a->pool, pitch_bytes, (char*)a->xb, row_bytes, cpr);
   return launch_status();
+}
+
+extern "C" int moe_assemble(const moe_assemble_args* a, hipStream_t stream) {
+  const int rc = check_assemble_args(a);
+  if (rc != MOE_OK) return rc;
+  return assemble_launch(a, LinkJob{}, stream);
+}
+
+bool moe::assemble_links(int n) { return n > kIdxT; }
+
+int moe::assemble_with_link(const moe_assemble_args* a, const LinkJob& link, hipStream_t stream) {
+  const int rc = check_assemble_args(a);
+  if (rc != MOE_OK) return rc;
+  if (!assemble_links(a->n) || link.m != a->n || !a->pos) return MOE_EINVAL_SIZE;
+  return assemble_launch(a, link, stream);
 }

@@ -90,37 +90,15 @@ constexpr int kMaxChain = 64;  // arrivals of one token handled per pass of the 
 constexpr int kMergeVec = 4;   // 8-element vectors per thread loaded in one batch (rows up to 8192 wide)
 constexpr int kRowBatch = 4;   // result rows of one token loaded before they are summed (list and plan paths)
 
-// Kernel 1: one thread per arrival.  Range and generation checks, then a push onto the
-// token's arrival list (head[t] = newest arrival, next[i] = the one pushed before it).
-__global__ __launch_bounds__(256) void combine_link_kernel(int m, int K, int64_t n_rows,
-                                                           const int32_t* __restrict__ row_idx,
-                                                           const int32_t* __restrict__ tok,
-                                                           const int32_t* __restrict__ kslot,
-                                                           const uint32_t* __restrict__ gen,
-                                                           const uint32_t* __restrict__ tgen,
-                                                           const uint32_t* __restrict__ mask, int T_cap,
-                                                           int32_t* __restrict__ head, int32_t* __restrict__ next,
-                                                           uint32_t* __restrict__ mpre, uint32_t* __restrict__ err) {
+// Kernel 1: one thread per arrival: the link step (combine_link.hpp) with the arrival's batch
+// row from row_idx.
+__global__ __launch_bounds__(256) void combine_link_kernel(LinkJob j, const int32_t* __restrict__ row_idx) {
   const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= m) return;
-  const int t = tok[i], j = kslot[i];
+  if (i >= j.m) return;
+  LinkIn a = link_load_meta(j, i);
   const int64_t r = row_idx[i];
-  unsigned flag = 0u;
-  if (t < 0 || t >= T_cap) flag |= MOE_ERR_TOKEN_RANGE;
-  if (j < 0 || j >= K) flag |= MOE_ERR_KSLOT_RANGE;
-  if (r < 0 || r >= n_rows) flag |= MOE_ERR_ROW_RANGE;
-  uint32_t m_t = 0u;
-  if (!flag) {
-    m_t = mask[t];  // (fetched with the generation; no kernel of this call has changed it yet)
-    if (gen[i] != tgen[t]) flag |= MOE_ERR_STALE_GEN;
-  }
-  if (flag) {
-    atomicOr(err, flag);
-    next[i] = -2;  // not linked
-    return;
-  }
-  mpre[i] = m_t;
-  next[i] = atomicExch(&head[t], i);
+  link_load_state(j, a);
+  link_push(j, i, r, a);
 }
 
 // Kernel 2: one workgroup per arrival; the workgroup of the token's first pushed arrival (the
@@ -634,6 +612,34 @@ static PlanJob make_plan_job(const moe_combine_args* a) {
   return j;
 }
 
+// the list path's link step: next[m] and mpre[m] at the start of the workspace
+static LinkJob make_link_job(const moe_combine_args* a) {
+  const moe_combine_state& s = a->state;
+  LinkJob j;
+  j.m = a->m;
+  j.K = a->K;
+  j.T_cap = s.T_cap;
+  j.n_rows = a->n_rows;
+  j.tok = a->tok;
+  j.kslot = a->kslot;
+  j.gen = a->gen;
+  j.tgen = s.tgen;
+  j.mask = s.mask;
+  j.head = s.head;
+  j.next = (int32_t*)a->workspace;
+  j.mpre = (uint32_t*)a->workspace + a->m;
+  j.err = a->err;
+  return j;
+}
+
+int moe::combine_link_job(const moe_combine_args* a, LinkJob* job) {
+  const int rc = check_combine(a);
+  if (rc != MOE_OK) return rc;
+  *job = LinkJob{};
+  if (a->m > 0 && !plan_path(a)) *job = make_link_job(a);
+  return MOE_OK;
+}
+
 int moe::combine_plan_job(const moe_combine_args* a, PlanJob* job) {
   const int rc = check_combine(a);
   if (rc != MOE_OK) return rc;
@@ -653,9 +659,8 @@ extern "C" int moe_combine_plan(const moe_combine_args* a, hipStream_t stream) {
     else
       hipLaunchKernelGGL(combine_plan_kernel<kPlanThreads>, dim3(1), dim3(kPlanThreads), 0, stream, job);
   } else if (a->m > 0) {
-    hipLaunchKernelGGL(combine_link_kernel, dim3((unsigned)((a->m + 255) / 256)), dim3(256), 0, stream, a->m, a->K,
-                       a->n_rows, a->row_idx, a->tok, a->kslot, a->gen, s.tgen, s.mask, s.T_cap, s.head,
-                       (int32_t*)a->workspace, (uint32_t*)a->workspace + a->m, a->err);
+    hipLaunchKernelGGL(combine_link_kernel, dim3((unsigned)((a->m + 255) / 256)), dim3(256), 0, stream,
+                       make_link_job(a), a->row_idx);
   }
   return launch_status();
 }

@@ -8,6 +8,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "combine_link.hpp"
 
 namespace moe {
 

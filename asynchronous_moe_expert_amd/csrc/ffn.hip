@@ -1915,11 +1915,20 @@ extern "C" int moe_expert_ffn_grouped(const moe_ffn_args* a, hipStream_t stream)
   // the plan reads its pos)
   const bool streaming = !f32 && !takes_gemm(n, E, H, 2 * I, f8 ? 1 : 2, gr);
   QueueIdx qi{};
+  bool linked = false;  // the plan's link step ran in the index launch
   if (ix && streaming && n <= kQueueFusedMax) {
     qi = QueueIdx{ix->slot, ix->expert, ix->expert_base, n, ix->P, ix->perm, ix->pos,
                   ix->counts, ix->offsets, ix->row_slot, ix->err};
   } else if (ix) {
-    const int rc = moe_assemble(ix, stream);
+    // the index kernel of a longer queue also links the arrivals of a list-path plan over its
+    // own batch rows (the combine's link step), instead of a launch of their own
+    LinkJob lj{};
+    if (a->plan && a->plan->row_idx == ix->pos && a->plan->m == ix->n && assemble_links(ix->n)) {
+      const int rc = combine_link_job(a->plan, &lj);
+      if (rc != MOE_OK) return rc;
+    }
+    linked = lj.m > 0;
+    const int rc = linked ? assemble_with_link(ix, lj, stream) : moe_assemble(ix, stream);
     if (rc != MOE_OK) return rc;
   }
   if (!streaming) job.m = 0;
@@ -1927,7 +1936,7 @@ extern "C" int moe_expert_ffn_grouped(const moe_ffn_args* a, hipStream_t stream)
   // only a plan over the index's own pos joins it)
   if (qi.slot && a->plan && a->plan->row_idx != ix->pos) job.m = 0;
   const bool plan_after_gu = a->plan && qi.slot && job.m == 0;
-  if (a->plan && job.m == 0 && !plan_after_gu) {
+  if (a->plan && job.m == 0 && !plan_after_gu && !linked) {
     const int rc = moe_combine_plan(a->plan, stream);
     if (rc != MOE_OK) return rc;
   }

@@ -6,6 +6,8 @@
 #include <cstdlib>
 #include <string>
 
+#include "combine_link.hpp"  // the link step the link kernel runs (namespace moe)
+
 namespace moe {
 #include "combine_kernels.inc"  // the kernels, cut from combine.hip by the test
 }
@@ -62,9 +64,21 @@ int main(int argc, char** argv) {
     uint32_t* g = rd<uint32_t>(dir, p + "gen", m);
     // the list path's workspace: next[m], then the tokens' masks before the call
     int32_t* ws = (int32_t*)std::malloc((size_t)m * 8 + 16);
-    run_grid((m + 255) / 256, 256, [&] {
-      combine_link_kernel(m, K, n_rows, ri, tk, ks, g, tgen, mask, T_cap, head, ws, (uint32_t*)ws + m, &err);
-    });
+    LinkJob lj;
+    lj.m = m;
+    lj.K = K;
+    lj.T_cap = T_cap;
+    lj.n_rows = n_rows;
+    lj.tok = tk;
+    lj.kslot = ks;
+    lj.gen = g;
+    lj.tgen = tgen;
+    lj.mask = mask;
+    lj.head = head;
+    lj.next = ws;
+    lj.mpre = (uint32_t*)ws + m;
+    lj.err = &err;
+    run_grid((m + 255) / 256, 256, [&] { combine_link_kernel(lj, ri); });
     auto merge = [&](auto vc) {
       constexpr int V = decltype(vc)::value;
       run_grid(m, kMergeThreads, [&] {

@@ -466,6 +466,50 @@ def test_fused_plan_matches_separate_plan():
         assert np.array_equal(f["acc"].view(np.uint32), u["acc"].view(np.uint32))
 
 
+def test_linked_index_matches_separate_link(c4_ref):
+    """Queues of more than 1024 pairs: the index launch that also links the call's arrivals
+    (the combine's link step; ExpertStep with the plan in the FFN call) gives the same bits as
+    the link launched on its own (the step without a fused plan), with stale generations,
+    repeated positions and rejected queue entries: release list and count, error word, masks,
+    generations, held partial sums and the combined rows."""
+    s, _ = c4_ref
+    b = W.c4_wave(s, 3)  # 1638 pairs, each token's seven remote results delivered first
+    _say(f"linked index: {b.n} pairs")
+    wt = weight_tensors(s.weights)
+    d = batch_tensors(b)
+    rng = np.random.default_rng(11)
+    bad = rng.choice(b.n, 12, replace=False)
+    gen, ks, slot = b.gen.copy(), b.kslot.copy(), b.slot.copy()
+    gen[bad[:4]] += 1                          # stale generation
+    ks[bad[4:8]] = (ks[bad[4:8]] + 1) % b.K    # a position the token already holds (remote)
+    slot[bad[8:]] = -1                          # rejected by the index: no batch row
+    d["gen"], d["kslot"], d["slot"] = dev(gen.astype(np.uint32)), dev(ks.astype(np.int32)), dev(slot.astype(np.int32))
+    res = []
+    for fuse in (True, False):
+        st = M.ExpertStep(b.E_loc, b.H, s.weights.I, b.K, M.MOE_BF16, M.MOE_FP8_E4M3, b.n, b.T, fuse_plan=fuse)
+        st.load_weights(wt["wg"], wt["wu"], wt["wd"], wt["s_gate"], wt["s_up"], wt["s_down"])
+        st.combine(d["r_rows"], d["r_idx"], d["r_tok"], d["r_kslot"], d["r_w"], d["r_gen"])
+        st.run(d["slot"], d["expert"], b.expert_base, d["pool"], d["tok"], d["kslot"], d["w"], d["gen"])
+        torch.cuda.synchronize()
+        cnt = int(st.rel_count.item())
+        mask = st.state.mask.cpu().numpy()
+        held = np.flatnonzero(mask)
+        res.append(dict(err=int(st.err.item()), cnt=cnt, rel=st.rel_list[:cnt].cpu().numpy(), mask=mask,
+                        tgen=st.state.tgen.cpu().numpy(), out=to_numpy_bits(st.out), held=held,
+                        acc=st.state.acc[torch.as_tensor(held, device="cuda").long()].cpu().numpy(),
+                        pos=st.pos[: b.n].cpu().numpy()))
+        del st
+    f, u = res
+    want = M.ERR_STALE_GEN | M.ERR_DUPLICATE | M.ERR_SLOT_RANGE | M.ERR_ROW_RANGE
+    assert f["err"] == u["err"] and (f["err"] & want) == want, (hex(f["err"]), hex(u["err"]))
+    assert np.array_equal(f["pos"], u["pos"]) and (f["pos"][bad[8:]] == -1).all()
+    assert f["cnt"] == u["cnt"] and np.array_equal(f["rel"], u["rel"]) and 0 < f["cnt"] < b.n
+    assert np.array_equal(f["mask"], u["mask"]) and np.array_equal(f["tgen"], u["tgen"])
+    assert np.array_equal(f["out"], u["out"])
+    assert np.array_equal(f["held"], u["held"]) and len(f["held"]) > 0
+    assert np.array_equal(f["acc"].view(np.uint32), u["acc"].view(np.uint32))
+
+
 @pytest.fixture(scope="module")
 def c4_ref():
     """The prefill setup and the oracle's FFN output of every one of its 16384 tokens
