@@ -524,7 +524,9 @@ def run_prefill(args) -> dict:
                   "note": "the same K steps captured as one HIP graph and replayed once"},
         "waves": per_wave,
         "note": "value: K steps timed back to back (step s = wave s mod 4, its remote results delivered before "
-                "the timed region); waves[].us: per-stage medians of HIP-event intervals, each step alone; "
+                "the timed region; each step's queue index also links its arrivals for the combine, in one "
+                "launch); waves[].us: per-stage medians of HIP-event intervals, each step alone (there the index "
+                "is timed on its own as assemble and the combine's link step runs at the start of gate_up); "
                 "gate_up_kernel and roofline.kernel_us: the gate/up projection alone, from events its dispatch "
                 "records; combine_cold: the combine after a 512 MiB write and two read passes over it (caches "
                 "hold clean lines of another buffer); combine_cold_dirty: after the write alone (every miss then "
