@@ -161,6 +161,7 @@ class StepRunner:
         self.base = b0.expert_base
         comp = [_compact(b) for b in batches]
         self.T_step = max(c[2] for c in comp)
+        n_steps = max(n_steps, len(batches))  # (the per-stage pass runs each batch once)
         self.n_steps = n_steps
         n_max = max(b.n for b in batches)
         self.st = M.ExpertStep(self.E, self.H, self.I, self.K, act_code, w_code, n_max, n_steps * self.T_step)
