@@ -8,11 +8,13 @@
 //   * Two launches: gate/up GEMM with the SwiGLU epilogue (writes h), then the down GEMM.
 //   * Decode-sized batches (streaming kernel below): work unit = (row chunk of <= 48 rows of
 //     one expert, WV waves x NS weight strips of 16 output columns).  Prefill-sized batches
-//     (>= 96 rows per expert on average) take the tiled GEMM kernel further down (128-row
-//     chunks x 256 columns).  The chunk list is derived on the device from `offsets`, so ragged
-//     and empty experts need no host round trip.  The grid is what the device holds at
-//     once (CUs x occupancy) and strides over the active units only: a decode batch's
-//     units all start in the first round and no workgroup slot is spent on an idle unit.
+//     (>= 96 rows per expert on average; the fp8 down projection from 48) take a tiled GEMM
+//     further down: units of 256 rows x 256 columns, one workgroup per CU, for fp8 weights;
+//     128-row chunks x 256 columns for bf16 weights.  The chunk list is derived on the device
+//     from `offsets`, so ragged and empty experts need no host round trip.  The streaming
+//     kernel's grid is what the device holds at once (CUs x occupancy) and strides over the
+//     active units only: a decode batch's units all start in the first round and no
+//     workgroup slot is spent on an idle unit.
 //   * At decode sizes (tens of rows per expert) the step is bound by streaming the expert
 //     weights once from HBM.  Each wave owns its strips over the whole contraction and
 //     keeps R-1 k-steps of weight loads in flight in a register ring (packed layout: one
@@ -1324,27 +1326,6 @@ __device__ __forceinline__ void g2_find(const G2Table& tb, int q, int& e, int& m
     m0 = tb.a0[e] + tb.nf[e] * kG2BM;
     mend = tb.a1[e];
   }
-}
-
-template <int MODE, int WDT, int MTT>
-__device__ __forceinline__ void gemm_epilogue_mt(const f32x16 (&acc)[MTT][2], int mt_act, int e, int m0, int mend,
-                                                 int col0, int hf, int l32, const float* __restrict__ s0,
-                                                 const float* __restrict__ s1, uint16_t* __restrict__ out,
-                                                 int out_ld) {
-  float sc0, sc1;
-  gemm_scales<MODE, WDT>(e, col0, l32, s0, s1, out_ld, sc0, sc1);
-  static_for<MTT>([&](auto mt) {
-    if (mt() < mt_act) {
-      static_for<4>([&](auto g) {
-        float a[4], b[4];
-        static_for<4>([&](auto k) {
-          a[k()] = acc[mt()][0][4 * g() + k()];
-          b[k()] = acc[mt()][1][4 * g() + k()];
-        });
-        gemm_store_group<MODE>(a, b, mt(), g(), m0, mend, col0, hf, l32, sc0, sc1, out, out_ld);
-      });
-    }
-  });
 }
 
 // Epilogue of a 256-row unit through LDS.  Each wave converts its tile (down: 256 rows x 64
