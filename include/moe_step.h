@@ -207,8 +207,12 @@ int moe_pack_ffn_weights(const moe_pack_args* args, hipStream_t stream);
  * regrouping among the costs that asynchrony adds); a plan given with it then runs in that
  * workgroup on the batch rows it derived (or, when the plan cannot join the launch, is
  * launched right after the gate/up kernel, as it reads pos).  Otherwise moe_assemble is
- * launched on the stream before the FFN.  Either way the outputs are complete when the down
- * projection starts. */
+ * launched on the stream before the FFN.  When that queue is longer than 1024 pairs and a plan
+ * for the same batch is given (its row_idx is the index's pos and its m the queue length, so the
+ * combine takes its linked-list path), the same launch also does the plan's link step (range
+ * and generation checks, then each arrival pushed onto its token's list once its batch row is
+ * known), with the same results, and the apply then runs only the merge and the release.
+ * Either way the outputs are complete when the down projection starts. */
 struct moe_combine_args;
 typedef struct moe_ffn_args {
   int32_t n, E_loc, H, I;
