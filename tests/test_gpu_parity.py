@@ -510,6 +510,89 @@ def test_linked_index_matches_separate_link(c4_ref):
     assert np.array_equal(f["acc"].view(np.uint32), u["acc"].view(np.uint32))
 
 
+LINK_CASES = [
+    # (n, E_loc, H, I, weight dtype): one pair past the first 1024-pair index workgroup, and
+    # three workgroups with a ragged last one
+    (1025, 8, 128, 64, "bf16"),
+    (2600, 8, 256, 128, "fp8"),
+]
+
+
+@pytest.mark.parametrize("case", LINK_CASES, ids=[f"n{c[0]}_{c[4]}" for c in LINK_CASES])
+def test_linked_index_multi_arrival_tokens(case):
+    """The index launch that links the call's arrivals, on queues where most tokens have two to
+    four arrivals in the call (the merge walks and sorts their lists) and a few have more than K
+    (repeated positions), with stale generations and rejected queue entries: the same bits as the
+    link launched on its own (index outputs, error word, release list, masks, generations, held
+    partial sums, released rows)."""
+    n, E, H, I, wdt = case
+    K, P = 4, 4096
+    T = n // 2
+    _say("linked index, multi-arrival tokens", case)
+    rng = np.random.default_rng(n + H)
+    wts = W.make_layer_weights(rng, E, H, I, 0.05, wdt)
+    wt = weight_tensors(wts)
+    pool = dev(W.to_bf16_bits(rng.standard_normal((P, H)).astype(np.float32)), "bf16")
+    slot = rng.integers(0, P, n).astype(np.int32)
+    expert = rng.integers(0, E, n).astype(np.int32)
+    tok = rng.integers(0, T, n).astype(np.int32)
+    # each token's arrivals take distinct positions from a random order; a fifth or later
+    # arrival repeats one (a duplicate)
+    kslot = np.zeros(n, np.int32)
+    seen = {}
+    for i in range(n):
+        order = seen.setdefault(int(tok[i]), list(rng.permutation(K)))
+        kslot[i] = order.pop(0) if order else int(rng.integers(0, K))
+    gen = np.zeros(n, np.uint32)
+    w = rng.standard_normal(n).astype(np.float32)
+    bad = rng.choice(n, 16, replace=False)
+    gen[bad[:8]] = 1          # stale generation
+    slot[bad[8:]] = -1        # rejected by the index: no batch row
+    per_tok = np.bincount(tok, minlength=T)
+    assert (per_tok >= 2).sum() > T // 3 and (per_tok >= K).any() and (per_tok > K).any()
+    codes = {"bf16": M.MOE_BF16, "fp8": M.MOE_FP8_E4M3}
+    d = dict(slot=dev(slot), expert=dev(expert), tok=dev(tok), kslot=dev(kslot), w=dev(w), gen=dev(gen))
+    res = []
+    for fuse in (True, False):
+        st = M.ExpertStep(E, H, I, K, M.MOE_BF16, codes[wdt], n, T, fuse_plan=fuse)
+        st.load_weights(wt["wg"], wt["wu"], wt["wd"], wt.get("s_gate"), wt.get("s_up"), wt.get("s_down"))
+        st.run(d["slot"], d["expert"], 0, pool, d["tok"], d["kslot"], d["w"], d["gen"])
+        torch.cuda.synchronize()
+        cnt = int(st.rel_count.item())
+        mask = st.state.mask.cpu().numpy()
+        held = np.flatnonzero(mask)
+        res.append(dict(err=int(st.err.item()), cnt=cnt, rel=st.rel_list[:cnt].cpu().numpy(), mask=mask,
+                        tgen=st.state.tgen.cpu().numpy(), out=to_numpy_bits(st.out), held=held,
+                        acc=st.state.acc[torch.as_tensor(held, device="cuda").long()].cpu().numpy(),
+                        pos=st.pos[:n].cpu().numpy(), perm=st.perm[:n].cpu().numpy(),
+                        offsets=st.offsets.cpu().numpy(), y=to_numpy_bits(st.y[:n])))
+        del st
+    f, u = res
+    want = M.ERR_STALE_GEN | M.ERR_DUPLICATE | M.ERR_SLOT_RANGE | M.ERR_ROW_RANGE
+    assert f["err"] == u["err"] and (f["err"] & want) == want, (hex(f["err"]), hex(u["err"]))
+    for k in ("pos", "perm", "offsets", "mask", "tgen", "held", "y"):
+        assert np.array_equal(f[k], u[k]), k
+    assert (f["pos"][bad[8:]] == -1).all()
+    assert f["cnt"] == u["cnt"] and np.array_equal(f["rel"], u["rel"]) and 0 < f["cnt"] < T
+    assert len(f["held"]) > 0
+    assert np.array_equal(f["acc"].view(np.uint32), u["acc"].view(np.uint32))
+    assert np.array_equal(f["out"], u["out"])
+    # against the oracle, on the GPU's FFN rows: its assemble gives the batch rows, its combine
+    # the acceptance, the release list, masks, generations and the error bits; released rows
+    # within bf16 rounding, held partial sums within fp32 rounding
+    a = O.assemble(slot, expert, 0, E, P)
+    assert np.array_equal(f["pos"], a["pos"]) and np.array_equal(f["offsets"], a["offsets"])
+    ocs = O.CombineState(T, K)
+    out, rel, oerr = O.combine_release(ocs, O.decode_bf16(f["y"]), a["pos"], tok, kslot, w, gen)
+    assert f["err"] == (a["err"] | oerr), (hex(f["err"]), hex(a["err"] | oerr))
+    assert np.array_equal(f["rel"], rel)
+    assert np.array_equal(f["mask"], ocs.mask) and np.array_equal(f["tgen"], ocs.tgen)
+    got = O.decode_bf16(f["out"][rel])
+    assert row_rel_err(got, np.stack([out[int(t)] for t in rel])) <= TOL["bf16"]
+    ref_held = np.stack([sum(ocs.parts[int(t)].values()) for t in f["held"]])
+    assert row_rel_err(f["acc"].astype(np.float64), ref_held) <= 1e-5
+
+
 @pytest.fixture(scope="module")
 def c4_ref():
     """The prefill setup and the oracle's FFN output of every one of its 16384 tokens
