@@ -860,6 +860,9 @@ GEMM256_CASES = [
     (3, 512, 256, [100, 170, 200]),
     # ... and more units than workgroups (18 chunks x 16 gate/up column blocks: two rounds)
     (2, 512, 2048, [3000, 1500]),
+    # ... and more full rounds than the cost-ranked last round covers (159 chunks x 16 gate/up
+    # column blocks: 9 full rounds and a tail in plain snake order)
+    (4, 256, 2048, [20000, 12000, 6000, 2200]),
 ]
 
 
