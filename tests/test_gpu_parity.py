@@ -127,6 +127,48 @@ def test_ffn_matches_oracle(case):
     assert err <= TOL[wdt]
 
 
+MANY_EXPERT_CASES = [
+    # (weight dtype, E_loc, H, I, mean rows per expert): expert tables of 2-4 groups of 64 on
+    # every FFN path: both weight-streaming kernels (bf16), streaming gate/up with the fp8 down
+    # on the 256-row GEMM, the 256-row fp8 GEMM, the 128-row bf16 GEMM
+    ("bf16", 200, 128, 64, 20),
+    ("fp8", 256, 128, 64, 60),
+    ("fp8", 130, 256, 128, 110),
+    ("bf16", 256, 128, 128, 100),
+]
+
+
+@pytest.mark.parametrize("case", MANY_EXPERT_CASES, ids=[f"{c[0]}_E{c[1]}_m{c[4]}" for c in MANY_EXPERT_CASES])
+def test_ffn_many_local_experts(case):
+    """Up to 256 local experts, Zipf-skewed row counts with about a tenth of the experts empty:
+    every row against the oracle."""
+    wdt, E, H, I, mean = case
+    _say("ffn many experts", case)
+    rng = np.random.default_rng(E * 7 + H + mean)
+    wts = W.make_layer_weights(rng, E, H, I, 0.05, wdt)
+    p = 1.0 / np.arange(1, E + 1) ** 0.8
+    p[rng.choice(E, E // 10, replace=False)] = 0.0
+    p = rng.permutation(p / p.sum())
+    n = mean * E
+    counts = rng.multinomial(n, p)
+    assert (counts == 0).sum() >= E // 10 and counts.max() > 2 * mean
+    x_np = W.to_bf16_bits(rng.standard_normal((n, H)).astype(np.float32))
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    codes = {"bf16": M.MOE_BF16, "fp8": M.MOE_FP8_E4M3}
+    st = M.ExpertStep(E, H, I, 2, M.MOE_BF16, codes[wdt], n, 4)
+    wt = weight_tensors(wts)
+    st.load_weights(wt["wg"], wt["wu"], wt["wd"], wt.get("s_gate"), wt.get("s_up"), wt.get("s_down"))
+    st.xb[:n].copy_(dev(x_np, "bf16"))
+    st.offsets.copy_(dev(offsets))
+    st.ffn(n)
+    torch.cuda.synchronize()
+    y_ref = O.expert_ffn(O.decode(x_np, "bf16"), offsets, wts)
+    y_gpu = decode_tensor(st.y[:n])
+    err, ee = row_rel_err(y_gpu, y_ref), elem_rel_err(y_gpu, y_ref)
+    _say(f"  {n} rows: row rel err {err:.3e} (elementwise {ee:.3e})")
+    assert err <= TOL[wdt]
+
+
 def test_ffn_empty_batch_is_a_no_op():
     st = M.ExpertStep(2, 64, 64, 2, M.MOE_BF16, M.MOE_BF16, 4, 4)
     z = torch.zeros((2, 64, 64), dtype=torch.bfloat16, device="cuda")
