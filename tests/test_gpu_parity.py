@@ -703,33 +703,40 @@ def test_c4_merged_waves(c4_ref, waves):
 
 
 GATHER_CASES = [
-    # (act/weight dtype, E, H, I, n, P): streaming kernel, 128-row GEMM kernel, fp32 path
-    ("bf16", 8, 2880, 2880, 256, 4096),
-    ("fp8", 3, 640, 192, 700, 900),
-    ("bf16", 4, 512, 256, 600, 1000),
-    ("f32", 3, 64, 128, 40, 64),
+    # (act/weight dtype, E, H, I, n, P, pitch padding): streaming kernel, 256-row fp8 GEMM,
+    # 128-row GEMM kernel, fp32 path; pools whose rows are wider than H
+    ("bf16", 8, 2880, 2880, 256, 4096, 0),
+    ("fp8", 3, 640, 192, 700, 900, 0),
+    ("bf16", 4, 512, 256, 600, 1000, 0),
+    ("f32", 3, 64, 128, 40, 64, 0),
+    ("bf16", 8, 2880, 2880, 256, 4096, 8),
+    ("fp8", 3, 640, 192, 700, 900, 64),
 ]
 
 
-@pytest.mark.parametrize("case", GATHER_CASES, ids=[f"{c[0]}_E{c[1]}_H{c[2]}_n{c[4]}" for c in GATHER_CASES])
+@pytest.mark.parametrize("case", GATHER_CASES,
+                         ids=[f"{c[0]}_E{c[1]}_H{c[2]}_n{c[4]}" + (f"_pad{c[6]}" if c[6] else "") for c in GATHER_CASES])
 def test_gather_on_load_matches_explicit_gather(case):
     """The FFN reading pool rows through slot[perm[r]] gives the same bits as the FFN on the
     batch moe_assemble copied out, and both match the oracle; queue entries with invalid
-    slots or non-local experts are rejected the same way."""
-    wdt, E, H, I, n, P = case
+    slots or non-local experts are rejected the same way.  The pool may be a view of wider
+    rows (pitch H + padding)."""
+    wdt, E, H, I, n, P, pad = case
     _say("gather-on-load case", case)
     rng = np.random.default_rng(n + H)
     act = "f32" if wdt == "f32" else "bf16"
     wts = W.make_layer_weights(rng, E, H, I, 0.05, wdt)
-    pool_raw = rng.standard_normal((P, H)).astype(np.float32)
-    pool_np = pool_raw if act == "f32" else W.to_bf16_bits(pool_raw)
+    pool_raw = rng.standard_normal((P, H + pad)).astype(np.float32)
+    pool_full = pool_raw if act == "f32" else W.to_bf16_bits(pool_raw)
+    pool_np = pool_full[:, :H]
     slot = rng.integers(0, P, n).astype(np.int32)
     expert = rng.integers(0, E, n).astype(np.int32)
     slot[:: 17] = P + 3          # rejected: slot out of range
     expert[5:: 29] = E + 1       # rejected: non-local expert
     codes = {"f32": M.MOE_F32, "bf16": M.MOE_BF16, "fp8": M.MOE_FP8_E4M3}
     wt = weight_tensors(wts)
-    pool = dev(pool_np, act)
+    pool = dev(pool_full, act)[:, :H]
+    assert pool.stride(0) == H + pad
     ys = []
     # gather through row_slot (the default), through perm and slot, and the explicit copy
     for mode in ("row_slot", "perm_slot", "explicit"):
