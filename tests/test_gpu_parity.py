@@ -1003,6 +1003,22 @@ def test_gemm_split_tail_matches_whole_units(wdt):
 
 
 def _fused_index_batch(case):
+    if case.startswith("many"):
+        # 200 (bf16) or 256 (fp8) local experts from a nonzero base, most with one or two pairs
+        # or none; two local pairs per token at distinct positions
+        E, wdt, n = (200, "bf16", 256) if case == "many_bf16" else (256, "fp8", 250)
+        rng = np.random.default_rng(E + n)
+        H, I, K, P, base = 256, 128, 4, 512, 56
+        T = (n + 1) // 2
+        wts = W.make_layer_weights(rng, E, H, I, 0.05, wdt)
+        tok = np.repeat(np.arange(T, dtype=np.int32), 2)[:n]
+        kslot = np.concatenate([rng.permutation(K)[:2] for _ in range(T)]).astype(np.int32)[:n]
+        b = W.Batch(act="bf16", H=H, K=K, E_loc=E, expert_base=base, P=P,
+                    pool=W.to_bf16_bits(rng.standard_normal((P, H)).astype(np.float32)),
+                    slot=rng.integers(0, P, n).astype(np.int32),
+                    expert=(base + rng.integers(0, E, n)).astype(np.int32), tok=tok, kslot=kslot,
+                    w=rng.standard_normal(n).astype(np.float32), gen=np.zeros(n, np.uint32), T=T)
+        return b, wts, M.MOE_BF16, (M.MOE_BF16 if wdt == "bf16" else M.MOE_FP8_E4M3)
     if case.startswith("c1"):
         b, wts = W.c1_decode()
         act, wc = M.MOE_BF16, M.MOE_BF16
@@ -1023,7 +1039,7 @@ def _fused_index_batch(case):
     return b, wts, act, wc
 
 
-@pytest.mark.parametrize("case", ["c1_bf16", "c1_bad_ragged", "c4_fp8_256"])
+@pytest.mark.parametrize("case", ["c1_bf16", "c1_bad_ragged", "c4_fp8_256", "many_bf16", "many_fp8"])
 def test_fused_queue_index(case):
     """moe_ffn_args.index: the queue index derived inside the gate/up launch gives the same bits
     as moe_assemble followed by the FFN (index outputs, error word, FFN rows, release list,
