@@ -25,7 +25,9 @@
  *   - Memory: the caller allocates every buffer (device memory unless stated).  The
  *     library never allocates, frees or synchronises.  Between calls it keeps only read-only
  *     device properties (compute-unit count, kernel occupancy), cached per device on first
- *     use with atomic stores, so concurrent calls from several host threads are safe.
+ *     use with atomic stores, so concurrent calls from several host threads are safe; the one
+ *     exception is moe_combine_release_noalloc, whose scratch is a static device array per GPU
+ *     (its declaration below gives the limits and the races of overlapping calls).
  *   - Ordering: all work is enqueued on `stream` in call order.  Calls return as soon as
  *     the work is enqueued.
  *   - Host-side errors: a call validates its arguments first and, on failure, returns a
