@@ -148,7 +148,7 @@ class StepRunner:
     """Expert steps over a cycle of ready batches: step s runs batch s mod len(batches) on
     combine-state range s (its own tokens), whose remote results deliver() puts in first."""
 
-    def __init__(self, batches, wts, act_code, w_code, n_steps: int, weight_copies: int = 1):
+    def __init__(self, batches, wts, act_code, w_code, n_steps: int, weight_copies: int = 1, weights_from=None):
         import torch
 
         import asynchronous_moe_expert_amd as M
@@ -165,14 +165,20 @@ class StepRunner:
         self.n_steps = n_steps
         n_max = max(b.n for b in batches)
         self.st = M.ExpertStep(self.E, self.H, self.I, self.K, act_code, w_code, n_max, n_steps * self.T_step)
-        wt = weight_tensors(wts)
-        self.st.load_weights(wt["wg"], wt["wu"], wt["wd"], wt.get("s_gate"), wt.get("s_up"), wt.get("s_down"))
-        del wt
-        # copies of the packed weights at distinct addresses; step s uses copy s % L, so no step
-        # finds the weights the one before it streamed still in a cache
-        L = max(1, weight_copies)
-        self.w_copies = [(self.st.w_gu, self.st.w_d)] + [(self.st.w_gu.clone(), self.st.w_d.clone())
-                                                         for _ in range(L - 1)]
+        if weights_from is None:
+            wt = weight_tensors(wts)
+            self.st.load_weights(wt["wg"], wt["wu"], wt["wd"], wt.get("s_gate"), wt.get("s_up"), wt.get("s_down"))
+            del wt
+            # copies of the packed weights at distinct addresses; step s uses copy s % L, so no step
+            # finds the weights the one before it streamed still in a cache
+            L = max(1, weight_copies)
+            self.w_copies = [(self.st.w_gu, self.st.w_d)] + [(self.st.w_gu.clone(), self.st.w_d.clone())
+                                                             for _ in range(L - 1)]
+        else:  # another runner's packed weights (read-only on the device), no second copy
+            src = weights_from.st
+            self.st.w_gu, self.st.w_d = src.w_gu, src.w_d
+            self.st.s_gate, self.st.s_up, self.st.s_down = src.s_gate, src.s_up, src.s_down
+            self.w_copies = weights_from.w_copies
         self.pool = tensor(b0.pool, b0.act)
         self.d = []
         for b, (tok, r_tok, _) in zip(batches, comp):
@@ -469,6 +475,44 @@ def run_decode(args, W_steps: int, K_steps: int, cpu_seconds: float) -> dict:
     return out
 
 
+def timed_two_streams(runs, W: int, K: int):
+    """Steps alternating between two runners (separate buffers and combine states, the same packed
+    weights), step s on stream s % 2 after W warm-up steps: consecutive batches are independent
+    (different tokens, different buffers), so one step's combine and launch gaps overlap the next
+    step's kernels.  Every step is the whole hot path over its batch; both runners' last steps are
+    checked.  Returns (ms, sum of pairs)."""
+    torch, M = runs[0].torch, runs[0].M
+    for i, r in enumerate(runs):
+        M.moe_state_reset(r.st.state, 0)
+        for s in range(i, W + K, 2):
+            r.deliver(s)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in range(W):
+        with torch.cuda.stream(streams[s % 2]):
+            runs[s % 2].step(s)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for st in streams:
+        st.wait_event(t0)
+    for s in range(W, W + K):
+        with torch.cuda.stream(streams[s % 2]):
+            runs[s % 2].step(s)
+    for st in streams:
+        e = torch.cuda.Event()
+        e.record(st)
+        torch.cuda.current_stream().wait_event(e)
+    t1.record()
+    torch.cuda.synchronize()
+    for i, r in enumerate(runs):
+        mine = [s for s in range(W, W + K) if s % 2 == i]
+        if mine:
+            r.check(max(mine))
+    return t0.elapsed_time(t1), sum(runs[0].batch(s).n for s in range(W, W + K))
+
+
 def run_prefill(args) -> dict:
     import torch
 
@@ -489,6 +533,9 @@ def run_prefill(args) -> dict:
     ev = HipEvents()
     stg = run.stages(ev, max(1, min(K_steps // nw, 5)), flush=True)
     g_ms, g_pairs = run.timed_graph(W_steps, K_steps)
+    run2 = StepRunner(waves, setup.weights, 1, 2, W_steps + K_steps, weights_from=run)
+    p_ms, p_pairs = timed_two_streams([run, run2], W_steps, K_steps)
+    del run2
     per_wave = []
     for w, b in enumerate(waves):
         m, n = stg[w], b.n
@@ -523,6 +570,10 @@ def run_prefill(args) -> dict:
                      "algorithmic_bytes": gu_alg, "kernel_us": round(gu0_ms * 1e3, 2)},
         "graph": {"value": round(g_pairs / (g_ms * 1e-3), 1), "ms_per_step": round(g_ms / K_steps, 5),
                   "note": "the same K steps captured as one HIP graph and replayed once"},
+        "two_streams": {"value": round(p_pairs / (p_ms * 1e-3), 1), "ms_per_step": round(p_ms / K_steps, 5),
+                        "note": "the same K steps alternating between two sets of buffers and combine states "
+                                "(shared weights) on two streams, so that consecutive waves overlap; every step "
+                                "is the whole path over its batch, both sets checked"},
         "waves": per_wave,
         "note": "value: K steps timed back to back (step s = wave s mod 4, its remote results delivered before "
                 "the timed region; each step's queue index also links its arrivals for the combine, in one "
