@@ -450,6 +450,9 @@ def run_decode(args, W_steps: int, K_steps: int, cpu_seconds: float) -> dict:
     ev = HipEvents()
     stg = run.stages(ev, max(1, min(K_steps, 20)))[0]
     g_ms, g_pairs = run.timed_graph(W_steps, K_steps)
+    run2 = StepRunner([b], wts, 1, 1, W_steps + K_steps, weights_from=run)
+    p_ms, p_pairs = timed_two_streams([run, run2], W_steps, K_steps)
+    del run2
     counts = run.st.counts.cpu().numpy()
     active = int((counts > 0).sum())
     H, I, n = b.H, wts.I, b.n
@@ -470,6 +473,9 @@ def run_decode(args, W_steps: int, K_steps: int, cpu_seconds: float) -> dict:
         "stages_us": {k: round(v * 1e3, 2) for k, v in stg.items()},
         "graph": {"value": round(g_pairs / (g_ms * 1e-3), 1), "ms_per_step": round(g_ms / K_steps, 5),
                   "note": "the same K steps captured as one HIP graph and replayed once"},
+        "two_streams": {"value": round(p_pairs / (p_ms * 1e-3), 1), "ms_per_step": round(p_ms / K_steps, 5),
+                        "note": "the same K steps alternating between two sets of buffers and combine states "
+                                "(the same weight copies) on two streams, so that consecutive steps overlap"},
     }
     out["cpu_baseline"] = cpu_baseline_decode(b, wts, cpu_seconds) if cpu_seconds > 0 else None
     return out
