@@ -114,3 +114,42 @@ def test_host_validation_rejects_bad_arguments(lib):
 
     p = N.PackArgs(E_loc=2, H=64, I=96, w_dtype=M.MOE_BF16)
     assert lib.moe_pack_ffn_weights(C.byref(p), null) == -5
+
+
+def test_host_validation_of_fused_arguments_and_other_entry_points(lib):
+    """Further host-side checks, all returning before anything is enqueued: the FFN's size limits,
+    a queue index or combine plan handed to the FFN that does not fit the call, the two halves of
+    the combine, and the allocation-free combine's arrival limit."""
+    null = None
+    base = dict(E_loc=2, H=64, I=64, act_dtype=M.MOE_BF16, w_dtype=M.MOE_BF16, xb=16, offsets=16, w_gu=16,
+                w_d=16, y=16, workspace=16, workspace_bytes=1 << 20)
+    for n in (-1, (1 << 24) + 1):
+        f = N.FfnArgs(n=n, **base)
+        assert lib.moe_expert_ffn_grouped(C.byref(f), null) == -2, n
+    f = N.FfnArgs(n=4, **dict(base, E_loc=257))
+    assert lib.moe_expert_ffn_grouped(C.byref(f), null) == -2
+    # a queue index whose call does not match the FFN's (n, xb given) is MOE_EINVAL_SIZE; one that
+    # moe_assemble itself would reject returns moe_assemble's status
+    ptrs = dict(slot=16, expert=16, pool=16, perm=16, pos=16, counts=16, offsets=16, err=16, row_slot=16)
+    ix = N.AssembleArgs(n=4, E_loc=2, H=64, P=10, pool_pitch=64, act_dtype=M.MOE_BF16, **ptrs)
+    f = N.FfnArgs(n=8, index=C.addressof(ix), **base)
+    assert lib.moe_expert_ffn_grouped(C.byref(f), null) == -2
+    ix_xb = N.AssembleArgs(n=4, E_loc=2, H=64, P=10, pool_pitch=64, act_dtype=M.MOE_BF16, xb=16, **ptrs)
+    f = N.FfnArgs(n=4, index=C.addressof(ix_xb), **base)
+    assert lib.moe_expert_ffn_grouped(C.byref(f), null) == -2
+    ix_bad = N.AssembleArgs(n=4, E_loc=0, H=64, P=10, pool_pitch=64, act_dtype=M.MOE_BF16, **ptrs)
+    f = N.FfnArgs(n=4, index=C.addressof(ix_bad), **base)
+    assert lib.moe_expert_ffn_grouped(C.byref(f), null) == -2
+    # a combine plan handed to the FFN is validated like moe_combine_plan (K > 32, fp8 rows)
+    st = N.StateC(acc=16, mask=16, head=16, tgen=16, rflag=16, T_cap=8, H=64)
+    for kw, code in ((dict(K=33), -2), (dict(K=4, row_dtype=M.MOE_FP8_E4M3), -3)):
+        plan = N.CombineArgs(m=1, state=st, **kw)
+        f = N.FfnArgs(n=4, plan=C.addressof(plan), **base)
+        assert lib.moe_expert_ffn_grouped(C.byref(f), null) == code, kw
+        assert lib.moe_combine_plan(C.byref(plan), null) == code, kw
+        assert lib.moe_combine_apply(C.byref(plan), null) == code, kw
+    assert lib.moe_combine_plan(None, null) == -1 and lib.moe_combine_apply(None, null) == -1
+    # the allocation-free combine: its static scratch holds a fixed number of arrivals
+    assert lib.moe_combine_release_noalloc(None, null) == -1
+    over = N.CombineArgs(m=int(lib.moe_combine_noalloc_max_arrivals()) + 1, K=4, state=st)
+    assert lib.moe_combine_release_noalloc(C.byref(over), null) == -8
