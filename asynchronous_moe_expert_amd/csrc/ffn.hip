@@ -91,6 +91,33 @@ struct GatherRows {
     s = s < 0 ? 0 : (s >= P ? P - 1 : s);
     return s * pitch;
   }
+  // row_offset of N rows at once: every row's index load is issued before the first is used
+  // (one at a time, each row's lookup waited for the one before: up to 2N load latencies
+  // between two units of a GEMM instead of two)
+  template <int N>
+  __device__ __forceinline__ void row_offsets(const int (&r)[N], int Kd, int64_t (&off)[N]) const {
+    if (perm == nullptr) {
+#pragma unroll
+      for (int i = 0; i < N; ++i) off[i] = (int64_t)r[i] * Kd;
+      return;
+    }
+    int s[N];
+    if (row_slot != nullptr) {
+#pragma unroll
+      for (int i = 0; i < N; ++i) s[i] = row_slot[r[i]];
+    } else {
+      int q[N];
+#pragma unroll
+      for (int i = 0; i < N; ++i) q[i] = perm[r[i]];
+#pragma unroll
+      for (int i = 0; i < N; ++i) s[i] = slot[q[i] < 0 ? 0 : q[i]];
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int64_t c = s[i] < 0 ? 0 : (s[i] >= P ? P - 1 : (int64_t)s[i]);
+      off[i] = c * pitch;
+    }
+  }
 };
 
 // The queue index of a moe_assemble call (index only) derived inside the gate/up launch of a
@@ -1256,7 +1283,7 @@ static_assert(kG2S == 4, "four LDS stages (the epilogue takes one per wave)");
 // Built by wave 0.
 struct G2Table {
   int a0[256], a1[256], nf[256], fs[256], pe[256], pt[256];
-  int E, F, total;
+  int E, F, total, psum;  // psum: the partial chunks' 32-row tiles, summed
 };
 
 __device__ __forceinline__ void g2_table_build(G2Table& tb, const int32_t* __restrict__ offsets, int E_loc,
@@ -1287,7 +1314,7 @@ __device__ __forceinline__ void g2_table_build(G2Table& tb, const int32_t* __res
     }
     base += __shfl(incl, 63, 64);
   });
-  int pos = 0;
+  int pos = 0, psum = 0;
   const uint64_t below = (1ull << lane) - 1ull;
   for (int t = kG2MT; t >= 1; --t) {
     static_for<4>([&](auto jc) {
@@ -1299,12 +1326,14 @@ __device__ __forceinline__ void g2_table_build(G2Table& tb, const int32_t* __res
         tb.pt[pos + __popcll(bal & below)] = t;
       }
       pos += __popcll(bal);
+      psum += t * __popcll(bal);
     });
   }
   if (lane == 0) {
     tb.E = E_loc;
     tb.F = base;
     tb.total = base + pos;
+    tb.psum = psum;
   }
 }
 
@@ -1419,43 +1448,90 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm256_kernel(const uint16_t* __r
   const int U = tab.total * n_blocks_N;
   const int G = gridDim.x, Gx = G >> 3, b = blockIdx.x;
   const int jw = (b & 7) * Gx + (b >> 3);  // logical workgroup: XCD-major
-  // The last, partial round (T = U mod G units, the cheapest) goes to the workgroups the full
-  // rounds loaded least: its unit i to the workgroup of rank i in (model cost, logical index)
-  // order, a unit of t row tiles costing t + 1 (measured unit times on prefill waves: 13 +
-  // 12.4 t us for gate/up, 6 + 7.6 t for down).  The snake alone hands the last round to the
-  // workgroups that drew the largest units of round 0 (up to 30 us longer on the prefill waves
-  // of 3277-4915 pairs).  For more than kG2RankRounds full rounds the snake order is kept.
-  const int R = U / G;
-  const bool ranked = R >= 1 && R <= kG2RankRounds && U > R * G && G <= 256;
-  int tail_u = -1;  // this workgroup's unit of the last round, if any
+  // A unit of t row tiles costs t + 1 (measured unit times on prefill waves: 13 + 12.4 t us for
+  // gate/up, 6 + 7.6 t for down).  Round 0 gives unit jw to logical workgroup jw.  The later units
+  // go to the workgroups whose round-0 unit leaves room for at least the cheapest unit under the
+  // target (the largest unit or the mean load, whichever is larger); a workgroup that drew one of
+  // the largest units stops there when that is not so (prefill wave of 1638 pairs: the busiest
+  // workgroup's model cost 11 -> 9, its down launch 76 -> 68 us).  Over those workgroups (their logical
+  // order kept) the later rounds run as a snake (the first of them reversed: a workgroup that drew
+  // a large unit draws a small one), and the last, partial round goes to the least loaded: its unit
+  // i to the workgroup of rank i in (model cost, index) order (the snake alone hands it to the
+  // workgroups that drew the largest units, up to 30 us longer).  For more than kG2RankRounds full
+  // rounds the snake order is kept.
+  auto ucost = [&](int uu) {
+    const int q = uu / n_blocks_N;
+    return (q < tab.F ? kG2MT : tab.pt[q - tab.F]) + 1;
+  };
+  __shared__ unsigned long long s_kept[4];
+  __shared__ int s_below[4];
+  int Gp = G, jk = jw;  // workgroups taking later units, this one's index among them
+  bool later = true;
+  const int total_cost = (tab.F * (kG2MT + 1) + tab.psum + (tab.total - tab.F)) * n_blocks_N;
+  const int target = max(ucost(0), (total_cost + G - 1) / G), min_later = U > G ? ucost(U - 1) : 0;
+  // (no workgroup is left out when even the largest unit leaves room for the cheapest)
+  if (U > G && G <= 256 && ucost(0) + min_later > target) {
+    const int w = wv * 64 + lane;
+    const uint64_t bal = __ballot(w < G && ucost(w) + min_later <= target);
+    if (lane == 0) s_kept[wv] = bal;
+    __syncthreads();
+    int cnt = 0, before = 0;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const uint64_t x = s_kept[v];
+      cnt += __popcll(x);
+      before += v < (jw >> 6) ? __popcll(x) : v == (jw >> 6) ? __popcll(x & ((1ull << (jw & 63)) - 1ull)) : 0;
+    }
+    if (cnt > 0 && cnt < G) {
+      Gp = __builtin_amdgcn_readfirstlane(cnt);
+      jk = __builtin_amdgcn_readfirstlane(before);
+      later = __builtin_amdgcn_readfirstlane((int)((s_kept[jw >> 6] >> (jw & 63)) & 1ull));
+    }
+  }
+  const int U2 = U - G, R2 = U2 > 0 ? U2 / Gp : 0;
+  const bool ranked = U2 > R2 * Gp && R2 + 1 <= kG2RankRounds && G <= 256;
+  int tail_u = -1;  // this workgroup's unit of the last, partial round, if any
   if (ranked) {
-    // model cost of logical workgroup w's full rounds
-    auto cost_of = [&](int w) {
-      int c = 0;
-      for (int r = 0; r < R; ++r) {
-        const int q = (r * G + ((r & 1) ? G - 1 - w : w)) / n_blocks_N;
-        c += q < tab.F ? kG2MT + 1 : tab.pt[q - tab.F] + 1;
-      }
+    // model cost of kept workgroup (logical w, kept index k) over round 0 and the full later rounds
+    auto cost_of = [&](int w, int k) {
+      int c = ucost(w);
+      for (int r = 0; r < R2; ++r) c += ucost(G + r * Gp + ((r & 1) ? k : Gp - 1 - k));
       return c;
     };
-    // each wave ranks 64 workgroups (one per lane) against this one
-    __shared__ int s_below[4];
-    const int mine = cost_of(jw), w = wv * 64 + lane;
+    // each wave ranks 64 workgroups (one per lane) against this one, among the kept ones
+    const int w = wv * 64 + lane;
     int ahead = 0;
-    if (w < G) {
-      const int c = cost_of(w);
-      ahead = c < mine || (c == mine && w < jw);
+    if (later && w < G) {
+      int k = w;
+      bool kw = true;
+      if (Gp < G) {
+        const uint64_t x = s_kept[wv];
+        kw = (x >> lane) & 1ull;
+        k = __popcll(x & ((1ull << lane) - 1ull));
+#pragma unroll
+        for (int v = 0; v < 4; ++v) k += v < wv ? __popcll(s_kept[v]) : 0;
+      }
+      if (kw) {
+        const int c = cost_of(w, k), mine = cost_of(jw, jk);
+        ahead = c < mine || (c == mine && k < jk);
+      }
     }
     const int cnt = __popcll(__ballot(ahead));
     if (lane == 0) s_below[wv] = cnt;
     __syncthreads();
     const int rank = s_below[0] + s_below[1] + s_below[2] + s_below[3];
-    if (rank < U - R * G) tail_u = R * G + rank;
+    if (later && rank < U2 - R2 * Gp) tail_u = G + R2 * Gp + rank;
+    tail_u = __builtin_amdgcn_readfirstlane(tail_u);
   }
 #pragma clang loop unroll(disable)
   for (int r = 0;; ++r) {
-    int u = r * G + ((r & 1) ? G - 1 - jw : jw);
-    if (r == R && ranked) u = tail_u < 0 ? U : tail_u;
+    int u = jw;
+    if (r > 0) {
+      if (!later) break;
+      const int r2 = r - 1;
+      u = G + r2 * Gp + ((r2 & 1) ? jk : Gp - 1 - jk);
+      if (r2 == R2 && ranked) u = tail_u < 0 ? U : tail_u;
+    }
     if (u >= U) break;
     const int q = u / n_blocks_N, nb = u - q * n_blocks_N;
     int e, m0, mend;
@@ -1495,11 +1571,19 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm256_kernel(const uint16_t* __r
       // lane of a stage; slot P holds row P / 8, piece (P % 8) ^ ((P / 8 >> 1) & 7) of that row
       // (rows past the chunk copy its last row; their results are never stored)
       int avo[MTA];
-      static_for<MTA>([&](auto d) {
-        const int P = (4 * d() + wv) * 64 + lane, row = P >> 3, kq = (P & 7) ^ ((row >> 1) & 7);
-        const int rr = min(m0 + row, mend - 1);
-        avo[d()] = (int)((gr.row_offset(rr, Kd) + kq * 8) * 2);
-      });
+      {
+        int rd[MTA];
+        int64_t od[MTA];
+        static_for<MTA>([&](auto d) {
+          const int P = (4 * d() + wv) * 64 + lane;
+          rd[d()] = min(m0 + (P >> 3), mend - 1);
+        });
+        gr.row_offsets(rd, Kd, od);
+        static_for<MTA>([&](auto d) {
+          const int P = (4 * d() + wv) * 64 + lane, row = P >> 3, kq = (P & 7) ^ ((row >> 1) & 7);
+          avo[d()] = (int)((od[d()] + kq * 8) * 2);
+        });
+      }
       f32x16 acc[MTA][2];
       static_for<MTA>([&](auto i) { static_for<2>([&](auto jj) { acc[i()][jj()] = f32x16{}; }); });
       GemmW<WDT> wr[S];
