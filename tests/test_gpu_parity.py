@@ -912,6 +912,12 @@ GEMM256_CASES = [
     # ... and more full rounds than the cost-ranked last round covers (159 chunks x 16 gate/up
     # column blocks: 9 full rounds and a tail in plain snake order)
     (4, 256, 2048, [20000, 12000, 6000, 2200]),
+    # ... and workgroups left out of the later rounds: gate/up round 0 holds 128 units of 9 tiles'
+    # cost (8 full chunks) and 128 of one tile; the later units of one tile go only to those 128:
+    # one snaked round (139 rows per expert on average) ...
+    (17, 256, 2048, [2048] + [20] * 16),
+    # ... and one snaked round and a cost-ranked tail of 32
+    (19, 256, 2048, [2048] + [20] * 18),
 ]
 
 
