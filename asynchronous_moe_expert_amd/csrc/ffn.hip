@@ -1263,10 +1263,13 @@ __global__ __launch_bounds__(256) void ffn_gemm_finalize_kernel(const int32_t* _
 // Work order: each workgroup's work is fixed on the device from `offsets` (no host round trip,
 // no atomics).  The chunks are sorted by cost: every full 256-row chunk first (expert order),
 // then each expert's partial last chunk by its 32-row tile count, descending (ties: expert
-// order); a chunk's 256-column blocks are consecutive units.  Round r gives unit r*G + j to
-// workgroup j (reversed in odd rounds: a snake, so that a workgroup that drew a large unit in
-// one round draws a small one in the next), and workgroup j is the j % Gx-th of XCD j / Gx,
-// so a chunk's column blocks run side by side on one XCD and share its activations in L2.
+// order); a chunk's 256-column blocks are consecutive units.  Round 0 gives unit j to workgroup
+// j, and workgroup j is the j % Gx-th of XCD j / Gx, so a chunk's column blocks run side by side
+// on one XCD and share its activations in L2.  The later rounds go, in the same order, to the
+// workgroups whose round-0 unit leaves room for another under the mean load (all of them on
+// large batches) as a snake (reversed in alternate rounds, so that a workgroup that drew a
+// large unit in one round draws a small one in the next), the last, partial round ranked by
+// load (in the kernel below).
 constexpr int kG2BM = 256;
 constexpr int kG2MT = kG2BM / 32;
 constexpr int kG2RankRounds = 8;
